@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of batched draft-block verification with the fused clipped reverse-KL.
+
+One step = one sv_verify_block call over one packed batch resident in HBM: the
+streaming pass over every target and draft logit row, the per-row finalize (rKL,
+acceptance test), the first-rejection scan and the residual / bonus draw.
+
+Workload (default): B=128 requests, k=15 drafts each (16-position blocks),
+V=151936, bf16 logits, drafter noise sigma_b in {0.5, 1, 2}, delta=1, seeded
+synthetic inputs (see synth/workloads.py).  Prints one JSON line on stdout;
+progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=128 k=15 V=151936"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "sv_rows_cfg4_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_verification_sv_amd", "csrc", f)
+                  for f in ("sv_kernels.hip", "sv_device.h", "sv_layout.h", "sv_launch.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+_W = None  # the workload, inherited by the forked cpu_baseline workers
+
+
+def _oracle_request(b):
+    # cpu_baseline worker: the oracle, unchanged, on one request
+    import oracle
+
+    w = _W
+    oracle.verify_block(target=w.target, draft=w.draft, dtype=w.dtype, V=w.V, k=w.k,
+                        draft_tokens=w.draft_tokens, uniforms=w.uniforms,
+                        temperature=w.temperature, delta=w.delta, requests=[b])
+    return int(w.k[b])
+
+
+def cpu_baseline(w, n_requests: int) -> dict:
+    """Runs before anything touches the GPU, so the forked workers inherit no device state."""
+    import multiprocessing as mp
+
+    global _W
+    _W = w
+    cores = max(1, min(16, os.cpu_count() or 1))
+    reqs = list(range(min(n_requests, w.B)))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        positions = sum(pool.map(_oracle_request, reqs, chunksize=1))
+    dt = time.perf_counter() - t0
+    return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions, all "
+                      f"outputs incl. the clipped rKL), float64 NumPy, {cores} worker processes, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=32)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification path is per-GPU data-parallel "
+              "(requests are independent), and this build runs on a single MI355X. "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+    from synth import config
+
+    t0 = time.perf_counter()
+    w = config(args.config)
+    log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
+        cpu = cpu_baseline(w, args.cpu_requests)
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} positions/s")
+
+    pkg.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def up(a, dt=None):
+        if dt is torch.bfloat16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    bf = torch.bfloat16 if w.dtype == "bf16" else None
+    target, draft = up(w.target, bf), up(w.draft, bf)
+    k = up(w.k.astype(np.int32))
+    toks = up(w.draft_tokens.astype(np.int32))
+    uni = up(w.uniforms.astype(np.float32))
+    temp = up(w.temperature.astype(np.float32))
+    code = pkg.SV_BF16 if w.dtype == "bf16" else pkg.SV_F32
+    ws = pkg.alloc_workspace(pkg.workspace_size(w.B, w.k_max, w.V, code), dev)
+    n_d, B, V = w.n_draft_rows, w.B, w.V
+    out = {
+        "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "out_tokens": torch.empty(n_d + B, dtype=torch.int32, device=dev),
+        "rkl": torch.empty(n_d, dtype=torch.float32, device=dev),
+        "p_at_draft": torch.empty(n_d, dtype=torch.float32, device=dev),
+        "q_at_draft": torch.empty(n_d, dtype=torch.float32, device=dev),
+        "device_status": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+
+    def step():
+        pkg.verify_block(target, draft, k, toks, uni, temp, w.delta, k_max=w.k_max,
+                         workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(out["device_status"].item()) == 0
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = 1e3 * elapsed / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # per-kernel durations: HIP events the library records around each launch on the
+    # call's stream, over a second pass of the same number of steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    pkg.profile_reset()
+    kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in kt.items()}
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    esize = 2 if w.dtype == "bf16" else 4
+    rows_bytes = (w.n_target_rows + n_d) * V * esize  # every logit read once
+    meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
+    rows_us = kernels["sv_rows"]["avg_us"]
+    achieved = rows_bytes / (rows_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash() and c.get("config") == args.config:
+            traffic = c.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+    value = n_d / (ms_per_step * 1e-3)
+    whole_gbs = (rows_bytes + meta_bytes) / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded logits shaped like the pages' workloads)",
+        "config": {"workload": w.name, "B": B, "k": int(w.k_max), "V": V, "input_dtype": w.dtype,
+                   "delta": w.delta, "verified_positions_per_step": n_d,
+                   "algorithmic_bytes_per_step": rows_bytes + meta_bytes},
+        "roofline": roofline,
+        "step_hbm_gbs": round(whole_gbs, 1),
+        "step_frac_of_peak": round(whole_gbs / PEAK_HBM_GBS, 4),
+        "kernels_us": {n: round(v["avg_us"], 2) for n, v in kernels.items()},
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,22 @@
+"""draft_block_verification_sv_amd: batched verification of a one-pass diffusion
+draft block with the fused entry-wise clipped reverse-KL, as hand-written HIP
+kernels for AMD Instinct MI355X (gfx950) behind the C ABI of libspecverify.
+
+The Python layer only marshals tensors into the C ABI; see ``binding``.
+"""
+
+from .binding import (  # noqa: F401
+    SV_BF16,
+    SV_F32,
+    SpecVerifyError,
+    alloc_workspace,
+    clipped_rkl,
+    lib,
+    library_path,
+    profile_enable,
+    profile_read,
+    profile_reset,
+    verify_block,
+    version,
+    workspace_size,
+)

@@ -1,0 +1,233 @@
+"""Python binding of libspecverify: argument marshalling only.
+
+Every step of the verification runs in the library's HIP kernels; this module
+checks tensor shapes (the C ABI trusts its caller for buffer extents), passes raw
+device pointers and the current HIP stream, and allocates outputs.  There is no
+fallback: if the library is not built, or a tensor is not on the GPU, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+_lib = None
+
+SV_BF16, SV_F32 = 0, 1
+SV_DEV_BAD_LENGTH, SV_DEV_ROWS_MISMATCH, SV_DEV_BAD_TOKEN = 1, 2, 4
+SV_DEV_BAD_TEMPERATURE, SV_DEV_BAD_UNIFORM = 8, 16
+SV_MAX_K = 64
+
+_c_i32, _c_i64, _c_f32, _c_sz, _c_p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                       ctypes.c_size_t, ctypes.c_void_p)
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise SpecVerifyError(f"{_LIB_PATH} is not built: run `python __graft_entry__.py` "
+                              "or draft_block_verification_sv_amd.build.build_library()")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.sv_workspace_size.argtypes = [_c_i32, _c_i32, _c_i64, _c_i32]
+    L.sv_workspace_size.restype = _c_sz
+    L.sv_rkl_workspace_size.argtypes = [_c_i64, _c_i64, _c_i32]
+    L.sv_rkl_workspace_size.restype = _c_sz
+    L.sv_verify_block.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64,
+                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f32,
+                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_verify_block.restype = _c_i32
+    L.sv_clipped_rkl.argtypes = [_c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                 _c_p, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_clipped_rkl.restype = _c_i32
+    L.sv_status_string.argtypes = [_c_i32]
+    L.sv_status_string.restype = ctypes.c_char_p
+    L.sv_version.argtypes = []
+    L.sv_version.restype = ctypes.c_char_p
+    L.sv_profile_enable.argtypes = [_c_i32]
+    L.sv_profile_enable.restype = _c_i32
+    L.sv_profile_reset.argtypes = []
+    L.sv_profile_reset.restype = _c_i32
+    L.sv_profile_count.argtypes = []
+    L.sv_profile_count.restype = _c_i32
+    L.sv_profile_get.argtypes = [_c_i32, ctypes.c_char_p, _c_sz, ctypes.POINTER(_c_i64),
+                                 ctypes.POINTER(ctypes.c_double)]
+    L.sv_profile_get.restype = _c_i32
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().sv_status_string(status).decode()
+        raise SpecVerifyError(f"{what}: status {status} ({msg})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: int, device):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be contiguous with {numel} elements, got {tuple(t.shape)}")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def version() -> str:
+    return lib().sv_version().decode()
+
+
+def workspace_size(B: int, k_max: int, V: int, dtype: int) -> int:
+    return int(lib().sv_workspace_size(B, k_max, V, dtype))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device buffer (torch's caching allocator aligns to >= 512 B)."""
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws
+
+
+def verify_block(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
+                 draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                 temperature: Optional[torch.Tensor] = None, delta: float = 1.0, *,
+                 k_max: Optional[int] = None, with_rkl: bool = True, with_probs: bool = True,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                 stream=None) -> dict:
+    """Runs sv_verify_block on the current stream and returns its outputs as tensors.
+
+    target [n_draft_rows + B, >= V] and draft [n_draft_rows, >= V] share the dtype
+    (bfloat16 or float32); V is their column count and the row strides are their
+    leading dimensions.  ``k_max`` defaults to the largest k_b the row count allows
+    (no device read is needed for it).
+    """
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    code = _dtype_code(target)
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft must share a dtype")
+    if target.dim() != 2 or draft.dim() != 2 or target.stride(1) != 1 or draft.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit column stride")
+    B = int(k.numel())
+    n_d = int(draft.shape[0])
+    V = int(target.shape[1])
+    if int(draft.shape[1]) != V or int(target.shape[0]) != n_d + B:
+        raise ValueError(f"shapes: target {tuple(target.shape)} must be [n_draft_rows + B, V], "
+                         f"draft {tuple(draft.shape)} [n_draft_rows, V], B = {B}")
+    if k_max is None:
+        k_max = max(1, min(SV_MAX_K, n_d - B + 1))
+    _need(k, "k", torch.int32, B, dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, n_d, dev)
+    _need(uniforms, "uniforms", torch.float32, n_d + B, dev)
+    if temperature is not None:
+        _need(temperature, "temperature", torch.float32, B, dev)
+    if workspace is None:
+        nbytes = workspace_size(B, k_max, V, code)
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape B={B} k_max={k_max} V={V}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {
+            "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty(n_d + B, dtype=torch.int32, device=dev),
+            "rkl": torch.empty(n_d, dtype=torch.float32, device=dev) if with_rkl else None,
+            "p_at_draft": torch.empty(n_d, dtype=torch.float32, device=dev) if with_probs else None,
+            "q_at_draft": torch.empty(n_d, dtype=torch.float32, device=dev) if with_probs else None,
+            "device_status": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    st = lib().sv_verify_block(
+        code, B, k_max, V, target.stride(0), draft.stride(0), n_d, _ptr(target), _ptr(draft),
+        _ptr(k), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), float(delta),
+        _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("rkl")),
+        _ptr(out.get("p_at_draft")), _ptr(out.get("q_at_draft")), _ptr(out["device_status"]),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sv_verify_block")
+    return out
+
+
+def clipped_rkl(target: torch.Tensor, draft: torch.Tensor, delta: float = 1.0,
+                p_row_index: Optional[torch.Tensor] = None, *,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> tuple:
+    """sv_clipped_rkl: returns (rkl [n_rows] float32, device_status [1] int32)."""
+    dev = target.device
+    code = _dtype_code(target)
+    if draft.dtype != target.dtype or target.dim() != 2 or draft.dim() != 2:
+        raise ValueError("target/draft must be 2-D tensors of one dtype")
+    if target.stride(1) != 1 or draft.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    n = int(draft.shape[0])
+    V = int(draft.shape[1])
+    if int(target.shape[1]) != V:
+        raise ValueError("target and draft must have the same column count")
+    if p_row_index is None:
+        if int(target.shape[0]) < n:
+            raise ValueError("without p_row_index target needs at least as many rows as draft")
+    else:
+        _need(p_row_index, "p_row_index", torch.int32, n, dev)
+    if workspace is None:
+        nbytes = int(lib().sv_rkl_workspace_size(n, V, code))
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape n_rows={n} V={V}")
+        workspace = alloc_workspace(nbytes, dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    st = lib().sv_clipped_rkl(code, n, int(target.shape[0]), V, target.stride(0), draft.stride(0),
+                              _ptr(target), _ptr(draft), _ptr(p_row_index), float(delta),
+                              _ptr(out), _ptr(status), _ptr(workspace), workspace.numel(),
+                              _stream(stream))
+    _check(st, "sv_clipped_rkl")
+    return out, status
+
+
+# ----------------------------------------------------------------------------- profiling
+def profile_enable(on: bool = True):
+    _check(lib().sv_profile_enable(1 if on else 0), "sv_profile_enable")
+
+
+def profile_reset():
+    _check(lib().sv_profile_reset(), "sv_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} for every kernel launched while profiling."""
+    L = lib()
+    res = {}
+    buf = ctypes.create_string_buffer(64)
+    for i in range(L.sv_profile_count()):
+        n = _c_i64(0)
+        ms = ctypes.c_double(0.0)
+        _check(L.sv_profile_get(i, buf, 64, ctypes.byref(n), ctypes.byref(ms)), "sv_profile_get")
+        if n.value:
+            res[buf.value.decode()] = (int(n.value), float(ms.value))
+    return res

@@ -1,0 +1,374 @@
+// C ABI of libspecverify: argument validation, workspace carving and the launch
+// sequence.  Everything host-checkable is checked before the first HIP call, so an
+// invalid call returns its status without touching the device or the runtime.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/specverify.h"
+#include "sv_launch.h"
+
+namespace {
+
+using sv::Dims;
+using sv::Workspace;
+
+constexpr int kNumKernels = 6;
+const char* const kKernelNames[kNumKernels] = {"sv_plan",     "sv_rows",     "sv_finalize",
+                                               "sv_sample",   "sv_rkl_rows", "sv_rkl_finalize"};
+enum { K_PLAN, K_ROWS, K_FIN, K_SAMPLE, K_RKL_ROWS, K_RKL_FIN };
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+  int kernel;
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRec> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[kNumKernels] = {};
+  double total_ms[kNumKernels] = {};
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+hipEvent_t take_event() {
+  Profiler& p = prof();
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Waits for pending event pairs and folds them into the per-kernel totals.
+hipError_t drain_pending() {
+  Profiler& p = prof();
+  hipError_t first = hipSuccess;
+  for (const ProfRec& r : p.pending) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e == hipSuccess) {
+      p.launches[r.kernel] += 1;
+      p.total_ms[r.kernel] += ms;
+    } else if (first == hipSuccess) {
+      first = e;
+    }
+    p.pool.push_back(r.start);
+    p.pool.push_back(r.stop);
+  }
+  p.pending.clear();
+  return first;
+}
+
+template <class F>
+hipError_t timed(int kernel, hipStream_t st, F&& launch) {
+  Profiler& p = prof();
+  std::unique_lock<std::mutex> lock(p.mu);
+  if (!p.on) {
+    lock.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  if (e != hipSuccess) return e;
+  p.pending.push_back({kernel, a, b});
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------------ helpers
+bool dtype_ok(int32_t dtype) { return dtype == SV_BF16 || dtype == SV_F32; }
+int64_t esize(int32_t dtype) { return dtype == SV_BF16 ? 2 : 4; }
+
+bool vec_ok(int32_t dtype, int64_t ld, const void* base) {
+  const int64_t per16 = 16 / esize(dtype);
+  return (ld % per16) == 0 && (reinterpret_cast<uintptr_t>(base) % 16) == 0;
+}
+
+Dims verify_dims(int64_t B, int64_t k_max, int64_t V) {
+  Dims d{};
+  d.B = B;
+  d.n_t = B * (k_max + 1);
+  d.n_d = B * k_max;
+  d.V = V;
+  d.n_units = d.n_t;
+  d.n_slices = sv::n_slices_for(V);
+  d.n_chunks = sv::n_chunks_for(V);
+  return d;
+}
+
+Dims rkl_dims(int64_t n_rows, int64_t V) {
+  Dims d{};
+  d.B = 1;
+  d.n_t = 0;
+  d.n_d = 0;
+  d.V = V;
+  d.n_units = n_rows;
+  d.n_slices = sv::n_slices_for(V);
+  d.n_chunks = 0;
+  return d;
+}
+
+bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
+  return V >= 1 && V <= SV_MAX_VOCAB && ld_t >= V && ld_d >= V;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_version(void) { return "libspecverify 0.1.0 (gfx950)"; }
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "shape out of range (B, k_max, V, ld or row count)";
+    case SV_ERR_DTYPE: return "unknown dtype (expected SV_BF16 or SV_F32)";
+    case SV_ERR_VALUE: return "delta must be finite and > 0 when the reverse-KL is requested";
+    case SV_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or too small";
+    case SV_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t sv_workspace_size(int32_t B, int32_t k_max, int64_t V, int32_t dtype) {
+  if (!dtype_ok(dtype) || B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || V < 1 ||
+      V > SV_MAX_VOCAB)
+    return 0;
+  return sv::carve(verify_dims(B, k_max, V), nullptr, nullptr);
+}
+
+size_t sv_rkl_workspace_size(int64_t n_rows, int64_t V, int32_t dtype) {
+  if (!dtype_ok(dtype) || n_rows < 1 || V < 1 || V > SV_MAX_VOCAB) return 0;
+  if (n_rows * sv::n_slices_for(V) >= (int64_t(1) << 31)) return 0;
+  return sv::carve(rkl_dims(n_rows, V), nullptr, nullptr);
+}
+
+sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, int64_t ld_target,
+                          int64_t ld_draft, int64_t n_draft_rows, const void* target_logits,
+                          const void* draft_logits, const int32_t* k, const int32_t* draft_tokens,
+                          const float* uniforms, const float* temperature, float delta,
+                          int32_t* accept_len, int32_t* out_tokens, float* rkl_out,
+                          float* p_at_draft, float* q_at_draft, int32_t* device_status,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || !shape_ok(V, ld_target, ld_draft))
+    return SV_ERR_SHAPE;
+  if (n_draft_rows < B || n_draft_rows > static_cast<int64_t>(B) * k_max) return SV_ERR_SHAPE;
+  const Dims dm = verify_dims(B, k_max, V);
+  if (dm.n_units * dm.n_slices >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
+  if (!target_logits || !draft_logits || !k || !draft_tokens || !uniforms || !accept_len ||
+      !out_tokens || !device_status)
+    return SV_ERR_NULL;
+  if (rkl_out && !(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
+  const size_t need = sv::carve(dm, nullptr, nullptr);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
+    return SV_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws{};
+  sv::carve(dm, &ws, static_cast<char*>(workspace));
+  const int64_t n_d = n_draft_rows, n_t = n_draft_rows + B;
+  const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
+  const int64_t n_slices = dm.n_slices, n_chunks = dm.n_chunks;
+
+  sv::PlanArgs pa{};
+  pa.B = B;
+  pa.k_max = k_max;
+  pa.V = V;
+  pa.n_d = n_d;
+  pa.k = k;
+  pa.tokens = draft_tokens;
+  pa.uniforms = uniforms;
+  pa.temperature = temperature;
+  pa.ws = ws;
+  pa.device_status = device_status;
+  if (timed(K_PLAN, st, [&] { return sv::launch_plan(pa, st); }) != hipSuccess) return SV_ERR_HIP;
+
+  sv::RowsArgs ra{};
+  ra.target = target_logits;
+  ra.draft = draft_logits;
+  ra.ld_t = ld_target;
+  ra.ld_d = ld_draft;
+  ra.V = static_cast<int32_t>(V);
+  ra.n_slices = n_slices;
+  ra.n_waves = n_t * n_slices;
+  ra.desc = ws.desc;
+  ra.glob = ws.glob;
+  ra.part = ws.part;
+  if (timed(K_ROWS, st, [&] { return sv::launch_rows(dtype, vec, ra, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+
+  sv::FinArgs fa{};
+  fa.target = target_logits;
+  fa.draft = draft_logits;
+  fa.ld_t = ld_target;
+  fa.ld_d = ld_draft;
+  fa.V = static_cast<int32_t>(V);
+  fa.n_slices = n_slices;
+  fa.n_units = n_t;
+  fa.n_d = n_d;
+  fa.desc = ws.desc;
+  fa.glob = ws.glob;
+  fa.req_flags = ws.req_flags;
+  fa.tokens = draft_tokens;
+  fa.uniforms = uniforms;
+  fa.device_status = device_status;
+  fa.part = ws.part;
+  fa.delta = delta;
+  fa.rkl_out = rkl_out;
+  fa.p_at = p_at_draft;
+  fa.q_at = q_at_draft;
+  fa.t_off = ws.t_off;
+  fa.t_lz = ws.t_lz;
+  fa.t_arg = ws.t_arg;
+  fa.d_off = ws.d_off;
+  fa.d_lz = ws.d_lz;
+  fa.acc = ws.acc;
+  if (timed(K_FIN, st, [&] { return sv::launch_finalize(dtype, fa, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+
+  sv::SampleArgs sa{};
+  sa.target = target_logits;
+  sa.draft = draft_logits;
+  sa.ld_t = ld_target;
+  sa.ld_d = ld_draft;
+  sa.V = static_cast<int32_t>(V);
+  sa.n_chunks = n_chunks;
+  sa.B = B;
+  sa.n_t = n_t;
+  sa.glob = ws.glob;
+  sa.off_t = ws.off_t;
+  sa.k = k;
+  sa.req_flags = ws.req_flags;
+  sa.desc = ws.desc;
+  sa.tokens = draft_tokens;
+  sa.uniforms = uniforms;
+  sa.t_off = ws.t_off;
+  sa.t_lz = ws.t_lz;
+  sa.t_arg = ws.t_arg;
+  sa.d_off = ws.d_off;
+  sa.d_lz = ws.d_lz;
+  sa.acc = ws.acc;
+  sa.chunk_r = ws.chunk_r;
+  sa.chunk_p = ws.chunk_p;
+  sa.counters = ws.counters;
+  sa.accept_len = accept_len;
+  sa.out_tokens = out_tokens;
+  if (timed(K_SAMPLE, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t V,
+                         int64_t ld_target, int64_t ld_draft, const void* target_logits,
+                         const void* draft_logits, const int32_t* p_row_index, float delta,
+                         float* rkl_out, int32_t* device_status, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
+  if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
+  const Dims dm = rkl_dims(n_rows, V);
+  if (dm.n_units * dm.n_slices >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
+  if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
+  if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
+  const size_t need = sv::carve(dm, nullptr, nullptr);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
+    return SV_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws{};
+  sv::carve(dm, &ws, static_cast<char*>(workspace));
+  const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
+
+  sv::RowsArgs ra{};
+  ra.target = target_logits;
+  ra.draft = draft_logits;
+  ra.ld_t = ld_target;
+  ra.ld_d = ld_draft;
+  ra.V = static_cast<int32_t>(V);
+  ra.n_slices = dm.n_slices;
+  ra.n_waves = n_rows * dm.n_slices;
+  ra.desc = nullptr;
+  ra.glob = nullptr;
+  ra.p_row_index = p_row_index;
+  ra.n_target_rows = n_target_rows;
+  ra.device_status = device_status;
+  ra.part = ws.part;
+  if (timed(K_RKL_ROWS, st, [&] { return sv::launch_rows(dtype, vec, ra, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+
+  sv::FinArgs fa{};
+  fa.target = target_logits;
+  fa.draft = draft_logits;
+  fa.ld_t = ld_target;
+  fa.ld_d = ld_draft;
+  fa.V = static_cast<int32_t>(V);
+  fa.n_slices = dm.n_slices;
+  fa.n_units = n_rows;
+  fa.desc = nullptr;
+  fa.p_row_index = p_row_index;
+  fa.n_target_rows = n_target_rows;
+  fa.device_status = device_status;
+  fa.part = ws.part;
+  fa.delta = delta;
+  fa.rkl_out = rkl_out;
+  if (timed(K_RKL_FIN, st, [&] { return sv::launch_finalize(dtype, fa, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+sv_status sv_profile_enable(int32_t on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  p.on = on != 0;
+  return SV_OK;
+}
+
+sv_status sv_profile_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  const hipError_t e = drain_pending();
+  for (int i = 0; i < kNumKernels; ++i) {
+    p.launches[i] = 0;
+    p.total_ms[i] = 0.0;
+  }
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int32_t sv_profile_count(void) { return kNumKernels; }
+
+sv_status sv_profile_get(int32_t index, char* name, size_t name_len, int64_t* launches,
+                         double* total_ms) {
+  if (index < 0 || index >= kNumKernels) return SV_ERR_SHAPE;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  const hipError_t e = drain_pending();
+  if (name && name_len) {
+    std::strncpy(name, kKernelNames[index], name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  if (launches) *launches = p.launches[index];
+  if (total_ms) *total_ms = p.total_ms[index];
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device helpers for the gfx950 (CDNA4) verification kernels: bf16 unpacking,
+// 64-lane wavefront reductions built from DPP row permutes and the gfx950
+// permlane16/32 swaps, and a fixed-order fp64 block scan.
+//
+// Every reduction here has a fixed combination tree, so results are bitwise
+// reproducible run to run (no atomics on floating-point data anywhere).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+// fp32 log2(e); the kernels evaluate exp(x) as exp2(x * kL2E).  The same fp32
+// constant is used everywhere a normaliser is formed or consumed, so the whole
+// path computes softmax(kL2E * ln(2) * l), a temperature within 1.3e-8 of 1.
+constexpr float kL2E = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- wave reductions
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Butterfly all-reduce over the 64 lanes: xor 1, xor 2 (quad permutes), half-row
+// mirror, row mirror, then the gfx950 permlane16 / permlane32 swaps combine the
+// four 16-lane rows.  Every lane ends with the same bits (the ops are commutative).
+template <class Op>
+__device__ __forceinline__ int wave_allreduce_i(int v, Op op) {
+  v = op(v, dpp_i<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_i<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_i<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_i<0x140>(v));  // row_mirror
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(static_cast<int>(s16[0]), static_cast<int>(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(static_cast<int>(s32[0]), static_cast<int>(s32[1]));
+  return v;
+}
+
+struct FMaxOp {
+  __device__ __forceinline__ int operator()(int a, int b) const {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }
+};
+struct FAddOp {
+  __device__ __forceinline__ int operator()(int a, int b) const {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }
+};
+struct IMinOp {
+  __device__ __forceinline__ int operator()(int a, int b) const { return a < b ? a : b; }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+  return __int_as_float(wave_allreduce_i(__float_as_int(v), FMaxOp{}));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(wave_allreduce_i(__float_as_int(v), FAddOp{}));
+}
+__device__ __forceinline__ int wave_min_i(int v) { return wave_allreduce_i(v, IMinOp{}); }
+
+// fp64 reductions and scans (finalize / sampler kernels, not the streaming loop).
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmax(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    int o = __shfl_xor(v, m, kWave);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Inclusive scan over a 256-thread block in fp64, fixed order (Hillis-Steele inside
+// each wave, then the four wave totals).  `lds` holds 4 doubles.
+__device__ __forceinline__ double block_inclusive_scan_256(double v, double* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    double o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  if (lane == kWave - 1) lds[wave] = v;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += lds[w];
+  __syncthreads();
+  return base + v;
+}
+
+}  // namespace sv

@@ -1,0 +1,184 @@
+/*
+ * libspecverify -- batched verification of a one-pass diffusion draft block,
+ * with the fused entry-wise clipped reverse-KL, for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI: device pointers, sizes, one stream handle.  No C++ or framework
+ * types cross this boundary and no exception escapes it.
+ *
+ * What is computed (cited by page title and section):
+ *   - "AdaFlash: Adaptive Speculative Decoding via On-Policy Distilled Diffusion
+ *     Drafters" (arXiv 2607.19223), Section 2.1: each draft token x_i is accepted
+ *     with probability min(1, p(x_i)/q(x_i)); tokens up to the first rejection are
+ *     kept; at the rejection a corrected token is drawn from the residual.
+ *   - AdaFlash reading notes (zhongzhuzhou.org), basic recipe step 4: the residual
+ *     is max(0, p - q), normalised.
+ *   - DFlash notes (zhangshuibai.github.io), Section 3.1 step 6: when every draft
+ *     is accepted the target emits one bonus token, so a round emits a_b + 1
+ *     tokens; Section 5.2: the drafter's per-position marginals play q.
+ *   - AdaFlash paper, Section 3.2: per-request verification length k_b in
+ *     [1, k_max]; Section 3.3: the batch is packed to total length sum_b k_b.
+ *   - AdaFlash paper, Section 3.1 (equation of the clipped reverse-KL) and
+ *     Appendix B.1 (reverse-KL temperature 1):
+ *         R_i = sum_y min(delta, q_i(y) log(q_i(y) / p_i(y))).
+ *
+ * Conventions where the pages leave a choice open:
+ *   - accept iff u < min(1, p_T(x)/q_T(x)) (equality rejects);
+ *   - uniforms slot k_b of a request drives its single final-token draw;
+ *   - the final token is the smallest id y with prefix mass(0..y) > u * Z,
+ *     Z the total mass, ids in ascending order (zero-mass ids are never drawn);
+ *   - a residual of zero total mass (possible only through rounding) falls
+ *     back to p_T of the same row;
+ *   - temperature T_b = 0 is greedy: accept iff x_i == argmax of target row i,
+ *     final token = argmax of the target row at a_b; ties go to the lowest id;
+ *   - the clipped reverse-KL always uses temperature 1 and is reported for every
+ *     draft row, accepted or not; min applies per entry, so R_i may be negative.
+ *
+ * Packed layout (request b has k_b drafts; off_t[b] = sum_{c<b} (k_c + 1)):
+ *   target row off_t[b] + i, i = 0..k_b: row i < k_b scores draft i, row k_b is the
+ *                                          bonus row;
+ *   draft  row off_t[b] - b + i, i < k_b;
+ *   draft_tokens and the reported per-draft outputs follow the draft rows;
+ *   uniforms and out_tokens follow the target rows.
+ * Logits are row-major with leading dimensions ld_target / ld_draft (elements,
+ * >= V); only columns [0, V) are read.
+ *
+ * Streams and memory: every pointer argument except where stated is a device
+ * pointer owned by the caller.  Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL = the null stream) and never synchronise the device.  The
+ * library allocates nothing per call; scratch lives in the caller's workspace,
+ * which a call may overwrite and which must not be shared by calls that can run
+ * concurrently.  Results are bitwise deterministic for identical inputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sv_status;
+
+/* Host-side status codes, returned synchronously before anything is enqueued. */
+enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+  SV_ERR_SHAPE = 2,     /* B, V, ld, k_max or a row count out of range                 */
+  SV_ERR_DTYPE = 3,     /* dtype is not SV_BF16 / SV_F32                               */
+  SV_ERR_VALUE = 4,     /* delta not finite or <= 0 while the rKL is requested         */
+  SV_ERR_WORKSPACE = 5, /* workspace NULL, misaligned (256 B) or smaller than required */
+  SV_ERR_HIP = 6        /* a HIP runtime call or kernel launch failed                  */
+};
+
+/* Logit element types. */
+enum { SV_BF16 = 0, SV_F32 = 1 };
+
+/* Bits written to *device_status by a call (0 = every request was valid). */
+enum {
+  SV_DEV_BAD_LENGTH = 1,       /* some k_b outside [1, k_max]: the whole call is void     */
+  SV_DEV_ROWS_MISMATCH = 2,    /* sum_b k_b != n_draft_rows: the whole call is void       */
+  SV_DEV_BAD_TOKEN = 4,        /* a draft token outside [0, V)                            */
+  SV_DEV_BAD_TEMPERATURE = 8,  /* a T_b negative, not finite, or positive below FLT_MIN   */
+  SV_DEV_BAD_UNIFORM = 16      /* a uniform outside [0, 1) or NaN                         */
+};
+
+/* Limits checked on the host. */
+#define SV_MAX_K 64          /* k_max <= 64                                  */
+#define SV_MAX_BATCH 65536   /* B <= 65536                                   */
+#define SV_MAX_VOCAB (1 << 24)
+
+/* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
+ * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */
+size_t sv_workspace_size(int32_t B, int32_t k_max, int64_t V, int32_t dtype);
+
+/*
+ * sv_verify_block: verify B packed draft blocks.
+ *
+ *   dtype           SV_BF16 or SV_F32, the element type of both logit arrays.
+ *   B, k_max        requests in the batch; upper bound on every k_b (1..SV_MAX_K).
+ *   V               vocabulary size (columns read per row).
+ *   ld_target/ld_draft  row strides in elements (>= V).
+ *   n_draft_rows    sum_b k_b, as packed by the caller (the host knows it from the
+ *                   shapes it allocated; the device checks it against k).
+ *   target_logits   [n_draft_rows + B, ld_target]
+ *   draft_logits    [n_draft_rows, ld_draft]
+ *   k               int32[B], k_b in [1, k_max]
+ *   draft_tokens    int32[n_draft_rows], ids in [0, V)
+ *   uniforms        float[n_draft_rows + B] in [0, 1): slot i < k_b of a request is the
+ *                   acceptance uniform of draft i, slot k_b drives the final token.
+ *   temperature     float[B], T_b >= 0 (0 = greedy), or NULL for all 1.0.
+ *   delta           clip threshold of the reverse-KL (finite, > 0 when rkl_out != NULL).
+ * Outputs (device):
+ *   accept_len      int32[B]: a_b, the accepted drafts (0..k_b); -1 for an invalid request.
+ *   out_tokens      int32[n_draft_rows + B], per target row: the a_b accepted drafts, then
+ *                   the final token (residual resample or bonus), then -1.
+ *   rkl_out         float[n_draft_rows] clipped reverse-KL per draft row, or NULL to skip.
+ *   p_at_draft      float[n_draft_rows] p_T(x_i) (temperature-1 value for greedy
+ *                   requests), or NULL.
+ *   q_at_draft      float[n_draft_rows] q_T(x_i), likewise, or NULL.
+ *   device_status   int32[1]: OR of SV_DEV_* bits found by this call (required).
+ *   workspace       device scratch of >= sv_workspace_size(B, k_max, V, dtype) bytes,
+ *                   256-byte aligned.
+ *   stream          hipStream_t to enqueue on (NULL = null stream).
+ *
+ * Errors: host-checkable problems return SV_ERR_* and enqueue nothing.  Data-dependent
+ * problems never stop the device: an invalid request gets accept_len = -1, out_tokens
+ * = -1 and NaN probabilities (its rKL values are still computed); a void call (bad k or
+ * row count) writes -1 / NaN everywhere.  A failed launch returns SV_ERR_HIP.
+ */
+sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, int64_t ld_target,
+                          int64_t ld_draft, int64_t n_draft_rows, const void* target_logits,
+                          const void* draft_logits, const int32_t* k, const int32_t* draft_tokens,
+                          const float* uniforms, const float* temperature, float delta,
+                          int32_t* accept_len, int32_t* out_tokens, float* rkl_out,
+                          float* p_at_draft, float* q_at_draft, int32_t* device_status,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sv_clipped_rkl needs for n_rows row pairs; 0 if invalid. */
+size_t sv_rkl_workspace_size(int64_t n_rows, int64_t V, int32_t dtype);
+
+/*
+ * sv_clipped_rkl: the clipped reverse-KL alone (AdaFlash paper, Section 3.1), for an
+ * on-policy-distillation reader of the same logits.
+ *
+ *   n_rows          draft rows to score.
+ *   target_logits   [n_target_rows, ld_target]; draft_logits [n_rows, ld_draft].
+ *   p_row_index     int32[n_rows]: target row paired with draft row r, or NULL for r.
+ *                   Entries must lie in [0, n_target_rows).
+ *   n_target_rows   rows in target_logits (bounds p_row_index).
+ *   delta           finite, > 0.
+ *   rkl_out         float[n_rows].
+ *   device_status   int32[1]: SV_DEV_ROWS_MISMATCH if some p_row_index entry is out of
+ *                   range (that row's output is NaN).
+ */
+sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t V,
+                         int64_t ld_target, int64_t ld_draft, const void* target_logits,
+                         const void* draft_logits, const int32_t* p_row_index, float delta,
+                         float* rkl_out, int32_t* device_status, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* sv_status_string(sv_status s);
+
+/* Library version string. */
+const char* sv_version(void);
+
+/*
+ * Kernel timing (diagnostics).  When enabled, every kernel the library launches is
+ * bracketed by HIP events on the call's stream; sv_profile_get waits for those events
+ * and reports, per kernel name, the number of launches and their summed duration.
+ * Process-wide state, not thread-safe; off by default.
+ */
+sv_status sv_profile_enable(int32_t on);
+sv_status sv_profile_reset(void);
+int32_t sv_profile_count(void);
+sv_status sv_profile_get(int32_t index, char* name, size_t name_len, int64_t* launches,
+                         double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

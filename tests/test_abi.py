@@ -1,0 +1,103 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects
+host-checkable argument errors synchronously without touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import draft_block_verification_sv_amd as pkg
+
+    if not os.path.exists(pkg.library_path()):
+        pytest.skip("libspecverify.so not built (run __graft_entry__.build())")
+    return pkg.lib()
+
+
+def test_header_declares_the_boundary():
+    fns = _declared_functions()
+    for f in ("sv_verify_block", "sv_clipped_rkl", "sv_workspace_size", "sv_status_string"):
+        assert f in fns
+
+
+def test_every_declared_symbol_is_exported(L):
+    raw = ctypes.CDLL(L._name)
+    missing = [f for f in _declared_functions() if not hasattr(raw, f)]
+    assert not missing, missing
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.sv_status_string(s)
+    assert b"unknown" in L.sv_status_string(99)
+
+
+def test_workspace_size(L):
+    assert L.sv_workspace_size(128, 15, 151936, 0) > 0
+    assert L.sv_workspace_size(0, 15, 100, 0) == 0
+    assert L.sv_workspace_size(1, 0, 100, 0) == 0
+    assert L.sv_workspace_size(1, 65, 100, 0) == 0
+    assert L.sv_workspace_size(1, 4, 100, 7) == 0
+    assert L.sv_rkl_workspace_size(10, 1000, 1) > 0
+    assert L.sv_rkl_workspace_size(0, 1000, 1) == 0
+
+
+NULL6 = [None] * 6
+
+
+def _verify(L, dtype=0, B=1, k_max=4, V=100, ld_t=100, ld_d=100, n_d=1, ptrs=None, delta=1.0,
+            outs=None, ws=None, ws_bytes=0):
+    ptrs = ptrs if ptrs is not None else [8] * 5 + [None]  # fake, never dereferenced
+    outs = outs if outs is not None else [8, 8, None, None, None, 8]
+    return L.sv_verify_block(dtype, B, k_max, V, ld_t, ld_d, n_d, *ptrs, delta, *outs, ws,
+                             ws_bytes, None)
+
+
+def test_verify_argument_errors(L):
+    big = 1 << 40
+    assert _verify(L, dtype=3) == 3  # dtype
+    assert _verify(L, B=0) == 2
+    assert _verify(L, k_max=0) == 2
+    assert _verify(L, k_max=65) == 2
+    assert _verify(L, V=0) == 2
+    assert _verify(L, ld_t=99) == 2
+    assert _verify(L, ld_d=50) == 2
+    assert _verify(L, n_d=0) == 2  # fewer draft rows than requests
+    assert _verify(L, n_d=5) == 2  # more than B * k_max
+    assert _verify(L, ptrs=[None, 8, 8, 8, 8, None]) == 1
+    assert _verify(L, outs=[8, None, None, None, None, 8]) == 1
+    assert _verify(L, outs=[8, 8, None, None, None, None]) == 1  # device_status is required
+    assert _verify(L, outs=[8, 8, 8, None, None, 8], delta=float("nan")) == 4
+    assert _verify(L, outs=[8, 8, 8, None, None, 8], delta=0.0) == 4
+    assert _verify(L, ws=None, ws_bytes=big) == 5  # no workspace
+    assert _verify(L, ws=256 * 3 + 8, ws_bytes=big) == 5  # misaligned
+    assert _verify(L, ws=256 * 4, ws_bytes=16) == 5  # too small
+
+
+def test_rkl_argument_errors(L):
+    def call(dtype=1, n=2, nt=2, V=10, ldt=10, ldd=10, tp=8, dp=8, idx=None, delta=1.0, out=8,
+             st=8, ws=None, wsb=0):
+        return L.sv_clipped_rkl(dtype, n, nt, V, ldt, ldd, tp, dp, idx, delta, out, st, ws, wsb,
+                                None)
+
+    assert call(dtype=9) == 3
+    assert call(n=0) == 2
+    assert call(nt=1) == 2  # identity pairing needs n_target_rows >= n_rows
+    assert call(ldd=9) == 2
+    assert call(tp=None) == 1
+    assert call(out=None) == 1
+    assert call(delta=-1.0) == 4
+    assert call(delta=float("inf")) == 4
+    assert call(ws=None, wsb=1 << 30) == 5

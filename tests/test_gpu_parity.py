@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded
+inputs.  Needs an MI355X and the built library."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from synth import config, make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import compare, run_gpu, run_oracle, to_device  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_block_verification_sv_amd as pkg
+
+    pkg.lib()  # fails loudly if the library is not built
+
+
+def _report(name, s):
+    print(f"[parity] {name}: exact={s['exact']} flips={len(s['flips'])} "
+          f"max_p_rel={s['max_p_rel']:.2e} max_rkl_rel={s['max_rkl_rel']:.2e}", flush=True)
+
+
+# ----------------------------------------------------------------------------- small cases
+def test_config1_tiny_fp32():
+    w = config(1)
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("cfg1", s)
+    assert s["exact"] == 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_mixed_temperatures(dtype):
+    # several slices and a ragged tail (V not a multiple of 8), every temperature mode
+    w = make_workload(B=8, k=[1, 15, 3, 7, 2, 5, 1, 9], V=5003, dtype=dtype, s=3.0,
+                      sigma=[0.3, 0.8, 1.5, 0.5, 2.0, 1.0, 0.7, 1.2],
+                      temperature=[1.0, 0.0, 0.7, 1.3, 0.0, 0.5, 2.0, 1.0], delta=0.2,
+                      seed=(1, dtype == "bf16"))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report(f"ragged {dtype}", s)
+    assert s["exact"] >= w.B - 1
+
+
+@pytest.mark.parametrize("dtype,ld", [("bf16", 4104), ("bf16", 4097), ("f32", 4100), ("f32", 4099)])
+def test_padded_rows(dtype, ld):
+    # ld > V; padding columns hold +100 so a read past V would change every result
+    w = make_workload(B=3, k=[4, 2, 6], V=4093, ld=ld, dtype=dtype, s=4.0, sigma=1.0,
+                      temperature=[1.0, 0.7, 0.0], delta=0.5, seed=(2, ld))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report(f"padded {dtype} ld={ld}", s)
+
+
+@pytest.mark.parametrize("V", [1, 7, 64, 2048, 2049])
+def test_tiny_and_boundary_vocab(V):
+    w = make_workload(B=2, k=[1, 3], V=V, dtype="bf16", s=2.0, sigma=0.5, temperature=[1.0, 0.7],
+                      delta=1.0, seed=(3, V))
+    got = run_gpu(w)
+    s = compare(w, got, run_oracle(w))
+    _report(f"V={V}", s)
+
+
+@pytest.mark.parametrize("delta", [1e-3, 1e-2, 0.1])
+def test_small_delta_rereads_clipped_slices(delta):
+    # small delta makes many slices fail the no-clip bound and take the direct path
+    w = make_workload(B=3, k=[5, 3, 4], V=40000, dtype="bf16", s=4.0, sigma=[0.5, 1.0, 2.0],
+                      temperature=1.0, delta=delta, outlier_frac=0.1, seed=(4,))
+    got = run_gpu(w)
+    s = compare(w, got, run_oracle(w))
+    _report(f"delta={delta}", s)
+
+
+# ----------------------------------------------------------------------------- benchmark configs
+def test_config2_single_request():
+    w = config(2)
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("cfg2", s)
+
+
+def test_config3_ragged_batch():
+    w = config(3)
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("cfg3", s)
+    assert len(s["flips"]) <= 2
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    return config(4)
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    return config(5)
+
+
+def test_config4_full_size_sampled(cfg4):
+    w = cfg4
+    dev = to_device(w)
+    got = run_gpu(w, dev)
+    assert got["device_status"][0] == 0
+    # every request: structural properties
+    assert np.all((got["accept_len"] >= 0) & (got["accept_len"] <= 15))
+    assert np.all(np.isfinite(got["rkl"])) and np.all(got["rkl"] <= w.delta * w.V)
+    # a sample of requests against the oracle, one by one
+    sample = [0, 1, 17, 63, 64, 100, 126, 127]
+    s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
+    _report("cfg4 sampled", s)
+    # bitwise determinism at full size
+    again = run_gpu(w, dev)
+    for key in ("accept_len", "out_tokens", "rkl", "p_at_draft", "q_at_draft"):
+        np.testing.assert_array_equal(got[key], again[key])
+
+
+def test_config5_full_size_edge_cases(cfg5):
+    w = cfg5
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    aa, fr = w.meta["all_accept"], w.meta["first_reject"]
+    for b in aa:
+        assert got["accept_len"][b] == 15
+        d0 = int(w.draft_offsets[b])
+        assert np.all(got["rkl"][d0: d0 + 15] == 0.0)
+    for b in fr:
+        assert got["accept_len"][b] == 0
+    sample = sorted(set(aa[:2]) | set(fr[:2]) | {5, 77})
+    s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
+    _report("cfg5 sampled", s)
+
+
+# ----------------------------------------------------------------------------- edge cases
+def test_all_accept_and_bonus():
+    w = make_workload(B=2, k=[6, 15], V=3000, dtype="bf16", temperature=[1.0, 0.7],
+                      all_accept=(0, 1), seed=(5,))
+    got = run_gpu(w)
+    assert list(got["accept_len"]) == [6, 15]
+    assert np.all(got["rkl"] == 0.0)
+    compare(w, got, run_oracle(w))
+
+
+def test_greedy_trace(golden_dir):
+    with open(os.path.join(golden_dir, "dflash_notes_greedy_trace.json")) as f:
+        g = json.load(f)
+    w = make_workload(B=1, k=[g["block_drafts"]], V=3001, dtype="bf16", temperature=0.0,
+                      seed=(6,))
+    tgt = w.rows_f32("target", slice(0, 16)).astype(np.float64)
+    argmax_p = np.argmax(tgt, axis=1)
+    x = argmax_p[:15].copy()
+    for i, match in enumerate(g["match_pattern_prefix"]):
+        if not match:
+            x[i] = (argmax_p[i] + 1) % w.V
+    w.draft_tokens[:] = x
+    got = run_gpu(w)
+    assert got["accept_len"][0] == g["expected_accept_len"]
+    toks = got["out_tokens"]
+    assert int(np.count_nonzero(toks >= 0)) == g["expected_tokens_emitted"]
+    assert toks[4] == argmax_p[4]
+
+
+def test_invalid_requests_are_flagged_not_fatal():
+    w = make_workload(B=4, k=[2, 3, 2, 1], V=500, dtype="f32", seed=(7,))
+    w.draft_tokens[2] = 500  # request 1: token out of range
+    w.temperature[2] = -1.0  # request 2: negative temperature
+    w.uniforms[-1] = 1.0  # request 3: uniform out of range
+    got = run_gpu(w)
+    st = int(got["device_status"][0])
+    assert st & 4 and st & 8 and st & 16 and not (st & 3)
+    assert list(got["accept_len"][1:]) == [-1, -1, -1]
+    ref = run_oracle(w, requests=[0])
+    compare(w, got, ref, requests=[0])
+    assert np.all(np.isfinite(got["rkl"]))  # the divergence does not depend on tokens
+
+
+def test_void_calls():
+    w = make_workload(B=3, k=[2, 2, 2], V=300, dtype="bf16", seed=(8,))
+    bad = w.k.copy()
+    bad[1] = 0  # k_b outside [1, k_max]
+    dev = to_device(w)
+    dev["k"] = torch.from_numpy(bad).cuda()
+    got = run_gpu(w, dev, k_max=4)
+    assert int(got["device_status"][0]) & 1
+    assert np.all(got["accept_len"] == -1) and np.all(got["out_tokens"] == -1)
+    assert np.all(np.isnan(got["rkl"]))
+    mism = w.k.copy()
+    mism[1] = 3  # sum k_b != rows packed
+    dev["k"] = torch.from_numpy(mism).cuda()
+    got = run_gpu(w, dev, k_max=4)
+    assert int(got["device_status"][0]) & 2
+    assert np.all(got["accept_len"] == -1)
+
+
+def test_workspace_reuse_between_shapes():
+    import draft_block_verification_sv_amd as pkg
+
+    big = make_workload(B=4, k=[5, 5, 5, 5], V=6000, dtype="bf16", seed=(9,))
+    small = make_workload(B=2, k=[1, 4], V=6000, dtype="bf16", seed=(10,))
+    ws = pkg.alloc_workspace(pkg.workspace_size(4, 5, 6000, pkg.SV_BF16), "cuda")
+    a = run_gpu(big, workspace=ws)
+    b = run_gpu(small, workspace=ws)
+    compare(big, a, run_oracle(big))
+    compare(small, b, run_oracle(small))
+
+
+# ----------------------------------------------------------------------------- standalone rKL
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_clipped_rkl_standalone(dtype):
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=3, k=[3, 2, 4], V=7001, dtype=dtype, sigma=1.5, outlier_frac=0.1,
+                      seed=(11,))
+    d = to_device(w)
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, w.n_target_rows, size=w.n_draft_rows).astype(np.int32)
+    for delta in (1.0, 0.01):
+        out, st = pkg.clipped_rkl(d["target"], d["draft"], delta,
+                                  torch.from_numpy(idx).cuda())
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        got = out.cpu().numpy().astype(np.float64)
+        import oracle
+
+        tl = oracle.widen_logits(w.target[:, : w.V], dtype)
+        dl = oracle.widen_logits(w.draft[:, : w.V], dtype)
+        for r in range(w.n_draft_rows):
+            ref = oracle.clipped_rkl_row(tl[idx[r]], dl[r], delta)
+            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + 1e-9
+            assert abs(got[r] - ref["R"]) <= tol, (r, got[r], ref["R"])
+    # out-of-range pairing is flagged and gives NaN for that row only
+    idx[0] = w.n_target_rows
+    out, st = pkg.clipped_rkl(d["target"], d["draft"], 1.0, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    assert int(st.item()) & 2
+    o = out.cpu().numpy()
+    assert np.isnan(o[0]) and np.all(np.isfinite(o[1:]))
+
+
+def test_fused_rkl_equals_standalone():
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=4, k=[3, 1, 5, 2], V=9000, dtype="bf16", seed=(12,))
+    d = to_device(w)
+    got = run_gpu(w, d)
+    # standalone with the verification pairing: draft row of request b, position i -> target
+    # row off_t[b] + i
+    idx = np.concatenate([np.arange(w.target_offsets[b], w.target_offsets[b] + w.k[b])
+                          for b in range(w.B)]).astype(np.int32)
+    out, _ = pkg.clipped_rkl(d["target"], d["draft"], w.delta, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), got["rkl"])
