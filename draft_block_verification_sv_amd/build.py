@@ -9,8 +9,16 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = [os.path.join(PKG, "csrc", "sv_kernels.hip"), os.path.join(PKG, "csrc", "sv_api.cpp")]
-HEADERS = [os.path.join(PKG, "csrc", f) for f in ("sv_device.h", "sv_layout.h", "sv_launch.h")] + [
+CSRC = os.path.join(PKG, "csrc")
+# (source, extra flags).  The streaming kernel is built with IEEE mode off and NaN-free
+# arithmetic assumed (finite logits are part of the contract); the other kernels keep
+# IEEE semantics because they write and test NaN.
+SOURCES = [
+    (os.path.join(CSRC, "sv_rows.hip"), ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
+    (os.path.join(CSRC, "sv_kernels.hip"), []),
+    (os.path.join(CSRC, "sv_api.cpp"), []),
+]
+HEADERS = [os.path.join(CSRC, f) for f in ("sv_device.h", "sv_layout.h", "sv_launch.h")] + [
     os.path.join(ROOT, "include", "specverify.h")
 ]
 
@@ -19,7 +27,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # IEEE arithmetic as written: fused multiply-adds only where the source asks for them
     "-ffp-contract=off",
     # no packed fp32 instructions
@@ -34,9 +41,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +51,23 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build_library(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compiles each source to an object (own flags), links the shared library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    extra_defs = [f"-D{d}" for d in defines]
+    for src, extra in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        _run([hipcc(), *FLAGS, *extra, *extra_defs, "-I", os.path.join(ROOT, "include"), "-c", src,
+              "-o", obj], verbose)
+        objs.append(obj)
+    tmp = out + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -17,10 +17,12 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 6;
-const char* const kKernelNames[kNumKernels] = {"sv_plan",     "sv_rows",     "sv_finalize",
-                                               "sv_sample",   "sv_rkl_rows", "sv_rkl_finalize"};
-enum { K_PLAN, K_ROWS, K_FIN, K_SAMPLE, K_RKL_ROWS, K_RKL_FIN };
+constexpr int kNumKernels = 7;
+const char* const kKernelNames[kNumKernels] = {"sv_plan",          "sv_rows",
+                                               "sv_finalize",      "sv_sample_chunks",
+                                               "sv_sample_finish", "sv_rkl_rows",
+                                               "sv_rkl_finalize"};
+enum { K_PLAN, K_ROWS, K_FIN, K_SAMPLE_CHUNKS, K_SAMPLE_FINISH, K_RKL_ROWS, K_RKL_FIN };
 
 // ------------------------------------------------------------------ profiling
 struct ProfRec {
@@ -270,10 +272,13 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.acc = ws.acc;
   sa.chunk_r = ws.chunk_r;
   sa.chunk_p = ws.chunk_p;
-  sa.counters = ws.counters;
   sa.accept_len = accept_len;
   sa.out_tokens = out_tokens;
-  if (timed(K_SAMPLE, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) != hipSuccess)
+  if (timed(K_SAMPLE_CHUNKS, st, [&] { return sv::launch_sample_chunks(dtype, vec, sa, st); }) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  if (timed(K_SAMPLE_FINISH, st, [&] { return sv::launch_sample_finish(dtype, vec, sa, st); }) !=
+      hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

@@ -1,11 +1,11 @@
 // HIP kernels for batched draft-block verification on gfx950 (MI355X).
 //
-// One call of the verification path runs four kernels on the caller's stream:
+// One call of the verification path runs five kernels on the caller's stream:
 //
 //   sv_plan      one workgroup: packed-layout offsets from k (AdaFlash paper,
 //                Section 3.3: one batch of total length sum k_b), per-row
 //                descriptors, input validation.
-//   sv_rows      the streaming pass.  One wavefront per (row, 2048-column slice):
+//   sv_rows      the streaming pass (sv_rows.hip).  One wavefront per (row, slice):
 //                every target and draft logit is read from HBM exactly once, with
 //                16-byte loads, and reduced to per-slice statistics: max, the
 //                softmax sums at temperature 1 and T_b, the first argmax, and for
@@ -18,12 +18,13 @@
 //                slices where an entry could reach delta; the acceptance test
 //                u < min(1, p_T(x)/q_T(x)) (paper, Section 2.1) or, for T = 0, the
 //                argmax match (DFlash notes, Section 5.2, worked example #4).
-//   sv_sample    grid (request, chunk): the first-rejection scan, then per-chunk
-//                mass of the residual max(0, p_T - q_T) at the rejected position
-//                (reading notes, basic recipe step 4) or of p_T of the bonus row
-//                (DFlash notes, Section 3.1 step 6); the last workgroup of a
-//                request to arrive locates u * Z among the chunk masses and scans
-//                one chunk for the token, then emits a_b drafts + 1 token.
+//   sv_sample_chunks  grid (request, 2048-column chunk): the first-rejection scan,
+//                then the mass of each chunk of the residual max(0, p_T - q_T) at
+//                the rejected position (reading notes, basic recipe step 4) or of
+//                p_T of the bonus row (DFlash notes, Section 3.1 step 6).
+//   sv_sample_finish  one workgroup per request: locates u * Z among the chunk
+//                masses, scans that one chunk for the token, and emits a_b drafts
+//                + 1 token.
 //
 // Why W and G make one HBM pass enough for the clipped sum:
 //   t_y = q_y (ln q_y - ln p_y) = ln2 * 2^(k_y - LZq) * (L2E d_y + c2), with
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
   }
   __syncthreads();
   Workspace& ws = a.ws;
+  // 1. offsets: exclusive scan of k_b + 1 over the requests, 1024 at a time
   int carry = 0;
   for (int64_t base = 0; base < a.B; base += 1024) {
     const int64_t b = base + tid;
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
     ws.glob[0] = (bad_len || mismatch) ? 1 : 0;
   }
   if (!bad_len && !mismatch) {
+    // 2. per request: temperature mode, and the descriptor of each of its rows (stores only)
     for (int64_t b = tid; b < a.B; b += 1024) {
       const int off = ws.off_t[b];
       const int kb = a.k[b];
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
       int flags = 0, mode = 0;
       float beta = kL2E;
       if (!(T >= 0.0f) || isinf(T) || (T > 0.0f && T < FLT_MIN)) {
-        flags |= 8;
+        flags = 8;
       } else if (T == 0.0f) {
         mode = 1;
       } else if (T != 1.0f) {
@@ -115,240 +118,35 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
         beta = kL2E / T;
       }
       for (int i = 0; i <= kb; ++i) {
-        const int64_t t = static_cast<int64_t>(off) + i;
         RowDesc rd;
         rd.d = (i < kb) ? static_cast<int32_t>(off - b + i) : -1;
         rd.b = static_cast<int32_t>(b);
         rd.mode = mode;
         rd.beta = beta;
-        ws.desc[t] = rd;
-        const float u = a.uniforms[t];
-        if (!(u >= 0.0f && u < 1.0f)) flags |= 16;
-        if (i < kb) {
-          const int32_t x = a.tokens[off - b + i];
-          if (x < 0 || static_cast<int64_t>(x) >= a.V) flags |= 4;
-        }
+        ws.desc[off + i] = rd;
       }
       ws.req_flags[b] = flags;
-      ws.counters[b] = 0u;
       if (flags) atomicOr(&s_status, flags);
+    }
+    __syncthreads();  // descriptors and flags written above are visible to the whole block
+    // 3. per target row: the row's uniform, and the draft token it scores
+    const int64_t n_t = a.n_d + a.B;
+    for (int64_t t = tid; t < n_t; t += 1024) {
+      const RowDesc rd = ws.desc[t];
+      const float u = a.uniforms[t];
+      int f = (u >= 0.0f && u < 1.0f) ? 0 : 16;
+      if (rd.d >= 0) {
+        const int32_t x = a.tokens[rd.d];
+        if (x < 0 || static_cast<int64_t>(x) >= a.V) f |= 4;
+      }
+      if (f) {
+        atomicOr(&ws.req_flags[rd.b], f);
+        atomicOr(&s_status, f);
+      }
     }
   }
   __syncthreads();
   if (tid == 0) *a.device_status = s_status | (bad_len ? 1 : 0) | (mismatch ? 2 : 0);
-}
-
-// =========================================================================== rows
-// Loads the lane's 32 elements of one row slice (4 groups of 8 consecutive columns,
-// groups 512 columns apart) as fp32.  Columns >= V read as -inf.
-template <int DT, bool VEC, bool FULL>
-__device__ __forceinline__ void load_slice(const void* base, int64_t row_off, int64_t col_lane,
-                                           int V, float (&x)[kElemsPerLane]) {
-  if constexpr (DT == 0) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + row_off;
-    if constexpr (VEC && FULL) {
-      uint4 raw[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const uint4*>(p + col_lane + c * 512);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        x[c * 8 + 0] = bf16_lo(raw[c].x);
-        x[c * 8 + 1] = bf16_hi(raw[c].x);
-        x[c * 8 + 2] = bf16_lo(raw[c].y);
-        x[c * 8 + 3] = bf16_hi(raw[c].y);
-        x[c * 8 + 4] = bf16_lo(raw[c].z);
-        x[c * 8 + 5] = bf16_hi(raw[c].z);
-        x[c * 8 + 6] = bf16_lo(raw[c].w);
-        x[c * 8 + 7] = bf16_hi(raw[c].w);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t col = col_lane + c * 512;
-        if (VEC && col + 8 <= V) {
-          const uint4 r = *reinterpret_cast<const uint4*>(p + col);
-          x[c * 8 + 0] = bf16_lo(r.x);
-          x[c * 8 + 1] = bf16_hi(r.x);
-          x[c * 8 + 2] = bf16_lo(r.y);
-          x[c * 8 + 3] = bf16_hi(r.y);
-          x[c * 8 + 4] = bf16_lo(r.z);
-          x[c * 8 + 5] = bf16_hi(r.z);
-          x[c * 8 + 6] = bf16_lo(r.w);
-          x[c * 8 + 7] = bf16_hi(r.w);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[c * 8 + e] = (col + e < V) ? bf16_at(p + col + e) : -INFINITY;
-        }
-      }
-    }
-  } else {
-    const float* p = static_cast<const float*>(base) + row_off;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t col = col_lane + c * 512;
-      if (VEC && (FULL || col + 8 <= V)) {
-        const float4 r0 = *reinterpret_cast<const float4*>(p + col);
-        const float4 r1 = *reinterpret_cast<const float4*>(p + col + 4);
-        x[c * 8 + 0] = r0.x;
-        x[c * 8 + 1] = r0.y;
-        x[c * 8 + 2] = r0.z;
-        x[c * 8 + 3] = r0.w;
-        x[c * 8 + 4] = r1.x;
-        x[c * 8 + 5] = r1.y;
-        x[c * 8 + 6] = r1.z;
-        x[c * 8 + 7] = r1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[c * 8 + e] = (col + e < V) ? p[col + e] : -INFINITY;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ float lane_max(const float (&x)[kElemsPerLane]) {
-  float m0 = fmaxf(x[0], x[1]), m1 = fmaxf(x[2], x[3]);
-#pragma unroll
-  for (int j = 4; j < kElemsPerLane; j += 4) {
-    m0 = fmaxf(m0, fmaxf(x[j], x[j + 1]));
-    m1 = fmaxf(m1, fmaxf(x[j + 2], x[j + 3]));
-  }
-  return fmaxf(m0, m1);
-}
-
-// Statistics of one (row pair | bonus row) slice, written by lane 0 to record `rec`.
-template <int DT, bool VEC, bool FULL, bool PAIR, int MODE>
-__device__ __forceinline__ void slice_stats(const RowsArgs& a, int64_t t, int64_t d, float beta,
-                                            int64_t s, int lane, int64_t rec) {
-  const int64_t col_lane = s * kSlice + lane * 8;
-  float xp[kElemsPerLane], xq[kElemsPerLane];
-  load_slice<DT, VEC, FULL>(a.target, t * a.ld_t, col_lane, a.V, xp);
-  if constexpr (PAIR) load_slice<DT, VEC, FULL>(a.draft, d * a.ld_d, col_lane, a.V, xq);
-
-  const float mp = wave_max(lane_max(xp));
-  const float op = -(mp * kL2E);
-  float mq = 0.0f, oq = 0.0f;
-  if constexpr (PAIR) {
-    mq = wave_max(lane_max(xq));
-    oq = -(mq * kL2E);
-  }
-  float otp = 0.0f, otq = 0.0f;
-  if constexpr (MODE == 2) {
-    otp = -(mp * beta);
-    if constexpr (PAIR) otq = -(mq * beta);
-  }
-
-  float sp0 = 0.f, sp1 = 0.f, sq0 = 0.f, sq1 = 0.f, w0 = 0.f, w1 = 0.f, g = -INFINITY;
-  float stp0 = 0.f, stp1 = 0.f, stq0 = 0.f, stq1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < kElemsPerLane; j += 2) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = j + h;
-      const float ep = fast_exp2(__builtin_fmaf(xp[e], kL2E, op));
-      if (h == 0) sp0 += ep; else sp1 += ep;
-      if constexpr (MODE == 2) {
-        const float etp = fast_exp2(__builtin_fmaf(xp[e], beta, otp));
-        if (h == 0) stp0 += etp; else stp1 += etp;
-      }
-      if constexpr (PAIR) {
-        const float eq = fast_exp2(__builtin_fmaf(xq[e], kL2E, oq));
-        float diff = xq[e] - xp[e];
-        if constexpr (!FULL) {
-          const int64_t col = col_lane + (e >> 3) * 512 + (e & 7);
-          if (col >= a.V) diff = 0.0f;
-        }
-        const float pr = eq * diff;
-        if (h == 0) {
-          sq0 += eq;
-          w0 = __builtin_fmaf(eq, diff, w0);
-        } else {
-          sq1 += eq;
-          w1 = __builtin_fmaf(eq, diff, w1);
-        }
-        g = fmaxf(g, pr);
-        if constexpr (MODE == 2) {
-          const float etq = fast_exp2(__builtin_fmaf(xq[e], beta, otq));
-          if (h == 0) stq0 += etq; else stq1 += etq;
-        }
-      }
-    }
-  }
-  const float sp = wave_sum(sp0 + sp1);
-  float stp = 0.f, sq = 0.f, stq = 0.f, w = 0.f;
-  if constexpr (MODE == 2) stp = wave_sum(stp0 + stp1);
-  if constexpr (PAIR) {
-    sq = wave_sum(sq0 + sq1);
-    w = wave_sum(w0 + w1);
-    g = wave_max(g);
-    if constexpr (MODE == 2) stq = wave_sum(stq0 + stq1);
-  }
-  int arg = 0;
-  if constexpr (MODE == 1) {
-    int best = 0x7fffffff;
-#pragma unroll
-    for (int e = kElemsPerLane - 1; e >= 0; --e)
-      if (xp[e] == mp) best = static_cast<int>(col_lane + (e >> 3) * 512 + (e & 7));
-    arg = wave_min_i(best);
-  }
-  if (lane == 0) {
-    a.part.mp[rec] = mp;
-    a.part.sp[rec] = sp;
-    if constexpr (MODE == 2) a.part.stp[rec] = stp;
-    if constexpr (MODE == 1) a.part.ap[rec] = arg;
-    if constexpr (PAIR) {
-      a.part.mq[rec] = mq;
-      a.part.sq[rec] = sq;
-      a.part.w[rec] = w;
-      a.part.g[rec] = g;
-      if constexpr (MODE == 2) a.part.stq[rec] = stq;
-    }
-  }
-}
-
-template <int DT, bool VEC, bool FULL>
-__device__ __forceinline__ void slice_dispatch(const RowsArgs& a, int64_t t, int64_t d, int mode,
-                                               float beta, int64_t s, int lane, int64_t rec) {
-  if (d >= 0) {
-    if (mode == 0) slice_stats<DT, VEC, FULL, true, 0>(a, t, d, beta, s, lane, rec);
-    else if (mode == 1) slice_stats<DT, VEC, FULL, true, 1>(a, t, d, beta, s, lane, rec);
-    else slice_stats<DT, VEC, FULL, true, 2>(a, t, d, beta, s, lane, rec);
-  } else {
-    if (mode == 0) slice_stats<DT, VEC, FULL, false, 0>(a, t, d, beta, s, lane, rec);
-    else if (mode == 1) slice_stats<DT, VEC, FULL, false, 1>(a, t, d, beta, s, lane, rec);
-    else slice_stats<DT, VEC, FULL, false, 2>(a, t, d, beta, s, lane, rec);
-  }
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void sv_rows_kernel(RowsArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * kRowsWavesPerBlock + wave;
-  if (wave_id >= a.n_waves) return;
-  const uint32_t uw = static_cast<uint32_t>(wave_id);
-  const int64_t unit = uw / static_cast<uint32_t>(a.n_slices);
-  const int64_t s = uw - static_cast<uint32_t>(unit) * static_cast<uint32_t>(a.n_slices);
-  if (!a.desc && wave_id == 0 && lane == 0) *a.device_status = 0;
-  int64_t t, d;
-  int mode;
-  float beta;
-  if (a.desc) {  // verification: unit = target row
-    if (a.glob[0]) return;
-    const RowDesc rd = a.desc[unit];
-    t = unit;
-    d = rd.d;
-    mode = rd.mode;
-    beta = rd.beta;
-  } else {  // clipped reverse-KL only: unit = draft row
-    d = unit;
-    t = a.p_row_index ? a.p_row_index[unit] : unit;
-    if (t < 0 || t >= a.n_target_rows) return;
-    mode = 0;
-    beta = kL2E;
-  }
-  const int64_t rec = unit * a.n_slices + s;
-  if ((s + 1) * kSlice <= a.V) slice_dispatch<DT, VEC, true>(a, t, d, mode, beta, s, lane, rec);
-  else slice_dispatch<DT, VEC, false>(a, t, d, mode, beta, s, lane, rec);
 }
 
 // =========================================================================== finalize
@@ -409,7 +207,7 @@ __device__ double clipped_rkl_row(const FinArgs& a, int64_t t, int64_t d, int64_
       const float c2f = static_cast<float>(c2);
       const float deltaf = a.delta;
       float part = 0.0f;
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < kGroups; ++c) {
         for (int e = 0; e < 8; ++e) {
           const int64_t col = ss * kSlice + c * 512 + lane * 8 + e;
           if (col < a.V) {
@@ -579,42 +377,81 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int
   }
 }
 
+// The first rejected position of request b (k_b if none); read by thread 0.
+__device__ __forceinline__ int accept_length(const SampleArgs& a, int64_t b, int kb, int64_t off) {
+  int al = kb;
+  for (int i = 0; i < kb; ++i)
+    if (!a.acc[off - b + i]) {
+      al = i;
+      break;
+    }
+  return al;
+}
+
+// Chunk masses of the row the request draws its final token from.  Grid (request,
+// chunk); greedy, invalid and void requests have nothing to draw.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void sv_sample_kernel(SampleArgs a) {
+__global__ __launch_bounds__(256) void sv_sample_chunks_kernel(SampleArgs a) {
   const int64_t b = blockIdx.x;
   const int64_t c = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ double s_scan[4];
+  __shared__ int s_alen;
+  if (a.glob[0]) return;
+  const int kb = a.k[b];
+  const int64_t off = a.off_t[b];
+  if (a.req_flags[b] & kReqInvalid) return;
+  const RowDesc rd = a.desc[off];
+  if (rd.mode == 1) return;
+  if (tid == 0) s_alen = accept_length(a, b, kb, off);
+  __syncthreads();
+  const int alen = s_alen;
+  const int64_t t = off + alen;
+  const bool pair = alen < kb;
+  const int64_t d = off - b + alen;
+  const float offq = pair ? a.d_off[d] : 0.0f, lzq = pair ? a.d_lz[d] : 0.0f;
+  float r[8], pm[8];
+  chunk_masses<DT, VEC>(a, t, d, pair, rd.beta, a.t_off[t], a.t_lz[t], offq, lzq, c, tid, r, pm);
+  double rs = 0.0, ps = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rs += static_cast<double>(r[e]);
+    ps += static_cast<double>(pm[e]);
+  }
+  const double r_incl = block_inclusive_scan_256(rs, s_scan);
+  const double p_incl = block_inclusive_scan_256(ps, s_scan);
+  if (tid == kSampleThreads - 1) {
+    a.chunk_r[b * a.n_chunks + c] = r_incl;
+    a.chunk_p[b * a.n_chunks + c] = p_incl;
+  }
+}
+
+// One workgroup per request: first-rejection scan, inverse CDF over the chunk masses,
+// then over the 2048 columns of the chosen chunk; writes accept_len and out_tokens.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void sv_sample_finish_kernel(SampleArgs a) {
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ double s_scan[4];
   __shared__ double s_incl[kSampleThreads];
-  __shared__ int s_alen, s_last, s_cstar, s_usep, s_tok, s_fallback, s_lastpos;
+  __shared__ int s_alen, s_cstar, s_usep, s_tok, s_fallback, s_lastpos;
   __shared__ double s_thr;
 
   if (a.glob[0]) {  // void call
-    if (c == 0) {
-      if (tid == 0) a.accept_len[b] = -1;
-      for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t; t += static_cast<int64_t>(kSampleThreads) * a.B)
-        a.out_tokens[t] = -1;
-    }
+    if (tid == 0) a.accept_len[b] = -1;
+    for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
+         t += static_cast<int64_t>(kSampleThreads) * a.B)
+      a.out_tokens[t] = -1;
     return;
   }
   const int kb = a.k[b];
   const int64_t off = a.off_t[b];
   if (a.req_flags[b] & kReqInvalid) {
-    if (c == 0) {
-      if (tid == 0) a.accept_len[b] = -1;
-      for (int j = tid; j <= kb; j += kSampleThreads) a.out_tokens[off + j] = -1;
-    }
+    if (tid == 0) a.accept_len[b] = -1;
+    for (int j = tid; j <= kb; j += kSampleThreads) a.out_tokens[off + j] = -1;
     return;
   }
-  if (tid == 0) {
-    int al = kb;
-    for (int i = 0; i < kb; ++i)
-      if (!a.acc[off - b + i]) {
-        al = i;
-        break;
-      }
-    s_alen = al;
-  }
+  if (tid == 0) s_alen = accept_length(a, b, kb, off);
   __syncthreads();
   const int alen = s_alen;
   const RowDesc rd = a.desc[off];
@@ -629,33 +466,9 @@ __global__ __launch_bounds__(256) void sv_sample_kernel(SampleArgs a) {
   };
 
   if (rd.mode == 1) {  // greedy: the target argmax at the first mismatch (or the bonus row)
-    if (c == 0) emit(a.t_arg[t]);
+    emit(a.t_arg[t]);
     return;
   }
-
-  const float beta = rd.beta;
-  const float offp = a.t_off[t], lzp = a.t_lz[t];
-  const float offq = pair ? a.d_off[d] : 0.0f, lzq = pair ? a.d_lz[d] : 0.0f;
-  float r[8], pm[8];
-  chunk_masses<DT, VEC>(a, t, d, pair, beta, offp, lzp, offq, lzq, c, tid, r, pm);
-  double rs = 0.0, ps = 0.0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    rs += static_cast<double>(r[e]);
-    ps += static_cast<double>(pm[e]);
-  }
-  const double r_incl = block_inclusive_scan_256(rs, s_scan);
-  const double p_incl = block_inclusive_scan_256(ps, s_scan);
-  if (tid == kSampleThreads - 1) {
-    a.chunk_r[b * a.n_chunks + c] = r_incl;
-    a.chunk_p[b * a.n_chunks + c] = p_incl;
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.counters[b], 1u);
-    s_last = (prev == static_cast<unsigned>(a.n_chunks - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
 
   if (tid == 0) {
     const double* cr = a.chunk_r + b * a.n_chunks;
@@ -670,9 +483,8 @@ __global__ __launch_bounds__(256) void sv_sample_kernel(SampleArgs a) {
     }
     const double* cm = usep ? cp : cr;
     const double thr = static_cast<double>(a.uniforms[off + kb]) * Z;
-    double cum = 0.0;
+    double cum = 0.0, before = 0.0;
     int cstar = -1, fallback = 0;
-    double before = 0.0;
     for (int64_t cc = 0; cc < a.n_chunks; ++cc) {
       const double nxt = cum + cm[cc];
       if (nxt > thr) {
@@ -696,12 +508,15 @@ __global__ __launch_bounds__(256) void sv_sample_kernel(SampleArgs a) {
     s_thr = thr - before;
     s_fallback = fallback;
     s_tok = 0x7fffffff;
-    a.counters[b] = 0u;
+    s_lastpos = -1;
   }
   __syncthreads();
   const int cstar = s_cstar;
   const bool usep = s_usep != 0;
-  chunk_masses<DT, VEC>(a, t, d, pair, beta, offp, lzp, offq, lzq, cstar, tid, r, pm);
+  const float offq = pair ? a.d_off[d] : 0.0f, lzq = pair ? a.d_lz[d] : 0.0f;
+  float r[8], pm[8];
+  chunk_masses<DT, VEC>(a, t, d, pair, rd.beta, a.t_off[t], a.t_lz[t], offq, lzq, cstar, tid, r,
+                        pm);
   double mine[8];
   double tsum = 0.0;
 #pragma unroll
@@ -733,42 +548,23 @@ __global__ __launch_bounds__(256) void sv_sample_kernel(SampleArgs a) {
         }
     if (found >= 0) atomicMin(&s_tok, static_cast<int>(col0 + found));
   }
+  int last = -1;
+  for (int e = 7; e >= 0; --e)
+    if (mine[e] > 0.0) {
+      last = static_cast<int>(col0 + e);
+      break;
+    }
+  if (last >= 0) atomicMax(&s_lastpos, last);
   __syncthreads();
-  if (s_tok == 0x7fffffff) {  // fallback: the chunk's last id with positive mass
-    int last = -1;
-    for (int e = 7; e >= 0; --e)
-      if (mine[e] > 0.0) {
-        last = static_cast<int>(col0 + e);
-        break;
-      }
-    if (tid == 0) s_lastpos = -1;
-    __syncthreads();
-    if (last >= 0) atomicMax(&s_lastpos, last);
-    __syncthreads();
-    if (tid == 0) s_tok = s_lastpos < 0 ? 0 : s_lastpos;
-    __syncthreads();
-  }
-  emit(s_tok);
+  // no thread claimed u * Z (rounding): the chunk's last id with positive mass
+  const int tok = (s_tok != 0x7fffffff) ? s_tok : (s_lastpos < 0 ? 0 : s_lastpos);
+  emit(tok);
 }
 
 // =========================================================================== launchers
-template <int DT, bool VEC>
-static hipError_t launch_rows_t(const RowsArgs& a, hipStream_t st) {
-  const int64_t blocks = (a.n_waves + kRowsWavesPerBlock - 1) / kRowsWavesPerBlock;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((sv_rows_kernel<DT, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     st, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(sv_plan_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
-}
-
-hipError_t launch_rows(int dtype, bool vec, const RowsArgs& a, hipStream_t st) {
-  if (dtype == 0) return vec ? launch_rows_t<0, true>(a, st) : launch_rows_t<0, false>(a, st);
-  return vec ? launch_rows_t<1, true>(a, st) : launch_rows_t<1, false>(a, st);
 }
 
 hipError_t launch_finalize(int dtype, const FinArgs& a, hipStream_t st) {
@@ -781,13 +577,24 @@ hipError_t launch_finalize(int dtype, const FinArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
+hipError_t launch_sample_chunks(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B), static_cast<unsigned>(a.n_chunks));
   if (dtype == 0) {
-    if (vec) hipLaunchKernelGGL((sv_sample_kernel<0, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((sv_sample_kernel<0, false>), grid, dim3(256), 0, st, a);
+    if (vec) hipLaunchKernelGGL((sv_sample_chunks_kernel<0, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((sv_sample_chunks_kernel<0, false>), grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((sv_sample_kernel<1, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((sv_sample_chunks_kernel<1, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_finish(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B));
+  if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_sample_finish_kernel<0, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((sv_sample_finish_kernel<0, false>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((sv_sample_finish_kernel<1, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

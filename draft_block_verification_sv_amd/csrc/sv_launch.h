@@ -88,7 +88,6 @@ struct SampleArgs {
   const int32_t* acc;
   double* chunk_r;
   double* chunk_p;
-  uint32_t* counters;
   int32_t* accept_len;
   int32_t* out_tokens;
 };
@@ -96,6 +95,7 @@ struct SampleArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_rows(int dtype, bool vec, const RowsArgs& a, hipStream_t st);
 hipError_t launch_finalize(int dtype, const FinArgs& a, hipStream_t st);
-hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
+hipError_t launch_sample_chunks(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
+hipError_t launch_sample_finish(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 
 }  // namespace sv

@@ -8,10 +8,16 @@
 namespace sv {
 
 // The streaming kernel gives one wavefront one slice of one row (pair): 64 lanes x
-// 32 elements.  A bf16 slice of a row pair is 8 KiB read with eight 16-byte loads
-// per lane, all issued before any arithmetic.
-constexpr int kElemsPerLane = 32;
-constexpr int kSlice = 64 * kElemsPerLane;  // 2048 columns
+// kElemsPerLane elements, in groups of 8 consecutive columns 512 columns apart.  At
+// 32 elements a bf16 slice of a row pair is 8 KiB, read with eight 16-byte loads per
+// lane, all issued before any arithmetic.
+#ifndef SV_ELEMS_PER_LANE
+#define SV_ELEMS_PER_LANE 32
+#endif
+constexpr int kElemsPerLane = SV_ELEMS_PER_LANE;
+static_assert(kElemsPerLane % 8 == 0 && kElemsPerLane >= 8, "groups of 8 columns per lane");
+constexpr int kGroups = kElemsPerLane / 8;
+constexpr int kSlice = 64 * kElemsPerLane;
 constexpr int kRowsWavesPerBlock = 4;       // 256-thread workgroups
 // The sampler gives one 256-thread workgroup 2048 columns (8 per thread).
 constexpr int kChunk = 2048;
@@ -50,7 +56,6 @@ struct Workspace {
   int32_t* glob;       // [4]: [0] call void (bad lengths / row count)
   int32_t* off_t;      // [B + 1] first target row of each request
   int32_t* req_flags;  // [B] SV_DEV_* bits of each request
-  uint32_t* counters;  // [B] sampler arrival counters
   RowDesc* desc;       // [n_t]
   Partials part;       // [n_units * n_slices] each
   float* t_off;        // [n_t] -(M * beta) for the sampler's temperature
@@ -81,7 +86,6 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.glob = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
   w.off_t = reinterpret_cast<int32_t*>(take((d.B + 1) * sizeof(int32_t)));
   w.req_flags = reinterpret_cast<int32_t*>(take(d.B * sizeof(int32_t)));
-  w.counters = reinterpret_cast<uint32_t*>(take(d.B * sizeof(uint32_t)));
   w.desc = reinterpret_cast<RowDesc*>(take(d.n_t * sizeof(RowDesc)));
   w.part.mp = reinterpret_cast<float*>(take(np * 4));
   w.part.sp = reinterpret_cast<float*>(take(np * 4));

@@ -9,7 +9,13 @@ Comparison rules (fp32 GPU against the float64 oracle):
   reported, and the rest of that request is not compared.  Greedy decisions have
   infinite margin and must always match.
 * p_T(x_i), q_T(x_i): |got - ref| <= 1e-5 |ref|.
-* clipped reverse-KL: |got - ref| <= 1e-5 max(|ref|, sum_y |min(delta, t_y)|).
+* clipped reverse-KL: |got - ref| <= 1e-5 max(|ref|, sum_y |min(delta, t_y)|) + 2^-21.
+  The absolute floor is the resolution of fp32 accumulation itself: each row's
+  log-normaliser comes from fp32 exponentials and fp32 slice sums (relative error
+  ~1e-7 of the sum), and an error eps in LZ_p - LZ_q moves R by ln2 * eps because
+  R = E_q[ln q - ln p] contains that difference with weight sum_y q_y = 1.  Rows whose
+  divergence is below ~1e-2 (nearly identical q and p, or V = 1) would otherwise be held
+  to an absolute accuracy fp32 cannot express.
 """
 
 from __future__ import annotations
@@ -21,6 +27,7 @@ import oracle
 
 MARGIN = 1e-5
 RTOL = 1e-5
+RKL_ABS = 2.0**-21
 
 
 def to_device(w, dev="cuda:0"):
@@ -105,6 +112,6 @@ def compare(w, got, ref, requests=None, check_rkl=True):
             g = got["rkl"][sl].astype(np.float64)
             scale = np.maximum(np.abs(r), ref["rkl_l1"][sl])
             err = np.abs(g - r)
-            assert np.all(err <= RTOL * scale + 1e-9), (b, g, r, err / scale)
+            assert np.all(err <= RTOL * scale + RKL_ABS), (b, g, r, err / scale)
             max_rkl_rel = max(max_rkl_rel, float(np.max(err / np.maximum(scale, 1e-30))))
     return dict(exact=exact, flips=flips, max_p_rel=max_p_rel, max_rkl_rel=max_rkl_rel)
