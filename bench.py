@@ -85,7 +85,21 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=32)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+
+        n = args.calibrate_copy // 4
+        x = torch.ones(n, dtype=torch.int32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verification path is per-GPU data-parallel "
