@@ -10,7 +10,7 @@ V=151936, bf16 logits, drafter noise sigma_b in {0.5, 1, 2}, delta=1, seeded
 synthetic inputs (see synth/workloads.py).  Prints one JSON line on stdout;
 progress goes to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload high_concurrency] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -27,9 +27,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=128 k=15 V=151936"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "sv_rows_cfg4_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "sv_rowpair_b128_k15_v151936_counters.json")
+STREAM_KERNEL = "sv_rowpair"  # the kernel that streams the logits: the roofline kernel
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_verification_sv_amd", "csrc", f)
-                  for f in ("sv_kernels.hip", "sv_device.h", "sv_layout.h", "sv_launch.h")]
+                  for f in ("sv_rowpair.hip", "sv_kernels.hip", "sv_device.h", "sv_layout.h",
+                            "sv_launch.h")]
 
 
 def log(*a):
@@ -82,9 +84,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--workload", default="high_concurrency")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=32)
+    ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -111,10 +113,10 @@ def main():
     import torch
 
     import draft_block_verification_sv_amd as pkg
-    from synth import config
+    from synth import workload
 
     t0 = time.perf_counter()
-    w = config(args.config)
+    w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
     cpu = None
     if not args.no_cpu_baseline:
@@ -184,13 +186,13 @@ def main():
     esize = 2 if w.dtype == "bf16" else 4
     rows_bytes = (w.n_target_rows + n_d) * V * esize  # every logit read once
     meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
-    rows_us = kernels["sv_rows"]["avg_us"]
+    rows_us = kernels[STREAM_KERNEL]["avg_us"]
     achieved = rows_bytes / (rows_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
-        if c.get("kernel_source_hash") == kernel_source_hash() and c.get("config") == args.config:
+        if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == args.workload:
             traffic = c.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}

@@ -17,12 +17,10 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 7;
-const char* const kKernelNames[kNumKernels] = {"sv_plan",          "sv_rows",
-                                               "sv_finalize",      "sv_sample_chunks",
-                                               "sv_sample_finish", "sv_rkl_rows",
-                                               "sv_rkl_finalize"};
-enum { K_PLAN, K_ROWS, K_FIN, K_SAMPLE_CHUNKS, K_SAMPLE_FINISH, K_RKL_ROWS, K_RKL_FIN };
+constexpr int kNumKernels = 5;
+const char* const kKernelNames[kNumKernels] = {"sv_plan", "sv_rowpair", "sv_sample",
+                                               "sv_rkl_rowpair", "sv_rkl_status"};
+enum { K_PLAN, K_ROWPAIR, K_SAMPLE, K_RKL_ROWPAIR, K_RKL_STATUS };
 
 // ------------------------------------------------------------------ profiling
 struct ProfRec {
@@ -129,7 +127,8 @@ Dims rkl_dims(int64_t n_rows, int64_t V) {
 }
 
 bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
-  return V >= 1 && V <= SV_MAX_VOCAB && ld_t >= V && ld_d >= V;
+  return V >= 1 && V <= SV_MAX_VOCAB && sv::n_slices_for(V) <= sv::kMaxSlices &&
+         sv::n_chunks_for(V) <= sv::kMaxChunks && ld_t >= V && ld_d >= V;
 }
 
 }  // namespace
@@ -152,15 +151,15 @@ const char* sv_status_string(sv_status s) {
 }
 
 size_t sv_workspace_size(int32_t B, int32_t k_max, int64_t V, int32_t dtype) {
-  if (!dtype_ok(dtype) || B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || V < 1 ||
-      V > SV_MAX_VOCAB)
+  if (!dtype_ok(dtype) || B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K ||
+      !shape_ok(V, V, V))
     return 0;
   return sv::carve(verify_dims(B, k_max, V), nullptr, nullptr);
 }
 
 size_t sv_rkl_workspace_size(int64_t n_rows, int64_t V, int32_t dtype) {
-  if (!dtype_ok(dtype) || n_rows < 1 || V < 1 || V > SV_MAX_VOCAB) return 0;
-  if (n_rows * sv::n_slices_for(V) >= (int64_t(1) << 31)) return 0;
+  if (!dtype_ok(dtype) || n_rows < 1 || n_rows >= (int64_t(1) << 31) || !shape_ok(V, V, V))
+    return 0;
   return sv::carve(rkl_dims(n_rows, V), nullptr, nullptr);
 }
 
@@ -176,7 +175,6 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
     return SV_ERR_SHAPE;
   if (n_draft_rows < B || n_draft_rows > static_cast<int64_t>(B) * k_max) return SV_ERR_SHAPE;
   const Dims dm = verify_dims(B, k_max, V);
-  if (dm.n_units * dm.n_slices >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
   if (!target_logits || !draft_logits || !k || !draft_tokens || !uniforms || !accept_len ||
       !out_tokens || !device_status)
     return SV_ERR_NULL;
@@ -192,60 +190,51 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
   const int64_t n_slices = dm.n_slices, n_chunks = dm.n_chunks;
 
-  sv::PlanArgs pa{};
-  pa.B = B;
-  pa.k_max = k_max;
-  pa.V = V;
-  pa.n_d = n_d;
-  pa.k = k;
-  pa.tokens = draft_tokens;
-  pa.uniforms = uniforms;
-  pa.temperature = temperature;
-  pa.ws = ws;
-  pa.device_status = device_status;
-  if (timed(K_PLAN, st, [&] { return sv::launch_plan(pa, st); }) != hipSuccess) return SV_ERR_HIP;
+  const bool inline_plan = B <= sv::kInlinePlanMaxB;
+  if (!inline_plan) {
+    sv::PlanArgs pa{};
+    pa.B = B;
+    pa.k_max = k_max;
+    pa.n_d = n_d;
+    pa.k = k;
+    pa.ws = ws;
+    pa.device_status = device_status;
+    if (timed(K_PLAN, st, [&] { return sv::launch_plan(pa, st); }) != hipSuccess) return SV_ERR_HIP;
+  }
 
-  sv::RowsArgs ra{};
+  sv::RowPairArgs ra{};
   ra.target = target_logits;
   ra.draft = draft_logits;
   ra.ld_t = ld_target;
   ra.ld_d = ld_draft;
   ra.V = static_cast<int32_t>(V);
   ra.n_slices = n_slices;
-  ra.n_waves = n_t * n_slices;
-  ra.desc = ws.desc;
+  ra.n_units = n_t;
+  ra.B = B;
+  ra.k_max = k_max;
+  ra.n_d = n_d;
+  ra.k = k;
+  ra.tokens = draft_tokens;
+  ra.uniforms = uniforms;
+  ra.temperature = temperature;
+  ra.desc = inline_plan ? nullptr : ws.desc;
   ra.glob = ws.glob;
-  ra.part = ws.part;
-  if (timed(K_ROWS, st, [&] { return sv::launch_rows(dtype, vec, ra, st); }) != hipSuccess)
-    return SV_ERR_HIP;
-
-  sv::FinArgs fa{};
-  fa.target = target_logits;
-  fa.draft = draft_logits;
-  fa.ld_t = ld_target;
-  fa.ld_d = ld_draft;
-  fa.V = static_cast<int32_t>(V);
-  fa.n_slices = n_slices;
-  fa.n_units = n_t;
-  fa.n_d = n_d;
-  fa.desc = ws.desc;
-  fa.glob = ws.glob;
-  fa.req_flags = ws.req_flags;
-  fa.tokens = draft_tokens;
-  fa.uniforms = uniforms;
-  fa.device_status = device_status;
-  fa.part = ws.part;
-  fa.delta = delta;
-  fa.rkl_out = rkl_out;
-  fa.p_at = p_at_draft;
-  fa.q_at = q_at_draft;
-  fa.t_off = ws.t_off;
-  fa.t_lz = ws.t_lz;
-  fa.t_arg = ws.t_arg;
-  fa.d_off = ws.d_off;
-  fa.d_lz = ws.d_lz;
-  fa.acc = ws.acc;
-  if (timed(K_FIN, st, [&] { return sv::launch_finalize(dtype, fa, st); }) != hipSuccess)
+  ra.off_t = ws.off_t;
+  ra.rkl_only = false;
+  ra.delta = delta;
+  ra.rkl_out = rkl_out;
+  ra.p_at = p_at_draft;
+  ra.q_at = q_at_draft;
+  ra.device_status = device_status;
+  ra.row_flags = ws.row_flags;
+  ra.t_off = ws.t_off;
+  ra.t_lz = ws.t_lz;
+  ra.t_beta = ws.t_beta;
+  ra.t_arg = ws.t_arg;
+  ra.d_off = ws.d_off;
+  ra.d_lz = ws.d_lz;
+  ra.acc = ws.acc;
+  if (timed(K_ROWPAIR, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
     return SV_ERR_HIP;
 
   sv::SampleArgs sa{};
@@ -260,25 +249,23 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.glob = ws.glob;
   sa.off_t = ws.off_t;
   sa.k = k;
-  sa.req_flags = ws.req_flags;
-  sa.desc = ws.desc;
+  sa.temperature = temperature;
   sa.tokens = draft_tokens;
   sa.uniforms = uniforms;
+  sa.row_flags = ws.row_flags;
   sa.t_off = ws.t_off;
   sa.t_lz = ws.t_lz;
+  sa.t_beta = ws.t_beta;
   sa.t_arg = ws.t_arg;
   sa.d_off = ws.d_off;
   sa.d_lz = ws.d_lz;
   sa.acc = ws.acc;
-  sa.chunk_r = ws.chunk_r;
-  sa.chunk_p = ws.chunk_p;
   sa.accept_len = accept_len;
   sa.out_tokens = out_tokens;
-  if (timed(K_SAMPLE_CHUNKS, st, [&] { return sv::launch_sample_chunks(dtype, vec, sa, st); }) !=
-      hipSuccess)
-    return SV_ERR_HIP;
-  if (timed(K_SAMPLE_FINISH, st, [&] { return sv::launch_sample_finish(dtype, vec, sa, st); }) !=
-      hipSuccess)
+  sa.p_at = p_at_draft;
+  sa.q_at = q_at_draft;
+  sa.device_status = device_status;
+  if (timed(K_SAMPLE, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }
@@ -291,8 +278,8 @@ sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, i
   if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
   if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
   if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
+  if (n_rows >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
   const Dims dm = rkl_dims(n_rows, V);
-  if (dm.n_units * dm.n_slices >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
   if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
   if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
   const size_t need = sv::carve(dm, nullptr, nullptr);
@@ -304,39 +291,27 @@ sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, i
   sv::carve(dm, &ws, static_cast<char*>(workspace));
   const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
 
-  sv::RowsArgs ra{};
+  sv::RowPairArgs ra{};
   ra.target = target_logits;
   ra.draft = draft_logits;
   ra.ld_t = ld_target;
   ra.ld_d = ld_draft;
   ra.V = static_cast<int32_t>(V);
   ra.n_slices = dm.n_slices;
-  ra.n_waves = n_rows * dm.n_slices;
-  ra.desc = nullptr;
-  ra.glob = nullptr;
+  ra.n_units = n_rows;
+  ra.rkl_only = true;
   ra.p_row_index = p_row_index;
   ra.n_target_rows = n_target_rows;
+  ra.delta = delta;
+  ra.rkl_out = rkl_out;
   ra.device_status = device_status;
-  ra.part = ws.part;
-  if (timed(K_RKL_ROWS, st, [&] { return sv::launch_rows(dtype, vec, ra, st); }) != hipSuccess)
+  ra.row_flags = ws.row_flags;
+  if (timed(K_RKL_ROWPAIR, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) !=
+      hipSuccess)
     return SV_ERR_HIP;
-
-  sv::FinArgs fa{};
-  fa.target = target_logits;
-  fa.draft = draft_logits;
-  fa.ld_t = ld_target;
-  fa.ld_d = ld_draft;
-  fa.V = static_cast<int32_t>(V);
-  fa.n_slices = dm.n_slices;
-  fa.n_units = n_rows;
-  fa.desc = nullptr;
-  fa.p_row_index = p_row_index;
-  fa.n_target_rows = n_target_rows;
-  fa.device_status = device_status;
-  fa.part = ws.part;
-  fa.delta = delta;
-  fa.rkl_out = rkl_out;
-  if (timed(K_RKL_FIN, st, [&] { return sv::launch_finalize(dtype, fa, st); }) != hipSuccess)
+  if (timed(K_RKL_STATUS, st,
+            [&] { return sv::launch_status(ws.row_flags, n_rows, device_status, st); }) !=
+      hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

@@ -1,6 +1,6 @@
-// Device helpers for the gfx950 (CDNA4) verification kernels: bf16 unpacking,
+// Device helpers for the gfx950 (CDNA4) verification kernels: bf16 unpacking and
 // 64-lane wavefront reductions built from DPP row permutes and the gfx950
-// permlane16/32 swaps, and a fixed-order fp64 block scan.
+// permlane16/32 swaps.
 //
 // Every reduction here has a fixed combination tree, so results are bitwise
 // reproducible run to run (no atomics on floating-point data anywhere).
@@ -93,24 +93,6 @@ __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
   return v;
-}
-
-// Inclusive scan over a 256-thread block in fp64, fixed order (Hillis-Steele inside
-// each wave, then the four wave totals).  `lds` holds 4 doubles.
-__device__ __forceinline__ double block_inclusive_scan_256(double v, double* lds) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    double o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  if (lane == kWave - 1) lds[wave] = v;
-  __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < wave; ++w) base += lds[w];
-  __syncthreads();
-  return base + v;
 }
 
 }  // namespace sv

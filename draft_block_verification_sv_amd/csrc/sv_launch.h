@@ -11,54 +11,44 @@ namespace sv {
 struct PlanArgs {
   int64_t B;
   int32_t k_max;
-  int64_t V;
+  int64_t n_d;
+  const int32_t* k;
+  Workspace ws;
+  int32_t* device_status;
+};
+
+struct RowPairArgs {
+  const void* target;
+  const void* draft;
+  int64_t ld_t, ld_d;
+  int32_t V;
+  int64_t n_slices;
+  int64_t n_units;  // workgroups: target rows (verification) or draft rows (rKL only)
+  // verification
+  int64_t B;
+  int32_t k_max;
   int64_t n_d;
   const int32_t* k;
   const int32_t* tokens;
   const float* uniforms;
   const float* temperature;  // nullable
-  Workspace ws;
-  int32_t* device_status;
-};
-
-struct RowsArgs {
-  const void* target;
-  const void* draft;
-  int64_t ld_t, ld_d;
-  int32_t V;
-  int64_t n_slices;
-  int64_t n_waves;            // n_units * n_slices (< 2^31)
-  const RowDesc* desc;        // verification: per target row; nullptr for rKL only
-  const int32_t* glob;        // verification: void flag
-  const int32_t* p_row_index; // rKL only (nullable = identity)
-  int64_t n_target_rows;      // rKL only: bound for p_row_index
-  int32_t* device_status;     // rKL only: reset by the first wave
-  Partials part;
-};
-
-struct FinArgs {
-  const void* target;
-  const void* draft;
-  int64_t ld_t, ld_d;
-  int32_t V;
-  int64_t n_slices;
-  int64_t n_units;
-  int64_t n_d;
-  const RowDesc* desc;  // nullptr for rKL only
-  const int32_t* glob;
-  const int32_t* req_flags;
-  const int32_t* tokens;
-  const float* uniforms;
-  const int32_t* p_row_index;
+  const RowDesc* desc;       // nullptr: every workgroup scans k itself
+  int32_t* glob;
+  int32_t* off_t;
+  // clipped reverse-KL only
+  bool rkl_only;
+  const int32_t* p_row_index;  // nullable = identity
   int64_t n_target_rows;
-  int32_t* device_status;
-  Partials part;
+  // outputs
   float delta;
   float* rkl_out;  // nullable in verification
   float* p_at;     // nullable
   float* q_at;     // nullable
+  int32_t* device_status;
+  int32_t* row_flags;
   float* t_off;
   float* t_lz;
+  float* t_beta;
   int32_t* t_arg;
   float* d_off;
   float* d_lz;
@@ -76,26 +66,27 @@ struct SampleArgs {
   const int32_t* glob;
   const int32_t* off_t;
   const int32_t* k;
-  const int32_t* req_flags;
-  const RowDesc* desc;
+  const float* temperature;
   const int32_t* tokens;
   const float* uniforms;
+  const int32_t* row_flags;
   const float* t_off;
   const float* t_lz;
+  const float* t_beta;
   const int32_t* t_arg;
   const float* d_off;
   const float* d_lz;
   const int32_t* acc;
-  double* chunk_r;
-  double* chunk_p;
   int32_t* accept_len;
   int32_t* out_tokens;
+  float* p_at;
+  float* q_at;
+  int32_t* device_status;
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
-hipError_t launch_rows(int dtype, bool vec, const RowsArgs& a, hipStream_t st);
-hipError_t launch_finalize(int dtype, const FinArgs& a, hipStream_t st);
-hipError_t launch_sample_chunks(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
-hipError_t launch_sample_finish(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
+hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
+hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
+hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 
 }  // namespace sv

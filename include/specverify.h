@@ -87,7 +87,7 @@ enum {
 /* Limits checked on the host. */
 #define SV_MAX_K 64          /* k_max <= 64                                  */
 #define SV_MAX_BATCH 65536   /* B <= 65536                                   */
-#define SV_MAX_VOCAB (1 << 24)
+#define SV_MAX_VOCAB (1 << 19) /* 524288 */
 
 /* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
  * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */

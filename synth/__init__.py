@@ -7,9 +7,9 @@ the method's code.
 """
 
 from .workloads import (  # noqa: F401
-    CONFIG_NAMES,
+    WORKLOADS,
     Workload,
-    config,
+    workload,
     make_workload,
     bf16_bits_from_f64,
     bf16_bits_to_f32,

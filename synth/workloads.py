@@ -40,12 +40,15 @@ import numpy as np
 
 ROOT_SEED = 20261202
 
-CONFIG_NAMES = {
-    1: "tiny: B=1 k=4 V=1000 fp32",
-    2: "single request: B=1 k=15 V=151936 bf16, sigma rising 0.3->2.0 with position",
-    3: "ragged: B=32 k_b~U[1,15] V=151936 bf16, T_b in {0, 0.7, 1.0}",
-    4: "high concurrency: B=128 k=15 V=151936 bf16, sigma_b in {0.5, 1, 2}, fused rKL delta=1",
-    5: "large vocab stress: B=128 k=15 V=248320 bf16, 10% outlier ids shifted -20, forced edge cases",
+# name -> (seed stream id, description).  The stream id only separates the seeded streams.
+WORKLOADS = {
+    "tiny": (1, "tiny: B=1 k=4 V=1000 fp32"),
+    "single": (2, "single request: B=1 k=15 V=151936 bf16, sigma rising 0.3->2.0 with position"),
+    "ragged": (3, "ragged: B=32 k_b~U[1,15] V=151936 bf16, T_b in {0, 0.7, 1.0}"),
+    "high_concurrency": (4, "high concurrency: B=128 k=15 V=151936 bf16, sigma_b in {0.5, 1, 2}, "
+                            "fused rKL delta=1"),
+    "large_vocab": (5, "large vocab stress: B=128 k=15 V=248320 bf16, 10% outlier ids shifted "
+                       "-20, forced edge cases"),
 }
 
 _POISON_BF16 = 0x42C8  # bf16 bits of +100.0: fills columns in [V, ld) so reads past V are visible
@@ -249,8 +252,11 @@ def _position_sigma(n: int) -> np.ndarray:
     return 0.3 + 1.7 * np.arange(n, dtype=np.float64) / 14.0
 
 
-def config(n: int, rep: int = 0, *, B: Optional[int] = None) -> Workload:
-    """The five benchmark configurations (``B`` may be lowered for quick tests of the recipe)."""
+def workload(name: str, rep: int = 0, *, B: Optional[int] = None) -> Workload:
+    """One of the named workloads (``B`` may be lowered for quick tests of the recipe)."""
+    if name not in WORKLOADS:
+        raise ValueError(f"unknown workload {name!r}; known: {', '.join(WORKLOADS)}")
+    n, desc = WORKLOADS[name]
     ss = np.random.SeedSequence([ROOT_SEED, n, rep])
     children = ss.spawn(8)
     rng_params = np.random.Generator(np.random.PCG64(children[1]))
@@ -258,11 +264,11 @@ def config(n: int, rep: int = 0, *, B: Optional[int] = None) -> Workload:
                   first_reject=(), zipf_exponent=1.1)
     if n == 1:
         Bn = 1
-        return _generate(children, name=f"cfg1 {CONFIG_NAMES[1]}", B=Bn, k=[4], V=1000,
+        return _generate(children, name=desc, B=Bn, k=[4], V=1000,
                          dtype="f32", s=3.0, sigma=np.full((1, 4), 0.5), temperature=[1.0],
                          delta=1.0, k_max=4, **common)
     if n == 2:
-        return _generate(children, name=f"cfg2 {CONFIG_NAMES[2]}", B=1, k=[15], V=151936,
+        return _generate(children, name=desc, B=1, k=[15], V=151936,
                          dtype="bf16", s=4.0, sigma=_position_sigma(15)[None, :],
                          temperature=[1.0], delta=1.0, k_max=15, **common)
     if n == 3:
@@ -270,7 +276,7 @@ def config(n: int, rep: int = 0, *, B: Optional[int] = None) -> Workload:
         k = rng_params.integers(1, 16, size=Bn).astype(np.int32)
         temp = rng_params.choice(np.array([0.0, 0.7, 1.0], dtype=np.float32), size=Bn)
         sig = np.repeat(_position_sigma(15)[None, :], Bn, axis=0)
-        return _generate(children, name=f"cfg3 {CONFIG_NAMES[3]}", B=Bn, k=k, V=151936,
+        return _generate(children, name=desc, B=Bn, k=k, V=151936,
                          dtype="bf16", s=4.0, sigma=sig, temperature=temp, delta=1.0,
                          k_max=15, **common)
     if n in (4, 5):
@@ -284,7 +290,7 @@ def config(n: int, rep: int = 0, *, B: Optional[int] = None) -> Workload:
             picks = rng_params.permutation(Bn)[: 2 * n_edge]
             extra.update(outlier_frac=0.10, all_accept=tuple(int(x) for x in picks[:n_edge]),
                          first_reject=tuple(int(x) for x in picks[n_edge:]))
-        return _generate(children, name=f"cfg{n} {CONFIG_NAMES[n]}", B=Bn,
+        return _generate(children, name=desc, B=Bn,
                          k=np.full(Bn, 15, np.int32), V=V, dtype="bf16", s=4.0, sigma=sig,
                          temperature=np.ones(Bn, np.float32), delta=1.0, k_max=15, **extra)
-    raise ValueError(f"unknown config {n}")
+    raise AssertionError(name)

@@ -8,7 +8,7 @@ import os
 import numpy as np
 import pytest
 
-from synth import config, make_workload
+from synth import make_workload, workload
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -31,12 +31,12 @@ def _report(name, s):
 
 
 # ----------------------------------------------------------------------------- small cases
-def test_config1_tiny_fp32():
-    w = config(1)
+def test_tiny_fp32():
+    w = workload("tiny")
     got = run_gpu(w)
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
-    _report("cfg1", s)
+    _report("tiny", s)
     assert s["exact"] == 1
 
 
@@ -86,34 +86,34 @@ def test_small_delta_rereads_clipped_slices(delta):
 
 # ----------------------------------------------------------------------------- benchmark configs
 def test_config2_single_request():
-    w = config(2)
+    w = workload("single")
     got = run_gpu(w)
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
-    _report("cfg2", s)
+    _report("single", s)
 
 
 def test_config3_ragged_batch():
-    w = config(3)
+    w = workload("ragged")
     got = run_gpu(w)
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
-    _report("cfg3", s)
+    _report("ragged B=32", s)
     assert len(s["flips"]) <= 2
 
 
 @pytest.fixture(scope="module")
-def cfg4():
-    return config(4)
+def high_concurrency():
+    return workload("high_concurrency")
 
 
 @pytest.fixture(scope="module")
-def cfg5():
-    return config(5)
+def large_vocab():
+    return workload("large_vocab")
 
 
-def test_config4_full_size_sampled(cfg4):
-    w = cfg4
+def test_high_concurrency_full_size_sampled(high_concurrency):
+    w = high_concurrency
     dev = to_device(w)
     got = run_gpu(w, dev)
     assert got["device_status"][0] == 0
@@ -123,15 +123,15 @@ def test_config4_full_size_sampled(cfg4):
     # a sample of requests against the oracle, one by one
     sample = [0, 1, 17, 63, 64, 100, 126, 127]
     s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
-    _report("cfg4 sampled", s)
+    _report("high concurrency sampled", s)
     # bitwise determinism at full size
     again = run_gpu(w, dev)
     for key in ("accept_len", "out_tokens", "rkl", "p_at_draft", "q_at_draft"):
         np.testing.assert_array_equal(got[key], again[key])
 
 
-def test_config5_full_size_edge_cases(cfg5):
-    w = cfg5
+def test_large_vocab_full_size_edge_cases(large_vocab):
+    w = large_vocab
     got = run_gpu(w)
     assert got["device_status"][0] == 0
     aa, fr = w.meta["all_accept"], w.meta["first_reject"]
@@ -143,7 +143,7 @@ def test_config5_full_size_edge_cases(cfg5):
         assert got["accept_len"][b] == 0
     sample = sorted(set(aa[:2]) | set(fr[:2]) | {5, 77})
     s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
-    _report("cfg5 sampled", s)
+    _report("large vocab sampled", s)
 
 
 # ----------------------------------------------------------------------------- edge cases

@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from synth import bf16_bits_from_f64, bf16_bits_to_f32, config, make_workload
+from synth import bf16_bits_from_f64, bf16_bits_to_f32, make_workload, workload
 
 
 def test_bf16_rounding_is_nearest_even():
@@ -14,24 +14,24 @@ def test_bf16_rounding_is_nearest_even():
 
 
 def test_same_seed_same_bytes():
-    a = config(3, rep=0, B=4)
-    b = config(3, rep=0, B=4)
-    c = config(3, rep=1, B=4)
+    a = workload("ragged", rep=0, B=4)
+    b = workload("ragged", rep=0, B=4)
+    c = workload("ragged", rep=1, B=4)
     for f in ("k", "temperature", "target", "draft", "draft_tokens", "uniforms"):
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
     assert not np.array_equal(a.target, c.target)
 
 
-def test_config1_shape_and_ranges():
-    w = config(1)
+def test_tiny_shape_and_ranges():
+    w = workload("tiny")
     assert w.dtype == "f32" and w.B == 1 and list(w.k) == [4] and w.V == 1000
     assert w.target.shape == (5, 1000) and w.draft.shape == (4, 1000)
     assert np.all((w.uniforms >= 0) & (w.uniforms < 1))
     assert np.all((w.draft_tokens >= 0) & (w.draft_tokens < 1000))
 
 
-def test_config3_ragged_mix():
-    w = config(3, B=12)
+def test_ragged_mix():
+    w = workload("ragged", B=12)
     assert w.k.min() >= 1 and w.k.max() <= 15
     assert set(np.unique(w.temperature)).issubset({0.0, np.float32(0.7), 1.0})
     do = w.draft_offsets
@@ -42,8 +42,8 @@ def test_config3_ragged_mix():
                 assert w.draft_tokens[do[b] + i] == int(np.argmax(row))
 
 
-def test_config5_forced_cases():
-    w = config(5, B=20)  # floor(5% of 20) = 1 forced request of each kind
+def test_large_vocab_forced_cases():
+    w = workload("large_vocab", B=20)  # floor(5% of 20) = 1 forced request of each kind
     assert len(w.meta["all_accept"]) == 1 and len(w.meta["first_reject"]) == 1
     to, do = w.target_offsets, w.draft_offsets
     for b in w.meta["all_accept"]:
