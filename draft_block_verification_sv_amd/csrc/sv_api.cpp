@@ -17,10 +17,10 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 5;
-const char* const kKernelNames[kNumKernels] = {"sv_plan", "sv_rowpair", "sv_sample",
-                                               "sv_rkl_rowpair", "sv_rkl_status"};
-enum { K_PLAN, K_ROWPAIR, K_SAMPLE, K_RKL_ROWPAIR, K_RKL_STATUS };
+constexpr int kNumKernels = 6;
+const char* const kKernelNames[kNumKernels] = {"sv_plan",   "sv_rowpair",     "sv_sample_mass",
+                                               "sv_sample", "sv_rkl_rowpair", "sv_rkl_status"};
+enum { K_PLAN, K_ROWPAIR, K_SAMPLE_MASS, K_SAMPLE, K_RKL_ROWPAIR, K_RKL_STATUS };
 
 // ------------------------------------------------------------------ profiling
 struct ProfRec {
@@ -260,11 +260,16 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.d_off = ws.d_off;
   sa.d_lz = ws.d_lz;
   sa.acc = ws.acc;
+  sa.chunk_mass = ws.chunk_mass;
+  sa.mass_blocks = static_cast<int32_t>(sv::mass_blocks_for(n_chunks));
   sa.accept_len = accept_len;
   sa.out_tokens = out_tokens;
   sa.p_at = p_at_draft;
   sa.q_at = q_at_draft;
   sa.device_status = device_status;
+  if (timed(K_SAMPLE_MASS, st, [&] { return sv::launch_sample_mass(dtype, vec, sa, st); }) !=
+      hipSuccess)
+    return SV_ERR_HIP;
   if (timed(K_SAMPLE, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

@@ -5,12 +5,14 @@
 //                      packed-layout offsets from k (AdaFlash paper, Section 3.3: one
 //                      batch of total length sum k_b) and the request of every row.
 //   sv_rowpair         the streaming pass fused with each row's finalize (sv_rowpair.hip).
-//   sv_sample          one 1024-thread workgroup per request: the first-rejection scan,
-//                      the chunk masses of the residual max(0, p_T - q_T) at the rejected
-//                      position (reading notes, basic recipe step 4) or of p_T of the bonus
-//                      row (DFlash notes, Section 3.1 step 6), the inverse CDF at u * Z,
-//                      and the emitted tokens; folds the request's input checks into
-//                      device_status.
+//   sv_sample_mass     the draw masses, per kChunk-column chunk, of each request's draw
+//                      row: the residual max(0, p_T - q_T) at the first rejected position
+//                      (reading notes, basic recipe step 4) or p_T of the bonus row (DFlash
+//                      notes, Section 3.1 step 6); a request's row is spread over several
+//                      workgroups so the whole chip takes part.
+//   sv_sample          one 1024-thread workgroup per request: the scan of its chunk masses,
+//                      the inverse CDF at u * Z, the emitted tokens; folds the request's
+//                      input checks into device_status.
 // sv_clipped_rkl runs sv_rowpair alone and then sv_status.
 #include <float.h>
 #include <math.h>
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void sv_status_kernel(const int32_t* row_flags
 constexpr int kReqInvalid = 4 | 8 | 16;  // SV_DEV_BAD_TOKEN | BAD_TEMPERATURE | BAD_UNIFORM
 
 // Draw masses of the lane's 8 columns starting at col: the residual max(0, p_T - q_T) of
-// a row pair (pair && !use_p), else p_T.  p_T(y) = 2^(fma(l_p(y), beta, offp) - lzp): the
+// a row pair (need_q), else p_T.  p_T(y) = 2^(fma(l_p(y), beta, offp) - lzp): the
 // fma is exact before its one rounding and lzp is small, so p_T keeps fp32 accuracy.
 struct RowScale {
   float beta, offp, lzp, offq, lzq;
@@ -117,11 +119,10 @@ __device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
 }
 
 template <int DT, bool VEC>
-__device__ __forceinline__ void column_masses(const SampleArgs& a, int64_t t, int64_t d, bool pair,
-                                              bool use_p, const RowScale& k, int64_t col,
+__device__ __forceinline__ void column_masses(const SampleArgs& a, int64_t t, int64_t d,
+                                              bool need_q, const RowScale& k, int64_t col,
                                               float (&r)[8]) {
   float lp[8], lq[8];
-  const bool need_q = pair && !use_p;
   if constexpr (DT == 0) {
     const uint16_t* P = static_cast<const uint16_t*>(a.target) + t * a.ld_t;
     const uint16_t* Q = static_cast<const uint16_t*>(a.draft) + d * a.ld_d;
@@ -196,34 +197,33 @@ __device__ __forceinline__ double block_inclusive_scan(double v, double* lds) {
   return base + v;
 }
 
-// Draw mass of every kChunk-column chunk of the row into s_c (one wave per chunk, wave w
-// taking chunks w, w + kSampleWaves, ...).  Each lane sums its kChunkGroups groups of 8
-// columns (groups 512 columns apart) in fp32; the lane sums are combined in fp64.  For
-// aligned bf16 rows two chunks' loads are issued before any arithmetic.
-template <int DT, bool VEC>
-__device__ __forceinline__ void chunk_pass(const SampleArgs& a, int64_t t, int64_t d, bool pair,
-                                           bool use_p, const RowScale& k, int nc, int wave,
-                                           int lane, double* s_c) {
-  const bool need_q = pair && !use_p;
+// Draw masses of chunks [c_begin, c_end) of one row into out[c]; wave w of WAVES takes
+// chunks c_begin + w, + WAVES, ...  Each lane sums its kChunkGroups groups of 8 columns
+// (groups 512 columns apart) in fp32; the lane sums are combined in fp64.  For aligned
+// bf16 rows two chunks' loads are issued before any arithmetic.
+template <int DT, bool VEC, int WAVES>
+__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int64_t d, bool need_q,
+                                             const RowScale& k, int c_begin, int c_end, int wave,
+                                             int lane, double* out) {
   if constexpr (DT == 0 && VEC) {
     const uint16_t* P = static_cast<const uint16_t*>(a.target) + t * a.ld_t + lane * 8;
     const uint16_t* Q = static_cast<const uint16_t*>(a.draft) + d * a.ld_d + lane * 8;
     constexpr int NL = 2 * kChunkGroups;  // 16-byte loads per row per lane per batch
-    for (int c0 = wave; c0 < nc; c0 += 2 * kSampleWaves) {
+    for (int c0 = c_begin + wave; c0 < c_end; c0 += 2 * WAVES) {
       uint4 wp[NL], wq[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int c = c0 + (j / kChunkGroups) * kSampleWaves;
+        const int c = c0 + (j / kChunkGroups) * WAVES;
         const int64_t col = static_cast<int64_t>(c) * kChunk + (j % kChunkGroups) * 512;
-        if (c < nc && col + lane * 8 + 8 <= a.V) {
+        if (c < c_end && col + lane * 8 + 8 <= a.V) {
           wp[j] = *reinterpret_cast<const uint4*>(P + col);
           if (need_q) wq[j] = *reinterpret_cast<const uint4*>(Q + col);
         }
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = c0 + h * kSampleWaves;
-        if (c >= nc) break;
+        const int c = c0 + h * WAVES;
+        if (c >= c_end) break;
         float acc = 0.0f;
 #pragma unroll
         for (int g = 0; g < kChunkGroups; ++g) {
@@ -236,36 +236,80 @@ __device__ __forceinline__ void chunk_pass(const SampleArgs& a, int64_t t, int64
 #pragma unroll
             for (int e = 0; e < 8; ++e) r[e] = draw_mass(lp[e], lq[e], need_q, k);
           } else {  // ragged tail
-            column_masses<DT, VEC>(a, t, d, pair, use_p, k, col, r);
+            column_masses<DT, VEC>(a, t, d, need_q, k, col, r);
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc += r[e];
         }
         const double cs = wave_sum_d(static_cast<double>(acc));
-        if (lane == 0) s_c[c] = cs;
+        if (lane == 0) out[c] = cs;
       }
     }
   } else {
-    for (int c = wave; c < nc; c += kSampleWaves) {
+    for (int c = c_begin + wave; c < c_end; c += WAVES) {
       float acc = 0.0f;
       for (int g = 0; g < kChunkGroups; ++g) {
         float r[8];
-        column_masses<DT, VEC>(a, t, d, pair, use_p, k,
+        column_masses<DT, VEC>(a, t, d, need_q, k,
                                static_cast<int64_t>(c) * kChunk + g * 512 + lane * 8, r);
         for (int e = 0; e < 8; ++e) acc += r[e];
       }
       const double cs = wave_sum_d(static_cast<double>(acc));
-      if (lane == 0) s_c[c] = cs;
+      if (lane == 0) out[c] = cs;
     }
   }
 }
 
-// One 1024-thread workgroup per request:
+// The row a request's final token is drawn from: target row t (with draft row d when the
+// draw is from the residual), and the exp2 offsets of both.
+struct DrawRow {
+  int64_t t, d;
+  bool pair;
+  RowScale k;
+};
+
+__device__ __forceinline__ DrawRow draw_row(const SampleArgs& a, int64_t b, const ReqState& rq) {
+  DrawRow r;
+  r.t = rq.off + rq.alen;
+  r.pair = rq.alen < rq.kb;
+  r.d = rq.off - b + rq.alen;
+  r.k.beta = a.t_beta[r.t];
+  r.k.offp = a.t_off[r.t];
+  r.k.lzp = a.t_lz[r.t];
+  r.k.offq = r.pair ? a.d_off[r.d] : 0.0f;
+  r.k.lzq = r.pair ? a.d_lz[r.d] : 0.0f;
+  return r;
+}
+
+// sv_sample_mass: workgroup g of request b computes the draw masses of chunks
+// [g * kMassChunksPerBlock, (g + 1) * kMassChunksPerBlock) of the request's draw row into
+// chunk_mass[b * n_chunks + c].  Each wave derives the request state itself (a few cached
+// loads), so the workgroup has no barrier.  Void calls, invalid and greedy requests write
+// nothing: sv_sample does not read their masses.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kMassThreads) void sv_sample_mass_kernel(SampleArgs a) {
+  const int64_t b = blockIdx.x / a.mass_blocks;
+  const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (a.glob[0]) return;
+  const float T = a.temperature ? a.temperature[b] : 1.0f;
+  if (T == 0.0f) return;
+  const ReqState rq = wave_request_state(a, b);
+  if (rq.flags & kReqInvalid) return;
+  const DrawRow dr = draw_row(a, b, rq);
+  const int nc = static_cast<int>(a.n_chunks);
+  const int c_begin = g * kMassChunksPerBlock;
+  const int c_end = min(nc, c_begin + kMassChunksPerBlock);
+  chunk_masses<DT, VEC, kMassWaves>(a, dr.t, dr.d, dr.pair, dr.k, c_begin, c_end, wave, lane,
+                                    a.chunk_mass + b * a.n_chunks);
+}
+
+// sv_sample, one 1024-thread workgroup per request:
 //   1. the first-rejection scan over the request's acceptance flags (one wave, ballot);
-//   2. the mass of every kChunk-column chunk of the row the final token is drawn from --
-//      the residual max(0, p_T - q_T) at the rejected position (reading notes, basic
-//      recipe step 4) or p_T of the bonus row (DFlash notes, Section 3.1 step 6) --
-//      into LDS; wave w takes chunks w, w + 16, ..., two chunks' loads in flight;
+//   2. the chunk masses sv_sample_mass wrote, one chunk per thread; when they sum to
+//      zero (a residual emptied by rounding) the p_T masses of the same row are
+//      computed here instead, wave w taking chunks w, w + 16, ...;
 //   3. a fixed-order scan of the chunk masses; the chunk where the prefix first exceeds
 //      u * Z (u = the request's last uniform), then the column inside it (one wave,
 //      32 consecutive columns per lane, so the prefix runs in column order);
@@ -326,26 +370,19 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
     return;
   }
 
-  // ---- 2. chunk masses into LDS
-  RowScale k;
-  k.beta = a.t_beta[t];
-  k.offp = a.t_off[t];
-  k.lzp = a.t_lz[t];
-  k.offq = pair ? a.d_off[d] : 0.0f;
-  k.lzq = pair ? a.d_lz[d] : 0.0f;
+  // ---- 2. chunk masses
+  const RowScale k = draw_row(a, b, rq).k;
   const int nc = static_cast<int>(a.n_chunks);
-  chunk_pass<DT, VEC>(a, t, d, pair, false, k, nc, wave, lane, s_cr);
-  __syncthreads();
 
   // ---- 3a. chunk level: fixed-order scan, one chunk per thread
   bool usep = false;
-  double v = (tid < nc) ? s_cr[tid] : 0.0;
+  double v = (tid < nc) ? a.chunk_mass[b * a.n_chunks + tid] : 0.0;
   double incl = block_inclusive_scan(v, s_scan);
   if (tid == kSampleThreads - 1) s_Z = incl;
   __syncthreads();
   if (!(s_Z > 0.0)) {  // zero residual mass (rounding only): draw from p_T of the same row
     usep = true;
-    chunk_pass<DT, VEC>(a, t, d, pair, true, k, nc, wave, lane, s_cr);
+    chunk_masses<DT, VEC, kSampleWaves>(a, t, d, false, k, 0, nc, wave, lane, s_cr);
     __syncthreads();
     v = (tid < nc) ? s_cr[tid] : 0.0;
     incl = block_inclusive_scan(v, s_scan);
@@ -382,7 +419,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
 #pragma unroll
   for (int g = 0; g < kChunkGroups; ++g) {
     float r[8];
-    column_masses<DT, VEC>(a, t, d, pair, usep, k, colL + g * 8, r);
+    column_masses<DT, VEC>(a, t, d, pair && !usep, k, colL + g * 8, r);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       m[g * 8 + e] = r[e];
@@ -439,6 +476,17 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status,
                          hipStream_t st) {
   hipLaunchKernelGGL(sv_status_kernel, dim3(1), dim3(256), 0, st, row_flags, n, device_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.mass_blocks));
+  if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_sample_mass_kernel<0, true>), grid, dim3(kMassThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_sample_mass_kernel<0, false>), grid, dim3(kMassThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((sv_sample_mass_kernel<1, false>), grid, dim3(kMassThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

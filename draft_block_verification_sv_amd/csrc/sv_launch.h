@@ -77,6 +77,8 @@ struct SampleArgs {
   const float* d_off;
   const float* d_lz;
   const int32_t* acc;
+  double* chunk_mass;   // [B * n_chunks], written by sv_sample_mass, read by sv_sample
+  int32_t mass_blocks;  // sv_sample_mass workgroups per request
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
@@ -87,6 +89,7 @@ struct SampleArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
+hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 
 }  // namespace sv

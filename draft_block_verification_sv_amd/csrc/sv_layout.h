@@ -28,16 +28,24 @@ constexpr int kMaxSlices = 512;
 // writes per-row descriptors first.
 constexpr int kInlinePerThread = 8;
 constexpr int kInlinePlanMaxB = kRowThreads * kInlinePerThread;
-// The sampler: one 1024-thread workgroup per request, chunks of kChunk columns (one wave,
-// kChunkGroups groups of 8 per lane), chunk masses in LDS (V <= kMaxChunks * kChunk).
+// The sampler works on chunks of kChunk columns (one wave, kChunkGroups groups of 8 per
+// lane).  sv_sample_mass: 256-thread workgroups of kMassChunksPerBlock chunks each, so a
+// request's row is spread over ceil(n_chunks / kMassChunksPerBlock) workgroups.  sv_sample:
+// one 1024-thread workgroup per request, one chunk per thread (V <= kMaxChunks * kChunk).
 constexpr int kChunkGroups = 4;
 constexpr int kChunk = 64 * 8 * kChunkGroups;
+constexpr int kMassWaves = 4;
+constexpr int kMassThreads = 64 * kMassWaves;
+constexpr int kMassChunksPerBlock = 2 * kMassWaves;
 constexpr int kSampleWaves = 16;
 constexpr int kSampleThreads = 64 * kSampleWaves;
 constexpr int kMaxChunks = kSampleThreads;
 
 inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 inline int64_t n_chunks_for(int64_t V) { return (V + kChunk - 1) / kChunk; }
+inline int64_t mass_blocks_for(int64_t n_chunks) {
+  return (n_chunks + kMassChunksPerBlock - 1) / kMassChunksPerBlock;
+}
 
 // Per streaming unit, filled by the plan kernel (large batches only): units 0 .. n_d-1
 // are the draft rows, units n_d .. n_d+B-1 the bonus rows.
@@ -59,6 +67,7 @@ struct Workspace {
   float* d_off;        // [n_d]
   float* d_lz;         // [n_d]
   int32_t* acc;        // [n_d] acceptance flag
+  double* chunk_mass;  // [B * n_chunks] draw mass of each chunk of each request's draw row
 };
 
 struct Dims {
@@ -86,6 +95,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.d_off = reinterpret_cast<float*>(take(d.n_d * 4));
   w.d_lz = reinterpret_cast<float*>(take(d.n_d * 4));
   w.acc = reinterpret_cast<int32_t*>(take(d.n_d * 4));
+  w.chunk_mass = reinterpret_cast<double*>(take(d.B * d.n_chunks * sizeof(double)));
   if (ws) *ws = w;
   return off;
 }

@@ -84,8 +84,8 @@ def test_small_delta_rereads_clipped_slices(delta):
     _report(f"delta={delta}", s)
 
 
-# ----------------------------------------------------------------------------- benchmark configs
-def test_config2_single_request():
+# ----------------------------------------------------------------------------- full-size workloads
+def test_single_request_full_vocab():
     w = workload("single")
     got = run_gpu(w)
     assert got["device_status"][0] == 0
@@ -93,7 +93,7 @@ def test_config2_single_request():
     _report("single", s)
 
 
-def test_config3_ragged_batch():
+def test_ragged_batch_mixed_temperatures():
     w = workload("ragged")
     got = run_gpu(w)
     assert got["device_status"][0] == 0
@@ -154,6 +154,40 @@ def test_all_accept_and_bonus():
     assert list(got["accept_len"]) == [6, 15]
     assert np.all(got["rkl"] == 0.0)
     compare(w, got, run_oracle(w))
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_residual_emptied_by_rounding(T):
+    # A draft row equal to its target row except at the draft token, one bf16 step higher
+    # at a logit of -30: the token is rejected (ratio e^(-0.125/T)), and the residual
+    # max(0, p - q) is zero at every id in fp32 (the normalisers agree to the last bit),
+    # so the draw falls back to p_T of the same row.  Four ids carry all of p's mass, so
+    # the draw's outcome is fixed by the uniform; the oracle reaches the same id.
+    from synth import bf16_bits_from_f64, bf16_bits_to_f32
+
+    w = make_workload(B=1, k=[3], V=5003, dtype="bf16", s=3.0, sigma=0.0,
+                      temperature=[T], seed=(12, int(T * 10)))
+    V, rej, x = w.V, 1, 10
+    row = np.full(V, -30.0)
+    row[[100, 2000, 3500, 4900]] = [0.0, -0.5, -1.0, -2.0]
+    w.target[rej, :V] = bf16_bits_from_f64(row)
+    for i in range(3):
+        w.draft[i, :V] = w.target[i, :V]  # equal rows: p_T(x)/q_T(x) = 1, accepted
+    w.draft_tokens[rej] = x
+    w.draft[rej, x] = bf16_bits_from_f64(np.array([-29.875]))[0]
+    assert bf16_bits_to_f32(w.draft[rej, x:x + 1])[0] == -29.875
+    got, ref = None, None
+    for u in (0.05, 0.5, 0.8, 0.97):
+        w.uniforms[:] = 0.5
+        w.uniforms[rej] = 0.9999
+        w.uniforms[3] = u  # slot k drives the final draw
+        got = run_gpu(w)
+        ref = run_oracle(w)
+        assert got["device_status"][0] == 0
+        assert got["accept_len"][0] == rej
+        s = compare(w, got, ref)
+        assert s["exact"] == 1, (u, got["out_tokens"])
+        assert got["out_tokens"][rej] in (100, 2000, 3500, 4900)
 
 
 def test_greedy_trace(golden_dir):
