@@ -26,6 +26,43 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- fp64 exp2 / log2
+// Inlined double-precision 2^x and log2(x) for the per-row finalize (the library versions
+// are large enough to be emitted as calls, which costs the streaming kernels registers).
+// exp2_d: 2^x = 2^n e^(f ln2), n = floor(x), f in [0, 1); Taylor series of e^t to t^13
+// (|t| < 0.7: truncation below 2^-53 relative).  log2_d: x = m 2^e, m in [0.5, 1); the fp32
+// hardware log2 of m refined by one Newton step on 2^y = m (error squared: ~1e-15).
+__device__ __forceinline__ double exp2_d(double x) {
+  if (!(x > -1100.0)) return 0.0;
+  if (x > 1100.0) return __builtin_inf();
+  const double n = floor(x);
+  const double t = (x - n) * 0.69314718055994530942;
+  double p = 1.0 / 6227020800.0;  // 1/13!
+  p = fma(p, t, 1.0 / 479001600.0);
+  p = fma(p, t, 1.0 / 39916800.0);
+  p = fma(p, t, 1.0 / 3628800.0);
+  p = fma(p, t, 1.0 / 362880.0);
+  p = fma(p, t, 1.0 / 40320.0);
+  p = fma(p, t, 1.0 / 5040.0);
+  p = fma(p, t, 1.0 / 720.0);
+  p = fma(p, t, 1.0 / 120.0);
+  p = fma(p, t, 1.0 / 24.0);
+  p = fma(p, t, 1.0 / 6.0);
+  p = fma(p, t, 0.5);
+  p = fma(p, t, 1.0);
+  p = fma(p, t, 1.0);
+  return ldexp(p, static_cast<int>(n));
+}
+
+__device__ __forceinline__ double log2_d(double x) {  // x > 0, finite
+  int e = 0;
+  const double m = frexp(x, &e);
+  const double y0 = static_cast<double>(__builtin_amdgcn_logf(static_cast<float>(m)));
+  const double r = exp2_d(y0);
+  const double y1 = y0 - (r - m) / (r * 0.69314718055994530942);
+  return static_cast<double>(e) + y1;
+}
+
 // ---------------------------------------------------------------- wave reductions
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {

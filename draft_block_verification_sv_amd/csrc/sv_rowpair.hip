@@ -49,6 +49,16 @@
 
 namespace sv {
 
+// Work-item and workgroup ids straight from the hardware registers: this translation unit
+// is built with IEEE mode off, and the runtime's accessor functions (built with it on) are
+// then not inlined; the calls would cost the kernel registers.
+__device__ __forceinline__ int thread_index() {
+  return static_cast<int>(__builtin_amdgcn_workitem_id_x());
+}
+__device__ __forceinline__ int64_t block_index() {
+  return static_cast<int64_t>(__builtin_amdgcn_workgroup_id_x());
+}
+
 constexpr uint32_t kNaNBits = 0x7fc00000u;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -99,6 +109,15 @@ struct PackedRow {
     }
     return fmaxf(bf16_hi(__float_as_uint(mh)), ml);
   }
+  // Running maxima across slices: raw words (high elements, masked at the end) into mh,
+  // low elements into ml.
+  __device__ __forceinline__ void fold_max(float& mh, float& ml) const {
+#pragma unroll
+    for (int i = 0; i < kElemsPerLane / 2; i += 2) {
+      mh = fmaxf(mh, fmaxf(__uint_as_float(w[i]), __uint_as_float(w[i + 1])));
+      ml = fmaxf(ml, fmaxf(bf16_lo(w[i]), bf16_lo(w[i + 1])));
+    }
+  }
   __device__ __forceinline__ void load(const uint16_t* p) {  // p: this lane's first column
 #pragma unroll
     for (int c = 0; c < kGroups; ++c) {
@@ -122,6 +141,11 @@ struct FloatRow {
       m1 = fmaxf(m1, x[j + 1]);
     }
     return fmaxf(m0, m1);
+  }
+  __device__ __forceinline__ void fold_max(float& mh, float& ml) const {
+    (void)mh;
+#pragma unroll
+    for (int j = 0; j < kElemsPerLane; j += 2) ml = fmaxf(ml, fmaxf(x[j], x[j + 1]));
   }
   // Columns >= V read as -inf.  VEC: the row allows 16-byte loads.
   template <int DT, bool VEC>
@@ -167,104 +191,205 @@ struct FloatRow {
   }
 };
 
-// ----------------------------------------------------------------------------- slice records
-struct SliceRecs {  // LDS, structure of arrays, one entry per slice
-  float mp[kMaxSlices], sp[kMaxSlices], stp[kMaxSlices];
-  int ap[kMaxSlices];
-  float mq[kMaxSlices], sq[kMaxSlices], stq[kMaxSlices], w[kMaxSlices], g[kMaxSlices];
+// ----------------------------------------------------------------------------- lane statistics
+// Each lane keeps running statistics over its own columns of the row (pair), against
+// exp2 offsets that are whole numbers (log2 units): a change of offset then rescales the
+// sums exactly, and no cross-lane work is needed until the row is done.
+constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
+
+struct LaneAcc {
+  float kp, kq, ktp, ktq;      // offsets: T = 1 for p and q; T_b (rows with T_b not in {0, 1})
+  double sp, sq, stp, stq, w;  // sums of 2^(l L2E - k), of 2^(l beta - kt), of E_q (l_q - l_p)
+  float dmax;                  // max of l_q - l_p
+  float mhp, mlp, mhq, mlq;    // running maxima of l_p and l_q (see fold_max)
+  float amax;                  // greedy rows: the lane's largest target logit ...
+  int aidx;                    // ... and its first column
 };
 
-// Statistics of one slice of the row (pair); lane 0 writes the record of slice s.
-// col_lane: column of the lane's first element (argmax positions, padding mask).
-// MASK: columns >= V are padding (-inf) whose difference term must be zeroed.
-template <bool PAIR, int MODE, bool MASK, class Row>
-__device__ __forceinline__ void slice_stats(const Row& rp, const Row& rq, float beta, int s,
-                                            int64_t col_lane, int V, int lane, SliceRecs& R) {
-  const float mp = wave_max(rp.max());
-  const float op = -(mp * kL2E);
-  float mq = 0.0f, oq = 0.0f;
+__device__ __forceinline__ void lane_clear(LaneAcc& A) {
+  A.kp = A.kq = A.ktp = A.ktq = 0.0f;
+  A.sp = A.sq = A.stp = A.stq = A.w = 0.0;
+  A.dmax = -INFINITY;
+  A.mhp = A.mlp = A.mhq = A.mlq = -INFINITY;
+  A.amax = -INFINITY;
+  A.aidx = 0x7fffffff;
+}
+
+// Whole-number offset for a lane whose largest value is m at scale `scale`: every
+// exponent of that lane's slice is then <= 0.  A lane holding padding only keeps 0.
+__device__ __forceinline__ float offset_for(float m, float scale) {
+  const float k = ceilf(m * scale);
+  return k > -INFINITY ? k : 0.0f;
+}
+
+template <bool PAIR, int MODE, class Row>
+__device__ __forceinline__ void lane_init(const Row& rp, const Row& rq, float beta, LaneAcc& A) {
+  const float mp = rp.max();
+  A.kp = offset_for(mp, kL2E);
+  if constexpr (MODE == 2) A.ktp = offset_for(mp, beta);
   if constexpr (PAIR) {
-    mq = wave_max(rq.max());
-    oq = -(mq * kL2E);
-  }
-  float otp = 0.0f, otq = 0.0f;
-  if constexpr (MODE == 2) {
-    otp = -(mp * beta);
-    if constexpr (PAIR) otq = -(mq * beta);
-  }
-  float sp0 = 0.f, sp1 = 0.f, sq0 = 0.f, sq1 = 0.f, w0 = 0.f, w1 = 0.f, g = -INFINITY;
-  float stp0 = 0.f, stp1 = 0.f, stq0 = 0.f, stq1 = 0.f;
-#pragma unroll
-  for (int e = 0; e < kElemsPerLane; ++e) {
-    const bool odd = e & 1;
-    const float xp = rp.at(e);
-    const float ep = fast_exp2(__builtin_fmaf(xp, kL2E, op));
-    if (odd) sp1 += ep; else sp0 += ep;
-    if constexpr (MODE == 2) {
-      const float etp = fast_exp2(__builtin_fmaf(xp, beta, otp));
-      if (odd) stp1 += etp; else stp0 += etp;
-    }
-    if constexpr (PAIR) {
-      const float xq = rq.at(e);
-      const float eq = fast_exp2(__builtin_fmaf(xq, kL2E, oq));
-      float diff = xq - xp;
-      if constexpr (MASK) {
-        if (col_lane + (e >> 3) * 512 + (e & 7) >= V) diff = 0.0f;
-      }
-      if (odd) {
-        sq1 += eq;
-        w1 = __builtin_fmaf(eq, diff, w1);
-      } else {
-        sq0 += eq;
-        w0 = __builtin_fmaf(eq, diff, w0);
-      }
-      g = fmaxf(g, eq * diff);
-      if constexpr (MODE == 2) {
-        const float etq = fast_exp2(__builtin_fmaf(xq, beta, otq));
-        if (odd) stq1 += etq; else stq0 += etq;
-      }
-    }
-  }
-  const float sp = wave_sum(sp0 + sp1);
-  float stp = 0.f, sq = 0.f, stq = 0.f, w = 0.f;
-  if constexpr (MODE == 2) stp = wave_sum(stp0 + stp1);
-  if constexpr (PAIR) {
-    sq = wave_sum(sq0 + sq1);
-    w = wave_sum(w0 + w1);
-    g = wave_max(g);
-    if constexpr (MODE == 2) stq = wave_sum(stq0 + stq1);
-  }
-  int arg = 0;
-  if constexpr (MODE == 1) {
-    int best = 0x7fffffff;
-#pragma unroll
-    for (int e = kElemsPerLane - 1; e >= 0; --e)
-      if (rp.at(e) == mp) best = static_cast<int>(col_lane + (e >> 3) * 512 + (e & 7));
-    arg = wave_min_i(best);
-  }
-  if (lane == 0) {
-    R.mp[s] = mp;
-    R.sp[s] = sp;
-    if constexpr (MODE == 2) R.stp[s] = stp;
-    if constexpr (MODE == 1) R.ap[s] = arg;
-    if constexpr (PAIR) {
-      R.mq[s] = mq;
-      R.sq[s] = sq;
-      R.w[s] = w;
-      R.g[s] = g;
-      if constexpr (MODE == 2) R.stq[s] = stq;
-    }
+    const float mq = rq.max();
+    A.kq = offset_for(mq, kL2E);
+    if constexpr (MODE == 2) A.ktq = offset_for(mq, beta);
   }
 }
 
-// Streams the wave's slices (s = wave, wave + 4, ...) of the row (pair).
-// Full bf16 slices of 16-byte-aligned rows: packed, next slice prefetched while the
-// current one is reduced.  The ragged last slice and every other case: fp32, masked.
+// The row values as fresh registers: keeps the compiler from hoisting the rare offset
+// raise (and the maxima it needs) out of its branch.
+template <class Row>
+__device__ __forceinline__ Row opaque(const Row& r) {
+  Row o = r;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(Row) / 4); ++i) asm volatile("" : "+v"(w[i]));
+  return o;
+}
+
+// Raises the offsets to cover the slice's maxima; sums scale by exact powers of two.
+__device__ __forceinline__ void raise_offset(float& k, double& s, float m, float scale) {
+  const float kn = fmaxf(k, offset_for(m, scale));
+  s = ldexp(s, static_cast<int>(k - kn));
+  k = kn;
+}
+
+template <bool PAIR, int MODE, class Row>
+__device__ __forceinline__ void lane_rebase(const Row& rp_in, const Row& rq_in, float beta,
+                                            LaneAcc& A) {
+  const Row rp = opaque(rp_in);
+  const float mp = rp.max();
+  raise_offset(A.kp, A.sp, mp, kL2E);
+  if constexpr (MODE == 2) raise_offset(A.ktp, A.stp, mp, beta);
+  if constexpr (PAIR) {
+    const Row rq = opaque(rq_in);
+    const float mq = rq.max();
+    const float kn = fmaxf(A.kq, offset_for(mq, kL2E));
+    const int sh = static_cast<int>(A.kq - kn);
+    A.sq = ldexp(A.sq, sh);
+    A.w = ldexp(A.w, sh);
+    A.kq = kn;
+    if constexpr (MODE == 2) raise_offset(A.ktq, A.stq, mq, beta);
+  }
+}
+
+// One slice's partial sums against the lane's current offsets.
+struct SlicePart {
+  float sp, sq, stp, stq, w, dm;
+  bool ok;  // every partial sum below 2^64
+};
+
+template <bool PAIR, int MODE, bool MASK, class Row>
+__device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq, float beta,
+                                                    int64_t col_lane, int V, const LaneAcc& A) {
+  const float op = -A.kp, oq = -A.kq, otp = -A.ktp, otq = -A.ktq;
+  float sp0 = 0.f, sp1 = 0.f, sq0 = 0.f, sq1 = 0.f, w0 = 0.f, w1 = 0.f;
+  float stp0 = 0.f, stp1 = 0.f, stq0 = 0.f, stq1 = 0.f;
+  float dm0 = -INFINITY, dm1 = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < kElemsPerLane; e += 2) {
+    float t[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float xp = rp.at(e + h);
+      const float ep = fast_exp2(__builtin_fmaf(xp, kL2E, op));
+      if (h) sp1 += ep; else sp0 += ep;
+      if constexpr (MODE == 2) {
+        const float etp = fast_exp2(__builtin_fmaf(xp, beta, otp));
+        if (h) stp1 += etp; else stp0 += etp;
+      }
+      if constexpr (PAIR) {
+        const float xq = rq.at(e + h);
+        const float eq = fast_exp2(__builtin_fmaf(xq, kL2E, oq));
+        float diff = xq - xp;
+        if constexpr (MASK) {
+          const int ee = e + h;
+          if (col_lane + (ee >> 3) * 512 + (ee & 7) >= V) diff = 0.0f;
+        }
+        if (h) {
+          sq1 += eq;
+          w1 = __builtin_fmaf(eq, diff, w1);
+        } else {
+          sq0 += eq;
+          w0 = __builtin_fmaf(eq, diff, w0);
+        }
+        t[h] = diff;
+        if constexpr (MODE == 2) {
+          const float etq = fast_exp2(__builtin_fmaf(xq, beta, otq));
+          if (h) stq1 += etq; else stq0 += etq;
+        }
+      }
+    }
+    if constexpr (PAIR) {
+      if (e & 2) dm1 = fmaxf(dm1, fmaxf(t[0], t[1]));
+      else dm0 = fmaxf(dm0, fmaxf(t[0], t[1]));
+    }
+  }
+  SlicePart P;
+  P.sp = sp0 + sp1;
+  P.ok = P.sp < kOverflow;
+  P.stp = P.sq = P.stq = P.w = 0.f;
+  P.dm = -INFINITY;
+  if constexpr (MODE == 2) {
+    P.stp = stp0 + stp1;
+    P.ok = P.ok && P.stp < kOverflow;
+  }
+  if constexpr (PAIR) {
+    P.sq = sq0 + sq1;
+    P.w = w0 + w1;
+    P.dm = fmaxf(dm0, dm1);
+    P.ok = P.ok && P.sq < kOverflow;
+    if constexpr (MODE == 2) {
+      P.stq = stq0 + stq1;
+      P.ok = P.ok && P.stq < kOverflow;
+    }
+  }
+  return P;
+}
+
+// Adds one slice of the lane's columns to its statistics.  col_lane: column of the lane's
+// first element.  MASK: columns >= V are padding (-inf) whose difference term is zeroed.
+// A slice whose partial sum reaches 2^64 (values far above the lane's offset) raises the
+// offsets and is summed again; the partial sums are otherwise added in fp64.
+template <bool PAIR, int MODE, bool MASK, class Row>
+__device__ __forceinline__ void slice_accumulate(const Row& rp, const Row& rq, float beta,
+                                                 int64_t col_lane, int V, LaneAcc& A) {
+  if constexpr (MODE == 1) {
+    const float m = rp.max();
+    if (m > A.amax) {
+      int best = 0;
+#pragma unroll
+      for (int e = kElemsPerLane - 1; e >= 0; --e)
+        if (rp.at(e) == m) best = e;
+      A.amax = m;
+      A.aidx = static_cast<int>(col_lane + (best >> 3) * 512 + (best & 7));
+    }
+  }
+  rp.fold_max(A.mhp, A.mlp);
+  if constexpr (PAIR) rq.fold_max(A.mhq, A.mlq);
+  SlicePart P = slice_partials<PAIR, MODE, MASK>(rp, rq, beta, col_lane, V, A);
+  if (!P.ok) {  // rare: raise the offsets, sum the slice again from fresh registers
+    lane_rebase<PAIR, MODE>(rp, rq, beta, A);
+    P = slice_partials<PAIR, MODE, MASK>(opaque(rp), opaque(rq), beta, col_lane, V, A);
+  }
+  A.sp += static_cast<double>(P.sp);
+  if constexpr (MODE == 2) A.stp += static_cast<double>(P.stp);
+  if constexpr (PAIR) {
+    A.sq += static_cast<double>(P.sq);
+    A.w += static_cast<double>(P.w);
+    A.dmax = fmaxf(A.dmax, P.dm);
+    if constexpr (MODE == 2) A.stq += static_cast<double>(P.stq);
+  }
+}
+
+// Streams the wave's slices (s = wave, wave + 4, ...) of the row (pair) into the lane's
+// statistics.  Full bf16 slices of 16-byte-aligned rows: packed, next slice prefetched
+// while the current one is reduced.  The ragged last slice and every other case: fp32,
+// masked.  The lane's first slice sets its offsets from that slice's maxima.
 template <int DT, bool VEC, bool PAIR, int MODE>
 __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, float beta, int V,
-                                           int n_slices, int wave, int lane, SliceRecs& R) {
+                                           int n_slices, int wave, int lane, LaneAcc& A) {
   const int n_full = V / kSlice;
   int s = wave;
+  bool fresh = true;
   if constexpr (DT == 0 && VEC && !SV_ROWS_PREFETCH) {
     const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
     const uint16_t* Q = static_cast<const uint16_t*>(qrow) + lane * 8;
@@ -272,8 +397,12 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
       PackedRow ap, aq;
       ap.load(P + static_cast<int64_t>(s) * kSlice);
       if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s) * kSlice);
-      slice_stats<PAIR, MODE, false>(ap, aq, beta, s, static_cast<int64_t>(s) * kSlice + lane * 8,
-                                     V, lane, R);
+      if (fresh) {
+        lane_init<PAIR, MODE>(ap, aq, beta, A);
+        fresh = false;
+      }
+      slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
+                                          static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
     }
   }
   if constexpr (DT == 0 && VEC && SV_ROWS_PREFETCH) {
@@ -283,6 +412,8 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
     if (s < n_full) {
       ap.load(P + static_cast<int64_t>(s) * kSlice);
       if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s) * kSlice);
+      lane_init<PAIR, MODE>(ap, aq, beta, A);
+      fresh = false;
     }
     while (s < n_full) {
       const int s2 = s + kRowWaves;
@@ -290,8 +421,8 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
         bp.load(P + static_cast<int64_t>(s2) * kSlice);
         if constexpr (PAIR) bq.load(Q + static_cast<int64_t>(s2) * kSlice);
       }
-      slice_stats<PAIR, MODE, false>(ap, aq, beta, s, static_cast<int64_t>(s) * kSlice + lane * 8,
-                                     V, lane, R);
+      slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
+                                          static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
       if (s2 >= n_full) {
         s = s2;
         break;
@@ -301,8 +432,8 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
         ap.load(P + static_cast<int64_t>(s3) * kSlice);
         if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s3) * kSlice);
       }
-      slice_stats<PAIR, MODE, false>(bp, bq, beta, s2,
-                                     static_cast<int64_t>(s2) * kSlice + lane * 8, V, lane, R);
+      slice_accumulate<PAIR, MODE, false>(bp, bq, beta,
+                                          static_cast<int64_t>(s2) * kSlice + lane * 8, V, A);
       s = s3;
     }
   }
@@ -311,7 +442,11 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
     FloatRow fp, fq;
     fp.template load<DT, VEC>(prow, col_lane, V);
     if constexpr (PAIR) fq.template load<DT, VEC>(qrow, col_lane, V);
-    slice_stats<PAIR, MODE, true>(fp, fq, beta, s, col_lane, V, lane, R);
+    if (fresh) {
+      lane_init<PAIR, MODE>(fp, fq, beta, A);
+      fresh = false;
+    }
+    slice_accumulate<PAIR, MODE, true>(fp, fq, beta, col_lane, V, A);
   }
 }
 
@@ -319,7 +454,7 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
 // Fixed-order reductions over the 256-thread workgroup: wave butterfly, then the four
 // wave results in order.  `red` holds kRowWaves doubles.
 __device__ __forceinline__ double block_sum_d(double v, double* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = thread_index() & 63, wave = thread_index() >> 6;
   v = wave_sum_d(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -330,7 +465,7 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
   return r;
 }
 __device__ __forceinline__ float block_max_f(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = thread_index() & 63, wave = thread_index() >> 6;
   v = wave_max_f(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -341,7 +476,7 @@ __device__ __forceinline__ float block_max_f(float v, float* red) {
   return r;
 }
 __device__ __forceinline__ int block_min_i(int v, int* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = thread_index() & 63, wave = thread_index() >> 6;
   v = wave_min_int(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -352,15 +487,31 @@ __device__ __forceinline__ int block_min_i(int v, int* red) {
   return r;
 }
 
-// log2 normaliser of the row from the slice records (m[], S[]) at scale `scale`:
-// K + log2(sum_s S_s 2^(fp32(m_s scale) - K)), K = fp32(M scale).
-__device__ __forceinline__ double row_lz(const float* m, const float* S, float M, float scale,
-                                         int n_slices, double* red) {
-  const float K = M * scale;
-  double acc = 0.0;
-  for (int s = threadIdx.x; s < n_slices; s += kRowThreads)
-    acc += static_cast<double>(S[s]) * exp2(static_cast<double>(m[s] * scale) - static_cast<double>(K));
-  return static_cast<double>(K) + log2(block_sum_d(acc, red));
+// The lane's largest logit from its running maxima.
+__device__ __forceinline__ float lane_max(float mh, float ml) {
+  return fmaxf(bf16_hi(__float_as_uint(mh)), ml);
+}
+
+// The lane's largest element entered its sum as the fp32 exponential of a rounded
+// exponent (up to one unit in the last place off).  In rows dominated by one token that
+// error moves the normaliser, and through it the reverse-KL, by more than the rest of the
+// row's rounding; the lane sum is corrected to carry that element's exact value.  The
+// same fma and exp2 as the stream reproduce the value that was added.
+__device__ __forceinline__ void correct_top(double& S, float M, float scale, float k) {
+  if (S > 0.0 && M > -INFINITY) {
+    const float added = fast_exp2(__builtin_fmaf(M, scale, -k));
+    const double exact = exp2_d(static_cast<double>(M) * static_cast<double>(scale) -
+                              static_cast<double>(k));
+    S += exact - static_cast<double>(added);
+  }
+}
+
+// log2 normaliser from every lane's (offset k, sum S): K + log2(sum_l S_l 2^(k_l - K)),
+// K the largest offset of a lane with mass; the scaling by 2^(k_l - K) is exact.
+__device__ __forceinline__ double lanes_lz(float k, double S, float* red_f, double* red_d) {
+  const float K = block_max_f(S > 0.0 ? k : -INFINITY, red_f);  // lanes with mass only
+  const double v = S > 0.0 ? ldexp(S, static_cast<int>(k - K)) : 0.0;
+  return static_cast<double>(K) + log2_d(block_sum_d(v, red_d));
 }
 
 template <int DT>
@@ -369,35 +520,46 @@ __device__ __forceinline__ float logit_at(const void* row, int64_t col) {
   else return static_cast<const float*>(row)[col];
 }
 
-// Clipped reverse-KL of the row pair from its records; slices whose bound may reach
-// delta are re-read and summed entry by entry (each by one wave).
+// Clipped reverse-KL of the row pair.  With Q = 2^(k_q - LZq) S_q, the q-mass of a lane's
+// columns, and c2 = LZp - LZq, those columns contribute exactly
+//   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
+// and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
+// ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p.  A lane whose bound may reach
+// delta has its columns re-read by one wave and summed entry by entry.
 template <int DT>
-__device__ __forceinline__ double row_clipped_rkl(const void* prow, const void* qrow, int V, int n_slices,
-                                  double LZp, double LZq, float delta, const SliceRecs& R,
-                                  double* contrib, int* failed, int* s_nfail, double* red) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ double lanes_clipped_rkl(const void* prow, const void* qrow, int V,
+                                                   int n_slices, double LZp, double LZq,
+                                                   float delta, const LaneAcc& A, double* direct,
+                                                   int* failed, int* s_nfail, double* red) {
+  const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double c2 = LZp - LZq;
-  const double c2pos = c2 > 0.0 ? c2 : 0.0;
+  double closed = 0.0;
+  bool fail = false;
+  if (A.sq > 0.0) {
+    const double scale = kLn2 * exp2_d(static_cast<double>(A.kq) - LZq);
+    closed = scale * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
+    const double slope = static_cast<double>(kL2E) * A.dmax + c2;
+    const double bound = scale * A.sq * (slope > 0.0 ? slope : 0.0);
+    fail = !(bound * 1.0001 < static_cast<double>(delta));
+  }
   if (tid == 0) *s_nfail = 0;
   __syncthreads();
-  for (int s = tid; s < n_slices; s += kRowThreads) {
-    const double scale = kLn2 * exp2(static_cast<double>(R.mq[s] * kL2E) - LZq);
-    const double bound = scale * (static_cast<double>(kL2E) * R.g[s] + c2pos * 1.0001);
-    contrib[s] = scale * (static_cast<double>(kL2E) * R.w[s] + c2 * R.sq[s]);
-    if (!(bound * 1.0001 < static_cast<double>(delta))) failed[atomicAdd(s_nfail, 1)] = s;
-  }
+  if (fail) failed[atomicAdd(s_nfail, 1)] = tid;
   __syncthreads();
   const int nfail = *s_nfail;
   const float c2f = static_cast<float>(c2);
   for (int f = wave; f < nfail; f += kRowWaves) {
-    const int s = failed[f];
+    const int src = failed[f];
+    const int sw = src >> 6, sl = src & 63;  // the failing lane's wave and lane
+    const int n_pieces = ((n_slices - sw + kRowWaves - 1) / kRowWaves) * kGroups;
     float part = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kGroups; ++c) {
+    for (int j = lane; j < n_pieces; j += 64) {
+      const int64_t col0 = static_cast<int64_t>(sw + (j / kGroups) * kRowWaves) * kSlice +
+                           (j % kGroups) * 512 + sl * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t col = static_cast<int64_t>(s) * kSlice + c * 512 + lane * 8 + e;
+        const int64_t col = col0 + e;
         if (col < V) {
           const float lq = logit_at<DT>(qrow, col);
           const float lp = logit_at<DT>(prow, col);
@@ -407,13 +569,19 @@ __device__ __forceinline__ double row_clipped_rkl(const void* prow, const void* 
         }
       }
     }
-    const double direct = wave_sum_d(static_cast<double>(part));
-    if (lane == 0) contrib[s] = direct;
+    const double dsum = wave_sum_d(static_cast<double>(part));
+    if (lane == 0) direct[src] = dsum;
   }
   __syncthreads();
-  double acc = 0.0;
-  for (int s = tid; s < n_slices; s += kRowThreads) acc += contrib[s];
-  return block_sum_d(acc, red);
+  return block_sum_d(fail ? direct[tid] : closed, red);
+}
+
+// Offsets the sampler uses to rebuild a row's p_T: p_T(y) = 2^(fma(l_y, beta, off) - lz)
+// with off = -round(LZ), so the exponent stays small wherever p_T is not negligible.
+__device__ __forceinline__ void draw_offsets(double LZ, float* off, float* lz) {
+  const double K = rint(LZ);
+  *off = static_cast<float>(-K);
+  *lz = static_cast<float>(LZ - K);
 }
 
 // ----------------------------------------------------------------------------- kernel
@@ -426,37 +594,45 @@ struct RowCtx {
 };
 
 template <int DT, bool VEC, bool PAIR, int MODE>
-__device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx, SliceRecs& R, double* contrib,
-                             int* failed, int* s_nfail, double* red_d, float* red_f, int* red_i,
-                             int x, float lpx, float lqx) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
+                                             LaneAcc* lacc, double* direct, int* failed,
+                                             int* s_nfail,
+                                             double* red_d, float* red_f, int* red_i, int x,
+                                             float lpx, float lqx) {
+  const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = a.V;
   const int n_slices = static_cast<int>(a.n_slices);
   const void* prow = static_cast<const char*>(a.target) + ctx.t * a.ld_t * (DT == 0 ? 2 : 4);
   const void* qrow = static_cast<const char*>(a.draft) + (PAIR ? ctx.d : 0) * a.ld_d * (DT == 0 ? 2 : 4);
 
-  stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, wave, lane, R);
-  __syncthreads();
+  {
+    LaneAcc L;
+    lane_clear(L);
+    stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, wave, lane, L);
+    const float Mp = lane_max(L.mhp, L.mlp);
+    correct_top(L.sp, Mp, kL2E, L.kp);
+    if constexpr (MODE == 2) correct_top(L.stp, Mp, ctx.beta, L.ktp);
+    if constexpr (PAIR) {
+      const float Mq = lane_max(L.mhq, L.mlq);
+      correct_top(L.sq, Mq, kL2E, L.kq);
+      if constexpr (MODE == 2) correct_top(L.stq, Mq, ctx.beta, L.ktq);
+    }
+    lacc[tid] = L;  // the finalize reads the record back as it needs it
+  }
+  const LaneAcc& A = lacc[tid];
 
-  // target row: normalisers at T = 1 and T_b, argmax
-  float m = -INFINITY;
-  for (int s = tid; s < n_slices; s += kRowThreads) m = fmaxf(m, R.mp[s]);
-  const float Mp = block_max_f(m, red_f);
-  const double LZ1p = row_lz(R.mp, R.sp, Mp, kL2E, n_slices, red_d);
-  const double LZTp = (MODE == 2) ? row_lz(R.mp, R.stp, Mp, ctx.beta, n_slices, red_d) : LZ1p;
+  // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
+  const double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
+  const double LZTp = (MODE == 2) ? lanes_lz(A.ktp, A.stp, red_f, red_d) : LZ1p;
   int argp = 0;
   if constexpr (MODE == 1) {
-    int best = 0x7fffffff;
-    for (int s = tid; s < n_slices; s += kRowThreads)
-      if (R.mp[s] == Mp) best = min(best, R.ap[s]);
-    argp = block_min_i(best, red_i);
+    const float Mx = block_max_f(A.amax, red_f);
+    argp = block_min_i(A.amax == Mx ? A.aidx : 0x7fffffff, red_i);
   }
   const float scale_T = (MODE == 2) ? ctx.beta : kL2E;
   if (tid == 0 && ctx.b >= 0) {
-    const float KT = Mp * scale_T;
-    a.t_off[ctx.t] = -KT;
-    a.t_lz[ctx.t] = static_cast<float>(LZTp - static_cast<double>(KT));
+    draw_offsets(LZTp, a.t_off + ctx.t, a.t_lz + ctx.t);
     a.t_beta[ctx.t] = scale_T;
     a.t_arg[ctx.t] = argp;
     a.row_flags[ctx.t] = ctx.row_flags;
@@ -464,20 +640,15 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   if constexpr (!PAIR) return;
 
   // draft row
-  m = -INFINITY;
-  for (int s = tid; s < n_slices; s += kRowThreads) m = fmaxf(m, R.mq[s]);
-  const float Mq = block_max_f(m, red_f);
-  const double LZ1q = row_lz(R.mq, R.sq, Mq, kL2E, n_slices, red_d);
-  const double LZTq = (MODE == 2) ? row_lz(R.mq, R.stq, Mq, ctx.beta, n_slices, red_d) : LZ1q;
+  const double LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
+  const double LZTq = (MODE == 2) ? lanes_lz(A.ktq, A.stq, red_f, red_d) : LZ1q;
   if (a.rkl_out) {
-    const double Rk = row_clipped_rkl<DT>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, R, contrib,
-                                          failed, s_nfail, red_d);
+    const double Rk = lanes_clipped_rkl<DT>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A,
+                                            direct, failed, s_nfail, red_d);
     if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk);
   }
   if (tid == 0 && ctx.b >= 0) {
-    const float KT = Mq * scale_T;
-    a.d_off[ctx.d] = -KT;
-    a.d_lz[ctx.d] = static_cast<float>(LZTq - static_cast<double>(KT));
+    draw_offsets(LZTq, a.d_off + ctx.d, a.d_lz + ctx.d);
     int accept = 0;
     if (ctx.row_flags == 0) {  // the request's own flags are combined by the sampler
       const double Lp = static_cast<double>(lpx) * scale_T - LZTp;  // log2 p_T(x)
@@ -485,11 +656,11 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       if constexpr (MODE == 1) {
         accept = (x == argp) ? 1 : 0;
       } else {
-        const double ratio = fmin(1.0, exp2(Lp - Lq));
+        const double ratio = fmin(1.0, exp2_d(Lp - Lq));
         accept = (static_cast<double>(a.uniforms[ctx.t]) < ratio) ? 1 : 0;
       }
-      if (a.p_at) a.p_at[ctx.d] = static_cast<float>(exp2(Lp));
-      if (a.q_at) a.q_at[ctx.d] = static_cast<float>(exp2(Lq));
+      if (a.p_at) a.p_at[ctx.d] = static_cast<float>(exp2_d(Lp));
+      if (a.q_at) a.q_at[ctx.d] = static_cast<float>(exp2_d(Lq));
     } else {
       if (a.p_at) store_nan(a.p_at + ctx.d);
       if (a.q_at) store_nan(a.q_at + ctx.d);
@@ -501,17 +672,17 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_ROWS_WAVES_PER_EU)))
 void sv_rowpair_kernel(RowPairArgs a) {
-  __shared__ SliceRecs R;
-  __shared__ double contrib[kMaxSlices];
-  __shared__ int failed[kMaxSlices];
+  __shared__ LaneAcc lacc[kRowThreads];
+  __shared__ double direct[kRowThreads];
+  __shared__ int failed[kRowThreads];
   __shared__ int s_nfail;
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
   __shared__ int s_req, s_off, s_t, s_void, s_x;
   __shared__ float s_lpx, s_lqx;
-  const int tid = threadIdx.x;
-  const int64_t unit = blockIdx.x;
+  const int tid = thread_index();
+  const int64_t unit = block_index();
 
   RowCtx ctx;
   if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
@@ -529,7 +700,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
       return;
     }
     if (tid == 0) a.row_flags[unit] = 0;
-    rowpair_body<DT, VEC, true, 0>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, 0,
+    rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, 0,
                                    0.0f, 0.0f);
     return;
   }
@@ -671,13 +842,13 @@ void sv_rowpair_kernel(RowPairArgs a) {
   const int x = s_x;
   const float lpx = s_lpx, lqx = s_lqx;
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, true, 0>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, true, 1>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, true, 2>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, true, 2>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, false, 0>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, R, contrib, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, false, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   }
 }
 
