@@ -18,6 +18,10 @@
 #include <math.h>
 
 #include "sv_device.h"
+
+#ifndef SV_MASS_WAVES_PER_EU
+#define SV_MASS_WAVES_PER_EU 5
+#endif
 #include "sv_layout.h"
 #include "sv_launch.h"
 
@@ -155,26 +159,74 @@ __device__ __forceinline__ void column_masses(const SampleArgs& a, int64_t t, in
   for (int e = 0; e < 8; ++e) r[e] = draw_mass(lp[e], lq[e], need_q, k);
 }
 
+// A request's state: whether the call is void, T_b, length, first target row, input
+// flags (OR over its k_b + 1 rows), the first rejected position a_b, the final uniform,
+// and what the draw needs of row a_b (its exp2 offsets, its argmax).  Gathered by one
+// wave in two dependent rounds of loads: (call flag, T_b, k_b, first row), then lane i
+// reads everything of row i at once (and its draft token into *tok) and the values of
+// row a_b are taken from lane a_b by a shuffle.
 struct ReqState {
-  int kb, flags, alen;
+  int void_call, kb, flags, alen, targ;
+  float T, ufin;
   int64_t off;
+  RowScale k;
 };
 
-// The request's length, offset, input flags (OR over its k_b + 1 rows) and first
-// rejected position, gathered by one wave: lane i reads row i (k_b <= 64 rows + 1).
-__device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int64_t b) {
+__device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int64_t b, int* tok) {
   const int lane = threadIdx.x & 63;
   ReqState r;
+  r.k.beta = r.k.offp = r.k.lzp = r.k.offq = r.k.lzq = 0.f;
+  r.targ = 0;
+  r.void_call = a.glob[0];
+  r.T = a.temperature ? a.temperature[b] : 1.0f;
   r.kb = a.k[b];
   r.off = a.off_t[b];
-  int f = 0;
-  for (int i = lane; i <= r.kb; i += 64) f |= a.row_flags[r.off + i];
+  const int64_t t = r.off + lane, d = r.off - b + lane;
+  int f = 0, targ = 0;
+  bool rej = false;
+  float beta = 0.f, offp = 0.f, lzp = 0.f, offq = 0.f, lzq = 0.f, u = 0.f;
+  *tok = -1;
+  if (!r.void_call) {
+    if (lane <= r.kb) {
+      f = a.row_flags[t];
+      beta = a.t_beta[t];
+      offp = a.t_off[t];
+      lzp = a.t_lz[t];
+      targ = a.t_arg[t];
+      u = a.uniforms[t];
+    }
+    if (lane < r.kb) {
+      rej = !a.acc[d];
+      offq = a.d_off[d];
+      lzq = a.d_lz[d];
+      *tok = a.tokens[d];
+    }
+  }
+  r.ufin = r.kb < 64 ? __shfl(u, r.kb < 0 ? 0 : r.kb, 64) : 0.f;
+  if (r.kb >= 64 && !r.void_call) {  // k_b = 64: the 65th row
+    if (lane == 0) f |= a.row_flags[r.off + 64];
+    r.ufin = a.uniforms[r.off + 64];
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) f |= __shfl_xor(f, m, 64);
   r.flags = f;
-  const bool rej = lane < r.kb && !a.acc[r.off - b + lane];
   const uint64_t mask = __ballot(rej);
   r.alen = mask ? __builtin_ctzll(mask) : r.kb;
+  if (r.alen < 64) {
+    r.k.beta = __shfl(beta, r.alen, 64);
+    r.k.offp = __shfl(offp, r.alen, 64);
+    r.k.lzp = __shfl(lzp, r.alen, 64);
+    r.k.offq = __shfl(offq, r.alen, 64);
+    r.k.lzq = __shfl(lzq, r.alen, 64);
+    r.targ = __shfl(targ, r.alen, 64);
+  } else if (!r.void_call) {  // k_b = 64 and every draft accepted: the bonus row is row 64
+    const int64_t tb = r.off + 64;
+    r.k.beta = a.t_beta[tb];
+    r.k.offp = a.t_off[tb];
+    r.k.lzp = a.t_lz[tb];
+    r.k.offq = r.k.lzq = 0.f;
+    r.targ = a.t_arg[tb];
+  }
   return r;
 }
 
@@ -200,108 +252,85 @@ __device__ __forceinline__ double block_inclusive_scan(double v, double* lds) {
 // Draw masses of chunks [c_begin, c_end) of one row into out[c]; wave w of WAVES takes
 // chunks c_begin + w, + WAVES, ...  Each lane sums its kChunkGroups groups of 8 columns
 // (groups 512 columns apart) in fp32; the lane sums are combined in fp64.  For aligned
-// bf16 rows two chunks' loads are issued before any arithmetic.
-template <int DT, bool VEC, int WAVES>
-__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int64_t d, bool need_q,
-                                             const RowScale& k, int c_begin, int c_end, int wave,
-                                             int lane, double* out) {
+// bf16 rows the loads of BATCH chunks are issued before any arithmetic.
+template <int DT, bool VEC, int WAVES, int BATCH, bool NEED_Q>
+__device__ __forceinline__ void chunk_masses_t(const SampleArgs& a, int64_t t, int64_t d,
+                                               const RowScale& k, int c_begin, int c_end,
+                                               int wave, int lane, double* out) {
+  const int n_full = a.V / kChunk;  // chunks that lie wholly inside [0, V)
+  int c0 = c_begin + wave;
   if constexpr (DT == 0 && VEC) {
     const uint16_t* P = static_cast<const uint16_t*>(a.target) + t * a.ld_t + lane * 8;
     const uint16_t* Q = static_cast<const uint16_t*>(a.draft) + d * a.ld_d + lane * 8;
-    constexpr int NL = 2 * kChunkGroups;  // 16-byte loads per row per lane per batch
-    for (int c0 = c_begin + wave; c0 < c_end; c0 += 2 * WAVES) {
+    constexpr int NL = BATCH * kChunkGroups;  // 16-byte loads per row per lane per batch
+    // full batches: every chunk of the batch inside the range and inside [0, V)
+    for (; c0 + (BATCH - 1) * WAVES < min(c_end, n_full); c0 += BATCH * WAVES) {
       uint4 wp[NL], wq[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int c = c0 + (j / kChunkGroups) * WAVES;
-        const int64_t col = static_cast<int64_t>(c) * kChunk + (j % kChunkGroups) * 512;
-        if (c < c_end && col + lane * 8 + 8 <= a.V) {
-          wp[j] = *reinterpret_cast<const uint4*>(P + col);
-          if (need_q) wq[j] = *reinterpret_cast<const uint4*>(Q + col);
-        }
+        const int64_t col =
+            static_cast<int64_t>(c0 + (j / kChunkGroups) * WAVES) * kChunk + (j % kChunkGroups) * 512;
+        wp[j] = *reinterpret_cast<const uint4*>(P + col);
+        if constexpr (NEED_Q) wq[j] = *reinterpret_cast<const uint4*>(Q + col);
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = c0 + h * WAVES;
-        if (c >= c_end) break;
+      for (int h = 0; h < BATCH; ++h) {
         float acc = 0.0f;
 #pragma unroll
         for (int g = 0; g < kChunkGroups; ++g) {
-          const int64_t col = static_cast<int64_t>(c) * kChunk + g * 512 + lane * 8;
-          float r[8];
-          if (col + 8 <= a.V) {
-            float lp[8], lq[8];
-            unpack8(wp[h * kChunkGroups + g], lp);
-            if (need_q) unpack8(wq[h * kChunkGroups + g], lq);
+          float lp[8], lq[8];
+          unpack8(wp[h * kChunkGroups + g], lp);
+          if constexpr (NEED_Q) unpack8(wq[h * kChunkGroups + g], lq);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) r[e] = draw_mass(lp[e], lq[e], need_q, k);
-          } else {  // ragged tail
-            column_masses<DT, VEC>(a, t, d, need_q, k, col, r);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += r[e];
+          for (int e = 0; e < 8; ++e) acc += draw_mass(lp[e], NEED_Q ? lq[e] : 0.0f, NEED_Q, k);
         }
         const double cs = wave_sum_d(static_cast<double>(acc));
-        if (lane == 0) out[c] = cs;
+        if (lane == 0) out[c0 + h * WAVES] = cs;
       }
     }
-  } else {
-    for (int c = c_begin + wave; c < c_end; c += WAVES) {
-      float acc = 0.0f;
-      for (int g = 0; g < kChunkGroups; ++g) {
-        float r[8];
-        column_masses<DT, VEC>(a, t, d, need_q, k,
-                               static_cast<int64_t>(c) * kChunk + g * 512 + lane * 8, r);
-        for (int e = 0; e < 8; ++e) acc += r[e];
-      }
-      const double cs = wave_sum_d(static_cast<double>(acc));
-      if (lane == 0) out[c] = cs;
+  }
+  for (int c = c0; c < c_end; c += WAVES) {  // the rest, one chunk at a time, bounds-checked
+    float acc = 0.0f;
+    for (int g = 0; g < kChunkGroups; ++g) {
+      float r[8];
+      column_masses<DT, VEC>(a, t, d, NEED_Q, k,
+                             static_cast<int64_t>(c) * kChunk + g * 512 + lane * 8, r);
+      for (int e = 0; e < 8; ++e) acc += r[e];
     }
+    const double cs = wave_sum_d(static_cast<double>(acc));
+    if (lane == 0) out[c] = cs;
   }
 }
 
-// The row a request's final token is drawn from: target row t (with draft row d when the
-// draw is from the residual), and the exp2 offsets of both.
-struct DrawRow {
-  int64_t t, d;
-  bool pair;
-  RowScale k;
-};
-
-__device__ __forceinline__ DrawRow draw_row(const SampleArgs& a, int64_t b, const ReqState& rq) {
-  DrawRow r;
-  r.t = rq.off + rq.alen;
-  r.pair = rq.alen < rq.kb;
-  r.d = rq.off - b + rq.alen;
-  r.k.beta = a.t_beta[r.t];
-  r.k.offp = a.t_off[r.t];
-  r.k.lzp = a.t_lz[r.t];
-  r.k.offq = r.pair ? a.d_off[r.d] : 0.0f;
-  r.k.lzq = r.pair ? a.d_lz[r.d] : 0.0f;
-  return r;
+template <int DT, bool VEC, int WAVES, int BATCH>
+__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int64_t d, bool need_q,
+                                             const RowScale& k, int c_begin, int c_end, int wave,
+                                             int lane, double* out) {
+  if (need_q) chunk_masses_t<DT, VEC, WAVES, BATCH, true>(a, t, d, k, c_begin, c_end, wave, lane, out);
+  else chunk_masses_t<DT, VEC, WAVES, BATCH, false>(a, t, d, k, c_begin, c_end, wave, lane, out);
 }
 
 // sv_sample_mass: workgroup g of request b computes the draw masses of chunks
 // [g * kMassChunksPerBlock, (g + 1) * kMassChunksPerBlock) of the request's draw row into
 // chunk_mass[b * n_chunks + c].  Each wave derives the request state itself (a few cached
 // loads), so the workgroup has no barrier.  Void calls, invalid and greedy requests write
-// nothing: sv_sample does not read their masses.
+// nothing: sv_sample does not read their masses.  Register use is capped so that all the
+// workgroups of a B = 128 call are resident at once.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kMassThreads) void sv_sample_mass_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(SV_MASS_WAVES_PER_EU)))
+void sv_sample_mass_kernel(SampleArgs a) {
   const int64_t b = blockIdx.x / a.mass_blocks;
   const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (a.glob[0]) return;
-  const float T = a.temperature ? a.temperature[b] : 1.0f;
-  if (T == 0.0f) return;
-  const ReqState rq = wave_request_state(a, b);
-  if (rq.flags & kReqInvalid) return;
-  const DrawRow dr = draw_row(a, b, rq);
+  int tok;
+  const ReqState rq = wave_request_state(a, b, &tok);
+  if (rq.void_call || rq.T == 0.0f || (rq.flags & kReqInvalid)) return;
   const int nc = static_cast<int>(a.n_chunks);
   const int c_begin = g * kMassChunksPerBlock;
   const int c_end = min(nc, c_begin + kMassChunksPerBlock);
-  chunk_masses<DT, VEC, kMassWaves>(a, dr.t, dr.d, dr.pair, dr.k, c_begin, c_end, wave, lane,
+  chunk_masses<DT, VEC, kMassWaves, 1>(a, rq.off + rq.alen, rq.off - b + rq.alen, rq.alen < rq.kb,
+                                    rq.k, c_begin, c_end, wave, lane,
                                     a.chunk_mass + b * a.n_chunks);
 }
 
@@ -326,19 +355,24 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
   __shared__ int s_sel, s_last, s_fallback;
   __shared__ double s_Z, s_thr_c;
 
-  if (a.glob[0]) {  // void call
+  // this request's chunk masses, fetched before its state is known (stale for requests
+  // that turn out greedy or invalid, which never read them)
+  const int nc = static_cast<int>(a.n_chunks);
+  double v = (tid < nc) ? a.chunk_mass[b * a.n_chunks + tid] : 0.0;
+  int my_tok = -1;  // wave 0: lane i holds draft token i of the request
+  if (tid < 64) {
+    const ReqState r = wave_request_state(a, b, &my_tok);
+    if (tid == 0) s_req = r;
+  }
+  __syncthreads();
+  const ReqState rq = s_req;
+  if (rq.void_call) {  // void call
     if (tid == 0) a.accept_len[b] = -1;
     for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
          t += static_cast<int64_t>(kSampleThreads) * a.B)
       a.out_tokens[t] = -1;
     return;
   }
-  if (tid < 64) {
-    const ReqState r = wave_request_state(a, b);
-    if (tid == 0) s_req = r;
-  }
-  __syncthreads();
-  const ReqState rq = s_req;
   const int kb = rq.kb;
   const int64_t off = rq.off;
   if (rq.flags & kReqInvalid) {
@@ -358,31 +392,27 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
   const bool pair = alen < kb;
   const int64_t d = off - b + alen;
 
+  // wave 0 writes the outputs: a_b drafts (held in its lanes), the final token, then -1
   auto emit = [&](int tok) {
-    if (tid == 0) a.accept_len[b] = alen;
-    for (int j = tid; j <= kb; j += kSampleThreads)
-      a.out_tokens[off + j] = (j < alen) ? a.tokens[off - b + j] : (j == alen ? tok : -1);
+    if (lane == 0) a.accept_len[b] = alen;
+    for (int j = lane; j <= kb; j += 64)
+      a.out_tokens[off + j] = (j < alen) ? my_tok : (j == alen ? tok : -1);
   };
 
-  const float T = a.temperature ? a.temperature[b] : 1.0f;
-  if (T == 0.0f) {  // greedy: the target argmax at the first mismatch (or the bonus row)
-    emit(a.t_arg[t]);
+  if (rq.T == 0.0f) {  // greedy: the target argmax at the first mismatch (or the bonus row)
+    if (tid < 64) emit(rq.targ);
     return;
   }
-
-  // ---- 2. chunk masses
-  const RowScale k = draw_row(a, b, rq).k;
-  const int nc = static_cast<int>(a.n_chunks);
+  const RowScale k = rq.k;
 
   // ---- 3a. chunk level: fixed-order scan, one chunk per thread
   bool usep = false;
-  double v = (tid < nc) ? a.chunk_mass[b * a.n_chunks + tid] : 0.0;
   double incl = block_inclusive_scan(v, s_scan);
   if (tid == kSampleThreads - 1) s_Z = incl;
   __syncthreads();
   if (!(s_Z > 0.0)) {  // zero residual mass (rounding only): draw from p_T of the same row
     usep = true;
-    chunk_masses<DT, VEC, kSampleWaves>(a, t, d, false, k, 0, nc, wave, lane, s_cr);
+    chunk_masses<DT, VEC, kSampleWaves, 2>(a, t, d, false, k, 0, nc, wave, lane, s_cr);
     __syncthreads();
     v = (tid < nc) ? s_cr[tid] : 0.0;
     incl = block_inclusive_scan(v, s_scan);
@@ -390,7 +420,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
     if (tid == kSampleThreads - 1) s_Z = incl;
     __syncthreads();
   }
-  const double thr = static_cast<double>(a.uniforms[off + kb]) * s_Z;
+  const double thr = static_cast<double>(rq.ufin) * s_Z;
   s_incl[tid] = incl;
   if (tid == 0) {
     s_sel = 0x7fffffff;
@@ -461,10 +491,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
     const int src = has ? 63 - __builtin_clzll(has) : 0;
     tok = __shfl(static_cast<int>(colL) + (last < 0 ? 0 : last), src, 64);
   }
-  // emit with the wave that is left
-  if (lane == 0) a.accept_len[b] = alen;
-  for (int j = lane; j <= kb; j += 64)
-    a.out_tokens[off + j] = (j < alen) ? a.tokens[off - b + j] : (j == alen ? tok : -1);
+  emit(tok);
 }
 
 // =========================================================================== launchers
