@@ -23,6 +23,11 @@ basic recipe; DFlash notes, Section 3.1 step 6 and Section 5.2):
 5. Emit.  a_b accepted drafts followed by the final token: a_b + 1 tokens.
 
 Plus the per-position clipped reverse-KL from ``oracle.rkl`` for every draft row.
+
+Parity unpinned: the fallback of step 4 for a residual of zero total mass (draw from
+p_T of the same row).  In exact arithmetic that mass equals the rejection probability,
+so the pages never reach the case; the fallback is a reading, and nothing on the pages
+gives a value to check it against.
 """
 
 from __future__ import annotations
