@@ -11,7 +11,8 @@ Sources (cited by page title and section):
 * "AdaFlash: Adaptive Speculative Decoding via On-Policy Distilled Diffusion
   Drafters" (arXiv 2607.19223) -- Section 2.1 (acceptance test, first-rejection
   truncation, residual resample, closed form of the expected output length),
-  Section 3.1 (entry-wise clipped reverse-KL equation), Section 3.2 (per-request
+  Section 3.1 (entry-wise clipped reverse-KL equation; the hard-label cross-entropy
+  and the mixture OPD loss), Section 3.2 (per-request
   verification length), Section 3.3 (packed batch of total length sum k_i),
   Appendix B.1 (greedy decoding default, reverse-KL temperature 1).
 * "AdaFlash reading notes" (zhongzhuzhou.org blog) -- steps 3-4 of the basic
@@ -56,3 +57,4 @@ from .verify import (  # noqa: F401
     expected_tau,
 )
 from .rkl import clipped_rkl_row, clipped_rkl  # noqa: F401
+from .opd import hard_ce_row, opd_loss  # noqa: F401
