@@ -11,6 +11,10 @@ synthetic inputs (see synth/workloads.py).  Prints one JSON line on stdout;
 progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload high_concurrency] [--no-cpu-baseline]
+
+With --op opd the step is instead one sv_opd_loss call (hard-label cross-entropy, clipped
+reverse-KL and the per-request OPD loss) over the same workload's draft rows, each paired
+with the target row that scores it.
 """
 
 from __future__ import annotations
@@ -79,12 +83,119 @@ def cpu_baseline(w, n_requests: int) -> dict:
                       f"{dt:.2f} s wall"}
 
 
+_OPD = None  # (target rows, draft rows, pairing, delta), inherited by forked workers
+
+
+def _oracle_opd_request(b):
+    import oracle
+
+    tl, dl, idx, off, k, delta = _OPD
+    sl = slice(int(off[b]), int(off[b + 1]))
+    oracle.opd_loss(tl[idx[sl]], dl[sl], [int(k[b])], delta, 0.8)
+    return int(k[b])
+
+
+def cpu_baseline_opd(w, idx, n_requests: int) -> dict:
+    import multiprocessing as mp
+
+    import oracle
+
+    global _OPD
+    tl = oracle.widen_logits(w.target[:, : w.V], w.dtype)
+    dl = oracle.widen_logits(w.draft[:, : w.V], w.dtype)
+    _OPD = (tl, dl, idx, w.draft_offsets, w.k, w.delta)
+    cores = max(1, min(16, os.cpu_count() or 1))
+    reqs = list(range(min(n_requests, w.B)))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        rows = sum(pool.map(_oracle_opd_request, reqs, chunksize=1))
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(reqs)} of {w.B} requests ({rows} row pairs: hard CE, clipped rKL, "
+                      f"OPD loss), float64 NumPy, {cores} worker processes, {dt:.2f} s wall"}
+
+
+def bench_opd(args, w):
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+
+    idx_np = np.concatenate([np.arange(w.target_offsets[b], w.target_offsets[b] + w.k[b])
+                             for b in range(w.B)]).astype(np.int32)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_opd(w, idx_np, args.cpu_requests)
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} rows/s")
+    pkg.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def up(a, dt=None):
+        if dt is torch.bfloat16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    bf = torch.bfloat16 if w.dtype == "bf16" else None
+    target, draft = up(w.target, bf), up(w.draft, bf)
+    idx, k = up(idx_np), up(w.k.astype(np.int32))
+    n, V, B = w.n_draft_rows, w.V, w.B
+    code = pkg.SV_BF16 if w.dtype == "bf16" else pkg.SV_F32
+    ws = pkg.alloc_workspace(int(pkg.lib().sv_rkl_workspace_size(n, V, code)), dev)
+    out = {"rkl": torch.empty(n, dtype=torch.float32, device=dev),
+           "hard_ce": torch.empty(n, dtype=torch.float32, device=dev),
+           "top1": torch.empty(n, dtype=torch.int32, device=dev),
+           "opd": torch.empty(B, dtype=torch.float32, device=dev),
+           "device_status": torch.empty(1, dtype=torch.int32, device=dev)}
+
+    def step():
+        pkg.opd_loss(target, draft, k, delta=w.delta, alpha=0.8, p_row_index=idx, workspace=ws,
+                     out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(out["device_status"].item()) == 0
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
+    esize = 2 if w.dtype == "bf16" else 4
+    rows_bytes = 2 * n * V * esize  # each draft row and its target row, once
+    achieved = rows_bytes / (kernels["sv_opd_rowpair"] * 1e-6) / 1e9
+    res = {
+        "metric": "OPD loss row pairs/sec (hard CE + clipped rKL + per-request loss)",
+        "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded logits shaped like the pages' workloads)",
+        "config": {"workload": w.name, "op": "opd_loss", "rows": n, "B": B, "V": V,
+                   "input_dtype": w.dtype, "delta": w.delta, "alpha": 0.8,
+                   "algorithmic_bytes_per_step": rows_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
+    ap.add_argument("--op", choices=("verify", "opd"), default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -118,6 +229,8 @@ def main():
     t0 = time.perf_counter()
     w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
+    if args.op == "opd":
+        return bench_opd(args, w)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")

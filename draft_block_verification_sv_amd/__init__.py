@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     clipped_rkl,
     lib,
     library_path,
+    opd_loss,
     profile_enable,
     profile_read,
     profile_reset,

@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
     L.sv_clipped_rkl.argtypes = [_c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
                                  _c_p, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_clipped_rkl.restype = _c_i32
+    L.sv_opd_loss.argtypes = [_c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                              _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                              _c_sz, _c_p]
+    L.sv_opd_loss.restype = _c_i32
     L.sv_status_string.argtypes = [_c_i32]
     L.sv_status_string.restype = ctypes.c_char_p
     L.sv_version.argtypes = []
@@ -166,6 +170,13 @@ def verify_block(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
             "q_at_draft": torch.empty(n_d, dtype=torch.float32, device=dev) if with_probs else None,
             "device_status": torch.empty(1, dtype=torch.int32, device=dev),
         }
+    else:  # caller-provided outputs: the C ABI writes them without bounds, so check here
+        _need(out["accept_len"], "accept_len", torch.int32, B, dev)
+        _need(out["out_tokens"], "out_tokens", torch.int32, n_d + B, dev)
+        for name in ("rkl", "p_at_draft", "q_at_draft"):
+            if out.get(name) is not None:
+                _need(out[name], name, torch.float32, n_d, dev)
+        _need(out["device_status"], "device_status", torch.int32, 1, dev)
     st = lib().sv_verify_block(
         code, B, k_max, V, target.stride(0), draft.stride(0), n_d, _ptr(target), _ptr(draft),
         _ptr(k), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), float(delta),
@@ -173,6 +184,70 @@ def verify_block(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
         _ptr(out.get("p_at_draft")), _ptr(out.get("q_at_draft")), _ptr(out["device_status"]),
         _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "sv_verify_block")
+    return out
+
+
+def _row_pair_shapes(target: torch.Tensor, draft: torch.Tensor,
+                     p_row_index: Optional[torch.Tensor]):
+    dev = target.device
+    code = _dtype_code(target)
+    if draft.dtype != target.dtype or target.dim() != 2 or draft.dim() != 2:
+        raise ValueError("target/draft must be 2-D tensors of one dtype")
+    if target.stride(1) != 1 or draft.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    n = int(draft.shape[0])
+    V = int(draft.shape[1])
+    if int(target.shape[1]) != V:
+        raise ValueError("target and draft must have the same column count")
+    if p_row_index is None:
+        if int(target.shape[0]) < n:
+            raise ValueError("without p_row_index target needs at least as many rows as draft")
+    else:
+        _need(p_row_index, "p_row_index", torch.int32, n, dev)
+    return dev, code, n, V
+
+
+def opd_loss(target: torch.Tensor, draft: torch.Tensor, k: Optional[torch.Tensor] = None,
+             delta: float = 1.0, alpha: float = 0.8, p_row_index: Optional[torch.Tensor] = None,
+             *, workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+             stream=None) -> dict:
+    """sv_opd_loss: per draft row the clipped rKL, -ln q(x*) and x*; with k (int32 [B], draft
+    rows packed request by request) the per-request OPD loss.  Returns a dict of tensors."""
+    dev, code, n, V = _row_pair_shapes(target, draft, p_row_index)
+    B = 1
+    if k is not None:
+        if k.dim() != 1:
+            raise ValueError("k must be 1-D")
+        B = int(k.numel())
+        _need(k, "k", torch.int32, B, dev)
+    if workspace is None:
+        nbytes = int(lib().sv_rkl_workspace_size(n, V, code))
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape n_rows={n} V={V}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {
+            "rkl": torch.empty(n, dtype=torch.float32, device=dev),
+            "hard_ce": torch.empty(n, dtype=torch.float32, device=dev),
+            "top1": torch.empty(n, dtype=torch.int32, device=dev),
+            "opd": torch.empty(B, dtype=torch.float32, device=dev) if k is not None else None,
+            "device_status": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    else:
+        _need(out["rkl"], "rkl", torch.float32, n, dev)
+        _need(out["hard_ce"], "hard_ce", torch.float32, n, dev)
+        if out.get("top1") is not None:
+            _need(out["top1"], "top1", torch.int32, n, dev)
+        if k is not None:
+            _need(out["opd"], "opd", torch.float32, B, dev)
+        _need(out["device_status"], "device_status", torch.int32, 1, dev)
+    st = lib().sv_opd_loss(code, B, n, int(target.shape[0]), V, target.stride(0), draft.stride(0),
+                           _ptr(target), _ptr(draft), _ptr(p_row_index), _ptr(k), float(delta),
+                           float(alpha), _ptr(out["rkl"]), _ptr(out["hard_ce"]),
+                           _ptr(out.get("top1")), _ptr(out.get("opd") if k is not None else None),
+                           _ptr(out["device_status"]), _ptr(workspace),
+                           workspace.numel(), _stream(stream))
+    _check(st, "sv_opd_loss")
     return out
 
 

@@ -17,10 +17,21 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 6;
-const char* const kKernelNames[kNumKernels] = {"sv_plan",   "sv_rowpair",     "sv_sample_mass",
-                                               "sv_sample", "sv_rkl_rowpair", "sv_rkl_status"};
-enum { K_PLAN, K_ROWPAIR, K_SAMPLE_MASS, K_SAMPLE, K_RKL_ROWPAIR, K_RKL_STATUS };
+constexpr int kNumKernels = 9;
+const char* const kKernelNames[kNumKernels] = {
+    "sv_plan",        "sv_rowpair",    "sv_sample_mass", "sv_sample",    "sv_rkl_rowpair",
+    "sv_rkl_status",  "sv_opd_rowpair", "sv_opd_status", "sv_opd_reduce"};
+enum {
+  K_PLAN,
+  K_ROWPAIR,
+  K_SAMPLE_MASS,
+  K_SAMPLE,
+  K_RKL_ROWPAIR,
+  K_RKL_STATUS,
+  K_OPD_ROWPAIR,
+  K_OPD_STATUS,
+  K_OPD_REDUCE
+};
 
 // ------------------------------------------------------------------ profiling
 struct ProfRec {
@@ -129,6 +140,63 @@ Dims rkl_dims(int64_t n_rows, int64_t V) {
 bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
   return V >= 1 && V <= SV_MAX_VOCAB && sv::n_slices_for(V) <= sv::kMaxSlices &&
          sv::n_chunks_for(V) <= sv::kMaxChunks && ld_t >= V && ld_d >= V;
+}
+
+}  // namespace
+
+namespace {
+
+// The clipped reverse-KL of n_rows row pairs, and with hard_out the hard-label
+// cross-entropy against each target row's top-1: sv_clipped_rkl and sv_opd_loss.
+sv_status rkl_rows(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t V,
+                   int64_t ld_target, int64_t ld_draft, const void* target_logits,
+                   const void* draft_logits, const int32_t* p_row_index, float delta,
+                   float* rkl_out, float* hard_out, int32_t* top1_out, int32_t* device_status,
+                   void* workspace, size_t workspace_bytes, hipStream_t st, int k_rowpair,
+                   int k_status, Workspace* ws_out) {
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
+  if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
+  if (n_rows >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
+  const Dims dm = rkl_dims(n_rows, V);
+  if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
+  if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
+  const size_t need = sv::carve(dm, nullptr, nullptr);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
+    return SV_ERR_WORKSPACE;
+
+  Workspace ws{};
+  sv::carve(dm, &ws, static_cast<char*>(workspace));
+  const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
+
+  sv::RowPairArgs ra{};
+  ra.target = target_logits;
+  ra.draft = draft_logits;
+  ra.ld_t = ld_target;
+  ra.ld_d = ld_draft;
+  ra.V = static_cast<int32_t>(V);
+  ra.n_slices = dm.n_slices;
+  ra.n_units = n_rows;
+  ra.rkl_only = true;
+  ra.p_row_index = p_row_index;
+  ra.n_target_rows = n_target_rows;
+  ra.delta = delta;
+  ra.rkl_out = rkl_out;
+  ra.hard_out = hard_out;
+  ra.top1_out = top1_out;
+  ra.device_status = device_status;
+  ra.row_flags = ws.row_flags;
+  if (timed(k_rowpair, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+  if (ws_out) {  // the caller folds the row flags into its own final kernel
+    *ws_out = ws;
+    return SV_OK;
+  }
+  if (timed(k_status, st,
+            [&] { return sv::launch_status(ws.row_flags, n_rows, device_status, st); }) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
 }
 
 }  // namespace
@@ -275,50 +343,40 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   return SV_OK;
 }
 
+
+sv_status sv_opd_loss(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target_rows, int64_t V,
+                      int64_t ld_target, int64_t ld_draft, const void* target_logits,
+                      const void* draft_logits, const int32_t* p_row_index, const int32_t* k,
+                      float delta, float alpha, float* rkl_out, float* hard_ce_out,
+                      int32_t* top1_out, float* opd_out, int32_t* device_status, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!hard_ce_out) return SV_ERR_NULL;
+  if (opd_out && (!k || B < 1 || B > SV_MAX_BATCH)) return k ? SV_ERR_SHAPE : SV_ERR_NULL;
+  if (!(std::isfinite(alpha) && alpha >= 0.0f && alpha <= 1.0f)) return SV_ERR_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws{};
+  const sv_status s = rkl_rows(dtype, n_rows, n_target_rows, V, ld_target, ld_draft, target_logits,
+                               draft_logits, p_row_index, delta, rkl_out, hard_ce_out, top1_out,
+                               device_status, workspace, workspace_bytes, st, K_OPD_ROWPAIR,
+                               K_OPD_STATUS, opd_out ? &ws : nullptr);
+  if (s != SV_OK || !opd_out) return s;
+  if (timed(K_OPD_REDUCE, st, [&] {
+        return sv::launch_opd_reduce(k, B, n_rows, rkl_out, hard_ce_out, alpha, ws.row_flags,
+                                     opd_out, device_status, st);
+      }) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
 sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t V,
                          int64_t ld_target, int64_t ld_draft, const void* target_logits,
                          const void* draft_logits, const int32_t* p_row_index, float delta,
                          float* rkl_out, int32_t* device_status, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-  if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
-  if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
-  if (n_rows >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
-  const Dims dm = rkl_dims(n_rows, V);
-  if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
-  if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
-  const size_t need = sv::carve(dm, nullptr, nullptr);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
-    return SV_ERR_WORKSPACE;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Workspace ws{};
-  sv::carve(dm, &ws, static_cast<char*>(workspace));
-  const bool vec = vec_ok(dtype, ld_target, target_logits) && vec_ok(dtype, ld_draft, draft_logits);
-
-  sv::RowPairArgs ra{};
-  ra.target = target_logits;
-  ra.draft = draft_logits;
-  ra.ld_t = ld_target;
-  ra.ld_d = ld_draft;
-  ra.V = static_cast<int32_t>(V);
-  ra.n_slices = dm.n_slices;
-  ra.n_units = n_rows;
-  ra.rkl_only = true;
-  ra.p_row_index = p_row_index;
-  ra.n_target_rows = n_target_rows;
-  ra.delta = delta;
-  ra.rkl_out = rkl_out;
-  ra.device_status = device_status;
-  ra.row_flags = ws.row_flags;
-  if (timed(K_RKL_ROWPAIR, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) !=
-      hipSuccess)
-    return SV_ERR_HIP;
-  if (timed(K_RKL_STATUS, st,
-            [&] { return sv::launch_status(ws.row_flags, n_rows, device_status, st); }) !=
-      hipSuccess)
-    return SV_ERR_HIP;
-  return SV_OK;
+  return rkl_rows(dtype, n_rows, n_target_rows, V, ld_target, ld_draft, target_logits,
+                  draft_logits, p_row_index, delta, rkl_out, nullptr, nullptr, device_status,
+                  workspace, workspace_bytes, static_cast<hipStream_t>(stream), K_RKL_ROWPAIR,
+                  K_RKL_STATUS, nullptr);
 }
 
 sv_status sv_profile_enable(int32_t on) {

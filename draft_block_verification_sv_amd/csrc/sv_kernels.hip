@@ -88,6 +88,67 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
   }
 }
 
+// =========================================================================== OPD loss
+// Per request: l_OPD = alpha mean_i(-ln q(x*_i)) + (1 - alpha) mean_i R_i over its k_b
+// packed draft rows (AdaFlash paper, Section 3.1).  One workgroup: fixed-order exclusive
+// scan of k for the row offsets, then each thread sums its requests' rows in row order in
+// fp64.  Bad lengths or sum k_b != n_rows give NaN and SV_DEV_* bits; *device_status is
+// written once, with the rows' own flags (row_flags) folded in.
+__global__ __launch_bounds__(1024) void sv_opd_reduce_kernel(const int32_t* k, int64_t B,
+                                                             int64_t n_rows, const float* rkl,
+                                                             const float* hard, float alpha,
+                                                             const int32_t* row_flags,
+                                                             float* opd_out,
+                                                             int32_t* device_status) {
+  __shared__ int s_waves[16];
+  __shared__ int s_bad, s_rows;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = s_rows = 0;
+  __syncthreads();
+  int rf = 0;
+  for (int64_t i = tid; i < n_rows; i += 1024) rf |= row_flags[i];
+  if (rf) atomicOr(&s_rows, rf);
+  int carry = 0;
+  for (int64_t base = 0; base < B; base += 1024) {  // validate and total first
+    const int64_t b = base + tid;
+    int kb = 0;
+    if (b < B) {
+      kb = k[b];
+      if (kb < 1 || kb > 64) {
+        atomicOr(&s_bad, 1);
+        kb = 0;
+      }
+    }
+    int total = 0;
+    block_excl_scan_1024(kb, s_waves, &total);
+    carry += total;
+  }
+  __syncthreads();
+  const int bad = s_bad ? 1 : (static_cast<int64_t>(carry) != n_rows ? 2 : 0);
+  if (tid == 0) *device_status = bad | s_rows;
+  carry = 0;
+  for (int64_t base = 0; base < B; base += 1024) {
+    const int64_t b = base + tid;
+    const int kb = (b < B && !bad) ? k[b] : 0;
+    int total = 0;
+    const int off = carry + block_excl_scan_1024(kb, s_waves, &total);
+    carry += total;
+    if (b < B) {
+      if (bad) {
+        opd_out[b] = NAN;
+      } else {
+        double sh = 0.0, sr = 0.0;
+        for (int i = 0; i < kb; ++i) {
+          sh += static_cast<double>(hard[off + i]);
+          sr += static_cast<double>(rkl[off + i]);
+        }
+        const double a = static_cast<double>(alpha);
+        opd_out[b] = static_cast<float>((a * sh + (1.0 - a) * sr) / static_cast<double>(kb));
+      }
+    }
+  }
+}
+
 // =========================================================================== status
 // OR of the per-row flags of a clipped-reverse-KL call into *device_status.
 __global__ __launch_bounds__(256) void sv_status_kernel(const int32_t* row_flags, int64_t n,
@@ -497,6 +558,14 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
 // =========================================================================== launchers
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(sv_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_opd_reduce(const int32_t* k, int64_t B, int64_t n_rows, const float* rkl,
+                             const float* hard, float alpha, const int32_t* row_flags,
+                             float* opd_out, int32_t* device_status, hipStream_t st) {
+  hipLaunchKernelGGL(sv_opd_reduce_kernel, dim3(1), dim3(1024), 0, st, k, B, n_rows, rkl, hard,
+                     alpha, row_flags, opd_out, device_status);
   return hipGetLastError();
 }
 

@@ -42,6 +42,8 @@ struct RowPairArgs {
   // outputs
   float delta;
   float* rkl_out;  // nullable in verification
+  float* hard_out;    // rKL only, nullable: -ln q(x*), x* the target row's first argmax
+  int32_t* top1_out;  // rKL only, nullable: x*
   float* p_at;     // nullable
   float* q_at;     // nullable
   int32_t* device_status;
@@ -88,6 +90,9 @@ struct SampleArgs {
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
+hipError_t launch_opd_reduce(const int32_t* k, int64_t B, int64_t n_rows, const float* rkl,
+                             const float* hard, float alpha, const int32_t* row_flags,
+                             float* opd_out, int32_t* device_status, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
 hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);

@@ -647,6 +647,15 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
                                             direct, failed, s_nfail, red_d);
     if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk);
   }
+  if constexpr (MODE == 1) {
+    // hard-label cross-entropy against the target's top-1 (AdaFlash paper, Section 3.1):
+    // -ln q(x*) = -ln2 (l_q(x*) L2E - LZq), temperature 1
+    if (a.hard_out && tid == 0) {
+      const double lq = static_cast<double>(logit_at<DT>(qrow, argp));
+      a.hard_out[ctx.d] = static_cast<float>(-kLn2 * (lq * static_cast<double>(kL2E) - LZ1q));
+      if (a.top1_out) a.top1_out[ctx.d] = argp;
+    }
+  }
   if (tid == 0 && ctx.b >= 0) {
     draw_offsets(LZTq, a.d_off + ctx.d, a.d_lz + ctx.d);
     int accept = 0;
@@ -695,13 +704,21 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (ctx.t < 0 || ctx.t >= a.n_target_rows) {
       if (tid == 0) {
         store_nan(a.rkl_out + unit);
+        if (a.hard_out) store_nan(a.hard_out + unit);
+        if (a.top1_out) a.top1_out[unit] = -1;
         a.row_flags[unit] = 2;  // SV_DEV_ROWS_MISMATCH
       }
       return;
     }
     if (tid == 0) a.row_flags[unit] = 0;
-    rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, 0,
-                                   0.0f, 0.0f);
+    if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
+      ctx.mode = 1;
+      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i,
+                                     0, 0.0f, 0.0f);
+    } else {
+      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i,
+                                     0, 0.0f, 0.0f);
+    }
     return;
   }
 

@@ -159,6 +159,34 @@ sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, i
                          float* rkl_out, int32_t* device_status, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * sv_opd_loss: the on-policy-distillation loss of the AdaFlash paper, Section 3.1 (mixture
+ * OPD loss with reverse-KL, entry-wise divergence clipping; Appendix B.1: temperature 1),
+ * read from the same logits in one pass over each row pair:
+ *     x*_r   = first argmax of target row p_row_index[r]   (the target's top-1 token)
+ *     hard_r = -ln q_r(x*_r)                                (hard-label cross-entropy)
+ *     R_r    = sum_y min(delta, q_r(y) ln(q_r(y) / p(y)))   (as sv_clipped_rkl)
+ *     opd_b  = alpha mean_r hard_r + (1 - alpha) mean_r R_r over request b's k_b rows.
+ *
+ *   B, k            requests and their draft-row counts (int32[B], device, k_b in [1, 64]);
+ *                   the draft rows are packed request by request, sum_b k_b = n_rows.  Needed
+ *                   only with opd_out (else pass NULL and any B).
+ *   p_row_index, n_target_rows, V, ld_*, logits, delta   as sv_clipped_rkl.
+ *   alpha           mixing coefficient in [0, 1].
+ * Outputs (device): rkl_out float[n_rows] and hard_ce_out float[n_rows] (both required),
+ *   top1_out int32[n_rows] (x*, or NULL), opd_out float[B] (or NULL), device_status int32[1]:
+ *   SV_DEV_ROWS_MISMATCH for a p_row_index entry out of range (that row's outputs are NaN) or
+ *   sum_b k_b != n_rows, SV_DEV_BAD_LENGTH for a k_b outside [1, 64] (opd_out is then NaN).
+ * Workspace: sv_rkl_workspace_size(n_rows, V, dtype) bytes, 256-byte aligned.
+ * Errors as sv_clipped_rkl; alpha outside [0, 1] is SV_ERR_VALUE.
+ */
+sv_status sv_opd_loss(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target_rows, int64_t V,
+                      int64_t ld_target, int64_t ld_draft, const void* target_logits,
+                      const void* draft_logits, const int32_t* p_row_index, const int32_t* k,
+                      float delta, float alpha, float* rkl_out, float* hard_ce_out,
+                      int32_t* top1_out, float* opd_out, int32_t* device_status, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* sv_status_string(sv_status s);
 

@@ -101,3 +101,22 @@ def test_rkl_argument_errors(L):
     assert call(delta=-1.0) == 4
     assert call(delta=float("inf")) == 4
     assert call(ws=None, wsb=1 << 30) == 5
+
+
+def test_opd_argument_errors(L):
+    def call(dtype=1, B=1, n=2, nt=2, V=10, ldt=10, ldd=10, tp=8, dp=8, idx=None, k=8,
+             delta=1.0, alpha=0.8, rkl=8, hard=8, top1=None, opd=8, st=8, ws=None, wsb=0):
+        return L.sv_opd_loss(dtype, B, n, nt, V, ldt, ldd, tp, dp, idx, k, delta, alpha, rkl,
+                             hard, top1, opd, st, ws, wsb, None)
+
+    assert call(hard=None) == 1
+    assert call(k=None) == 1  # the per-request loss needs k
+    assert call(B=0) == 2
+    assert call(alpha=1.5) == 4
+    assert call(alpha=float("nan")) == 4
+    assert call(dtype=9) == 3
+    assert call(n=0) == 2
+    assert call(delta=0.0) == 4
+    assert call(rkl=None) == 1
+    assert call(ws=None, wsb=1 << 30) == 5
+    assert call(k=None, opd=None, ws=None, wsb=1 << 30) == 5  # per-row outputs only: k optional
