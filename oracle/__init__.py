@@ -57,4 +57,4 @@ from .verify import (  # noqa: F401
     expected_tau,
 )
 from .rkl import clipped_rkl_row, clipped_rkl  # noqa: F401
-from .opd import hard_ce_row, opd_loss  # noqa: F401
+from .opd import hard_ce_row, opd_loss, clipped_rkl_grad_row, opd_grad  # noqa: F401

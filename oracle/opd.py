@@ -12,6 +12,11 @@ fixes the distillation temperature at 1, so both distributions are plain softmax
 
 for one request whose drafter proposed k positions (after the length head's truncation,
 Section 3.2, k is that request's k_b).  Ties in the argmax go to the lowest id.
+
+The gradient of l_OPD with respect to the drafter's logits (the signal OPD trains with;
+the paper motivates the clip by the outlier gradients it removes, Section 3.1 and
+Figure 3) is derived here from these definitions; where an entry sits exactly on the
+clip (t = delta) the clipped side's derivative, 0, is taken.
 """
 
 from __future__ import annotations
@@ -61,3 +66,43 @@ def opd_loss(target_rows: np.ndarray, draft_rows: np.ndarray, k, delta: float, a
         "rkl_mean": rkl_mean,
         "opd": alpha * hard_mean + (1.0 - alpha) * rkl_mean,
     }
+
+
+def clipped_rkl_grad_row(target_logits: np.ndarray, draft_logits: np.ndarray,
+                         delta: float) -> np.ndarray:
+    """d R / d a_z for one position, a the drafter's logits (temperature 1).
+
+    With L_y = log q_y - log p_y, t_y = q_y L_y and dq_y/da_z = q_y (1[y = z] - q_z):
+        dt_y/da_z = q_y (1[y = z] - q_z) (L_y + 1),
+    and min(delta, t) passes the derivative where t < delta and stops it where the clip is
+    active (at t = delta exactly the clipped side, 0, is taken), so
+        dR/da_z = q_z (g_z - sum_y q_y g_y),   g_y = 1[t_y < delta] (L_y + 1).
+    """
+    log_p = _log_softmax_t1(target_logits)
+    log_q = _log_softmax_t1(draft_logits)
+    q = np.exp(log_q)
+    L = log_q - log_p
+    g = np.where(q * L < delta, L + 1.0, 0.0)
+    return q * (g - math.fsum((q * g).tolist()))
+
+
+def opd_grad(target_rows: np.ndarray, draft_rows: np.ndarray, k, delta: float, alpha: float,
+             p_row_index=None) -> np.ndarray:
+    """d l_OPD,b / d a_r for every draft row r of request b (rows packed, k[b] each):
+        (alpha / k_b) (q_r - e_{x*_r}) + ((1 - alpha) / k_b) dR_r/da_r,
+    the first term the gradient of -log q_r(x*_r), x*_r the target's top-1."""
+    n = draft_rows.shape[0]
+    idx = np.arange(n) if p_row_index is None else np.asarray(p_row_index)
+    k = np.asarray(k, dtype=np.int64)
+    assert int(k.sum()) == n
+    req = np.repeat(np.arange(k.shape[0]), k)
+    out = np.empty(draft_rows.shape, dtype=np.float64)
+    for r in range(n):
+        kb = float(k[req[r]])
+        q = np.exp(_log_softmax_t1(draft_rows[r]))
+        _, x = hard_ce_row(target_rows[idx[r]], draft_rows[r])
+        ce = q.copy()
+        ce[x] -= 1.0
+        out[r] = (alpha / kb) * ce + ((1.0 - alpha) / kb) * clipped_rkl_grad_row(
+            target_rows[idx[r]], draft_rows[r], delta)
+    return out

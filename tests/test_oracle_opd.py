@@ -97,3 +97,95 @@ def test_p_row_index_pairs_rows():
     out = opd_loss(lp, lq, [3], delta=0.5, alpha=0.8, p_row_index=idx)
     for r, t in enumerate(idx):
         assert out["hard"][r] == pytest.approx(hard_ce_row(lp[t], lq[r])[0], rel=1e-15)
+
+
+# ----------------------------------------------------------------------------- gradient
+from oracle import clipped_rkl_grad_row, opd_grad  # noqa: E402
+
+
+def _fd_grad(f, a, h=1e-6):
+    g = np.empty_like(a)
+    for z in range(a.shape[0]):
+        e = np.zeros_like(a)
+        e[z] = h
+        g[z] = (f(a + e) - f(a - e)) / (2 * h)
+    return g
+
+
+def _R(lp, lq, delta):
+    from oracle import clipped_rkl_row
+
+    return clipped_rkl_row(lp, lq, delta)["R"]
+
+
+@pytest.mark.parametrize("delta", [math.inf, 0.05, 0.01])
+def test_rkl_gradient_matches_finite_differences(delta):
+    rng = np.random.default_rng(7)
+    for V in (3, 8, 16):
+        lp = rng.normal(size=V) * 2
+        lq = lp + rng.normal(size=V)
+        g = clipped_rkl_grad_row(lp, lq, delta)
+        # stay away from the kink: no entry within the difference step of delta
+        lpq = sp_log_softmax(lq) - sp_log_softmax(lp)
+        t = np.exp(sp_log_softmax(lq)) * lpq
+        assert np.all(np.abs(t - delta) > 1e-3)
+        fd = _fd_grad(lambda a: _R(lp, a, delta), lq)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-9)
+        assert abs(g.sum()) < 1e-12  # logits are shift-invariant
+
+
+def test_rkl_gradient_equals_autograd_of_the_definition():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    lp = rng.normal(size=40) * 3
+    lq = lp + rng.normal(size=40) * 1.5
+    for delta in (math.inf, 0.02):
+        a = torch.tensor(lq, dtype=torch.float64, requires_grad=True)
+        log_q = torch.log_softmax(a, 0)
+        log_p = torch.log_softmax(torch.tensor(lp, dtype=torch.float64), 0)
+        terms = log_q.exp() * (log_q - log_p)
+        loss = torch.clamp(terms, max=delta).sum() if math.isfinite(delta) else terms.sum()
+        loss.backward()
+        np.testing.assert_allclose(clipped_rkl_grad_row(lp, lq, delta), a.grad.numpy(),
+                                   rtol=1e-12, atol=1e-15)
+
+
+def test_unclipped_gradient_is_the_kl_gradient():
+    # delta -> inf: dKL(q||p)/da_z = q_z (L_z - KL)
+    rng = np.random.default_rng(9)
+    lp, lq = rng.normal(size=25), rng.normal(size=25)
+    q = np.exp(sp_log_softmax(lq))
+    L = sp_log_softmax(lq) - sp_log_softmax(lp)
+    kl = float(np.sum(rel_entr(q, np.exp(sp_log_softmax(lp)))))
+    np.testing.assert_allclose(clipped_rkl_grad_row(lp, lq, math.inf), q * (L - kl),
+                               rtol=1e-12, atol=1e-16)
+
+
+def test_clip_cuts_the_gradient_of_every_positive_term():
+    # delta below every positive term: those entries pass no gradient, the negative ones do
+    lp = np.log(np.array([0.1, 0.2, 0.3, 0.4]))
+    lq = np.log(np.array([0.4, 0.3, 0.2, 0.1]))
+    t = np.array([0.4, 0.3, 0.2, 0.1]) * (lq - lp)
+    g = clipped_rkl_grad_row(lp, lq, delta=1e-9)
+    neg = t < 0
+    assert np.any(neg)  # negative terms keep a gradient; positives are cut
+    q = np.exp(lq)
+    gy = np.where(neg, (lq - lp) + 1.0, 0.0)
+    np.testing.assert_allclose(g, q * (gy - np.sum(q * gy)), rtol=1e-13)
+
+
+def test_opd_gradient_matches_finite_differences_of_the_loss():
+    rng = np.random.default_rng(10)
+    lp = rng.normal(size=(5, 12)) * 2
+    lq = lp + rng.normal(size=(5, 12))
+    k = [2, 3]
+    delta, alpha = 0.05, 0.8
+    g = opd_grad(lp, lq, k, delta, alpha)
+    off = [0, 2, 5]
+    for b in range(2):
+        for r in range(off[b], off[b + 1]):
+            def f(a, r=r, b=b):
+                rows = lq[off[b]:off[b + 1]].copy()
+                rows[r - off[b]] = a
+                return opd_loss(lp[off[b]:off[b + 1]], rows, [k[b]], delta, alpha)["opd"][0]
+            np.testing.assert_allclose(g[r], _fd_grad(f, lq[r]), rtol=1e-6, atol=1e-9)
