@@ -115,7 +115,7 @@ def cpu_baseline_opd(w, idx, n_requests: int) -> dict:
                       f"OPD loss), float64 NumPy, {cores} worker processes, {dt:.2f} s wall"}
 
 
-def bench_opd(args, w):
+def bench_opd(args, w, grad=False):
     import numpy as np
     import torch
 
@@ -141,16 +141,23 @@ def bench_opd(args, w):
     idx, k = up(idx_np), up(w.k.astype(np.int32))
     n, V, B = w.n_draft_rows, w.V, w.B
     code = pkg.SV_BF16 if w.dtype == "bf16" else pkg.SV_F32
-    ws = pkg.alloc_workspace(int(pkg.lib().sv_rkl_workspace_size(n, V, code)), dev)
+    size_fn = pkg.lib().sv_opd_grad_workspace_size if grad else pkg.lib().sv_rkl_workspace_size
+    ws = pkg.alloc_workspace(int(size_fn(n, V, code)), dev)
     out = {"rkl": torch.empty(n, dtype=torch.float32, device=dev),
            "hard_ce": torch.empty(n, dtype=torch.float32, device=dev),
            "top1": torch.empty(n, dtype=torch.int32, device=dev),
            "opd": torch.empty(B, dtype=torch.float32, device=dev),
            "device_status": torch.empty(1, dtype=torch.int32, device=dev)}
+    if grad:  # the gradient in the logits' dtype
+        out["grad"] = torch.empty(n, V, dtype=target.dtype, device=dev)
 
     def step():
-        pkg.opd_loss(target, draft, k, delta=w.delta, alpha=0.8, p_row_index=idx, workspace=ws,
-                     out=out)
+        if grad:
+            pkg.opd_loss_grad(target, draft, k, delta=w.delta, alpha=0.8, p_row_index=idx,
+                              workspace=ws, out=out)
+        else:
+            pkg.opd_loss(target, draft, k, delta=w.delta, alpha=0.8, p_row_index=idx,
+                         workspace=ws, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -170,17 +177,25 @@ def bench_opd(args, w):
     pkg.profile_enable(False)
     kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
     esize = 2 if w.dtype == "bf16" else 4
-    rows_bytes = 2 * n * V * esize  # each draft row and its target row, once
-    achieved = rows_bytes / (kernels["sv_opd_rowpair"] * 1e-6) / 1e9
+    if grad:  # the roofline kernel is the gradient pass: both rows read, the gradient written
+        rows_bytes = 3 * n * V * esize
+        roof_kernel = "sv_opd_grad"
+        metric = "OPD loss + gradient row pairs/sec (forward pass, then gradient rows)"
+    else:  # each draft row and its target row, once
+        rows_bytes = 2 * n * V * esize
+        roof_kernel = "sv_opd_rowpair"
+        metric = "OPD loss row pairs/sec (hard CE + clipped rKL + per-request loss)"
+    achieved = rows_bytes / (kernels[roof_kernel] * 1e-6) / 1e9
     res = {
-        "metric": "OPD loss row pairs/sec (hard CE + clipped rKL + per-request loss)",
+        "metric": metric,
         "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded logits shaped like the pages' workloads)",
-        "config": {"workload": w.name, "op": "opd_loss", "rows": n, "B": B, "V": V,
+        "config": {"workload": w.name, "op": args.op, "rows": n, "B": B, "V": V,
                    "input_dtype": w.dtype, "delta": w.delta, "alpha": 0.8,
-                   "algorithmic_bytes_per_step": rows_bytes},
+                   "roofline_kernel": roof_kernel,
+                   "roofline_kernel_bytes": rows_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
         "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
@@ -195,7 +210,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--op", choices=("verify", "opd"), default="verify")
+    ap.add_argument("--op", choices=("verify", "opd", "opd_grad"), default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -229,8 +244,8 @@ def main():
     t0 = time.perf_counter()
     w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
-    if args.op == "opd":
-        return bench_opd(args, w)
+    if args.op in ("opd", "opd_grad"):
+        return bench_opd(args, w, grad=(args.op == "opd_grad"))
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")

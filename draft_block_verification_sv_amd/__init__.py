@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     opd_loss,
+    opd_loss_grad,
     profile_enable,
     profile_read,
     profile_reset,

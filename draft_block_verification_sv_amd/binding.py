@@ -58,6 +58,12 @@ def lib() -> ctypes.CDLL:
                               _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                               _c_sz, _c_p]
     L.sv_opd_loss.restype = _c_i32
+    L.sv_opd_grad_workspace_size.argtypes = [_c_i64, _c_i64, _c_i32]
+    L.sv_opd_grad_workspace_size.restype = _c_sz
+    L.sv_opd_loss_grad.argtypes = [_c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
+                                   _c_p, _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p,
+                                   _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_opd_loss_grad.restype = _c_i32
     L.sv_status_string.argtypes = [_c_i32]
     L.sv_status_string.restype = ctypes.c_char_p
     L.sv_version.argtypes = []
@@ -248,6 +254,57 @@ def opd_loss(target: torch.Tensor, draft: torch.Tensor, k: Optional[torch.Tensor
                            _ptr(out["device_status"]), _ptr(workspace),
                            workspace.numel(), _stream(stream))
     _check(st, "sv_opd_loss")
+    return out
+
+
+def opd_loss_grad(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
+                  delta: float = 1.0, alpha: float = 0.8,
+                  p_row_index: Optional[torch.Tensor] = None, *,
+                  grad_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                  stream=None) -> dict:
+    """sv_opd_loss_grad: the sv_opd_loss outputs plus "grad", d l_OPD / d draft logits
+    ([n_rows, V], bfloat16 or float32; default the logits' dtype)."""
+    dev, code, n, V = _row_pair_shapes(target, draft, p_row_index)
+    if k.dim() != 1:
+        raise ValueError("k must be 1-D")
+    B = int(k.numel())
+    _need(k, "k", torch.int32, B, dev)
+    gdt = target.dtype if grad_dtype is None else grad_dtype
+    gcode = _dtype_code(torch.empty(0, dtype=gdt))
+    if workspace is None:
+        nbytes = int(lib().sv_opd_grad_workspace_size(n, V, code))
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape n_rows={n} V={V}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {
+            "rkl": torch.empty(n, dtype=torch.float32, device=dev),
+            "hard_ce": torch.empty(n, dtype=torch.float32, device=dev),
+            "top1": torch.empty(n, dtype=torch.int32, device=dev),
+            "opd": torch.empty(B, dtype=torch.float32, device=dev),
+            "grad": torch.empty(n, V, dtype=gdt, device=dev),
+            "device_status": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    else:
+        _need(out["rkl"], "rkl", torch.float32, n, dev)
+        _need(out["hard_ce"], "hard_ce", torch.float32, n, dev)
+        if out.get("top1") is not None:
+            _need(out["top1"], "top1", torch.int32, n, dev)
+        if out.get("opd") is not None:
+            _need(out["opd"], "opd", torch.float32, B, dev)
+        _need(out["device_status"], "device_status", torch.int32, 1, dev)
+    g = out["grad"]
+    if (g.device != dev or g.dtype != gdt or g.dim() != 2 or g.shape[0] != n or g.shape[1] != V
+            or g.stride(1) != 1):
+        raise ValueError(f"grad must be a [{n}, {V}] {gdt} tensor with unit column stride")
+    st = lib().sv_opd_loss_grad(code, B, n, int(target.shape[0]), V, target.stride(0),
+                                draft.stride(0), _ptr(target), _ptr(draft), _ptr(p_row_index),
+                                _ptr(k), float(delta), float(alpha), _ptr(out["rkl"]),
+                                _ptr(out["hard_ce"]), _ptr(out.get("top1")), _ptr(out.get("opd")),
+                                gcode, g.stride(0), _ptr(g), _ptr(out["device_status"]),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sv_opd_loss_grad")
     return out
 
 

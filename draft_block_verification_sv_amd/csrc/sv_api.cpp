@@ -17,10 +17,11 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 9;
+constexpr int kNumKernels = 12;
 const char* const kKernelNames[kNumKernels] = {
-    "sv_plan",        "sv_rowpair",    "sv_sample_mass", "sv_sample",    "sv_rkl_rowpair",
-    "sv_rkl_status",  "sv_opd_rowpair", "sv_opd_status", "sv_opd_reduce"};
+    "sv_plan",        "sv_rowpair",     "sv_sample_mass", "sv_sample",
+    "sv_rkl_rowpair", "sv_rkl_status",  "sv_opd_rowpair", "sv_opd_status",
+    "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -30,7 +31,10 @@ enum {
   K_RKL_STATUS,
   K_OPD_ROWPAIR,
   K_OPD_STATUS,
-  K_OPD_REDUCE
+  K_OPD_REDUCE,
+  K_GRAD_ROWPAIR,
+  K_GRAD_REDUCE,
+  K_GRAD
 };
 
 // ------------------------------------------------------------------ profiling
@@ -125,8 +129,9 @@ Dims verify_dims(int64_t B, int64_t k_max, int64_t V) {
   return d;
 }
 
-Dims rkl_dims(int64_t n_rows, int64_t V) {
+Dims rkl_dims(int64_t n_rows, int64_t V, bool with_grad = false) {
   Dims d{};
+  d.n_grad = with_grad ? n_rows : 0;
   d.B = 1;
   d.n_t = 0;
   d.n_d = 0;
@@ -153,12 +158,12 @@ sv_status rkl_rows(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t
                    const void* draft_logits, const int32_t* p_row_index, float delta,
                    float* rkl_out, float* hard_out, int32_t* top1_out, int32_t* device_status,
                    void* workspace, size_t workspace_bytes, hipStream_t st, int k_rowpair,
-                   int k_status, Workspace* ws_out) {
+                   int k_status, Workspace* ws_out, bool with_grad = false) {
   if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
   if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
   if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
   if (n_rows >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
-  const Dims dm = rkl_dims(n_rows, V);
+  const Dims dm = rkl_dims(n_rows, V, with_grad);
   if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
   if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
   const size_t need = sv::carve(dm, nullptr, nullptr);
@@ -184,6 +189,7 @@ sv_status rkl_rows(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t
   ra.rkl_out = rkl_out;
   ra.hard_out = hard_out;
   ra.top1_out = top1_out;
+  ra.stats = with_grad ? ws.stats : nullptr;
   ra.device_status = device_status;
   ra.row_flags = ws.row_flags;
   if (timed(k_rowpair, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
@@ -362,8 +368,59 @@ sv_status sv_opd_loss(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target
   if (s != SV_OK || !opd_out) return s;
   if (timed(K_OPD_REDUCE, st, [&] {
         return sv::launch_opd_reduce(k, B, n_rows, rkl_out, hard_ce_out, alpha, ws.row_flags,
-                                     opd_out, device_status, st);
+                                     opd_out, nullptr, device_status, st);
       }) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+size_t sv_opd_grad_workspace_size(int64_t n_rows, int64_t V, int32_t dtype) {
+  if (!dtype_ok(dtype) || n_rows < 1 || n_rows >= (int64_t(1) << 31) || !shape_ok(V, V, V)) return 0;
+  return sv::carve(rkl_dims(n_rows, V, true), nullptr, nullptr);
+}
+
+sv_status sv_opd_loss_grad(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target_rows,
+                           int64_t V, int64_t ld_target, int64_t ld_draft,
+                           const void* target_logits, const void* draft_logits,
+                           const int32_t* p_row_index, const int32_t* k, float delta, float alpha,
+                           float* rkl_out, float* hard_ce_out, int32_t* top1_out, float* opd_out,
+                           int32_t grad_dtype, int64_t ld_grad, void* grad_out,
+                           int32_t* device_status, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!hard_ce_out || !k || !grad_out) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || ld_grad < V) return SV_ERR_SHAPE;
+  if (!dtype_ok(grad_dtype)) return SV_ERR_DTYPE;
+  if (!(std::isfinite(alpha) && alpha >= 0.0f && alpha <= 1.0f)) return SV_ERR_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws{};
+  const sv_status s = rkl_rows(dtype, n_rows, n_target_rows, V, ld_target, ld_draft, target_logits,
+                               draft_logits, p_row_index, delta, rkl_out, hard_ce_out, top1_out,
+                               device_status, workspace, workspace_bytes, st, K_GRAD_ROWPAIR,
+                               K_OPD_STATUS, &ws, true);
+  if (s != SV_OK) return s;
+  if (timed(K_GRAD_REDUCE, st, [&] {
+        return sv::launch_opd_reduce(k, B, n_rows, rkl_out, hard_ce_out, alpha, ws.row_flags,
+                                     opd_out, ws.coef, device_status, st);
+      }) != hipSuccess)
+    return SV_ERR_HIP;
+  sv::GradArgs ga{};
+  ga.target = target_logits;
+  ga.draft = draft_logits;
+  ga.ld_t = ld_target;
+  ga.ld_d = ld_draft;
+  ga.ld_g = ld_grad;
+  ga.V = static_cast<int32_t>(V);
+  ga.n_rows = n_rows;
+  ga.n_target_rows = n_target_rows;
+  ga.p_row_index = p_row_index;
+  ga.delta = delta;
+  ga.stats = ws.stats;
+  ga.coef = ws.coef;
+  ga.grad = grad_out;
+  const bool vec = vec_ok(dtype, ld_target, target_logits) &&
+                   vec_ok(dtype, ld_draft, draft_logits) && vec_ok(grad_dtype, ld_grad, grad_out);
+  if (timed(K_GRAD, st, [&] { return sv::launch_opd_grad(dtype, grad_dtype, vec, ga, st); }) !=
+      hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

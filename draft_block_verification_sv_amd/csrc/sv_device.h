@@ -26,6 +26,12 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Eight consecutive bf16 values (one 16-byte load) widened to fp32.
+__device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
 // ---------------------------------------------------------------- fp64 exp2 / log2
 // Inlined double-precision 2^x and log2(x) for the per-row finalize (the library versions
 // are large enough to be emitted as calls, which costs the streaming kernels registers).

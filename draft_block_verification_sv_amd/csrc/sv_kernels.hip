@@ -94,11 +94,13 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
 // scan of k for the row offsets, then each thread sums its requests' rows in row order in
 // fp64.  Bad lengths or sum k_b != n_rows give NaN and SV_DEV_* bits; *device_status is
 // written once, with the rows' own flags (row_flags) folded in.
+// With coef, also each row's gradient coefficients (alpha / k_b, (1 - alpha) / k_b) (NaN
+// for a void call).
 __global__ __launch_bounds__(1024) void sv_opd_reduce_kernel(const int32_t* k, int64_t B,
                                                              int64_t n_rows, const float* rkl,
                                                              const float* hard, float alpha,
                                                              const int32_t* row_flags,
-                                                             float* opd_out,
+                                                             float* opd_out, float* coef,
                                                              int32_t* device_status) {
   __shared__ int s_waves[16];
   __shared__ int s_bad, s_rows;
@@ -135,15 +137,119 @@ __global__ __launch_bounds__(1024) void sv_opd_reduce_kernel(const int32_t* k, i
     carry += total;
     if (b < B) {
       if (bad) {
-        opd_out[b] = NAN;
+        if (opd_out) opd_out[b] = NAN;
       } else {
-        double sh = 0.0, sr = 0.0;
-        for (int i = 0; i < kb; ++i) {
-          sh += static_cast<double>(hard[off + i]);
-          sr += static_cast<double>(rkl[off + i]);
-        }
         const double a = static_cast<double>(alpha);
-        opd_out[b] = static_cast<float>((a * sh + (1.0 - a) * sr) / static_cast<double>(kb));
+        if (opd_out) {
+          double sh = 0.0, sr = 0.0;
+          for (int i = 0; i < kb; ++i) {
+            sh += static_cast<double>(hard[off + i]);
+            sr += static_cast<double>(rkl[off + i]);
+          }
+          opd_out[b] = static_cast<float>((a * sh + (1.0 - a) * sr) / static_cast<double>(kb));
+        }
+        if (coef) {
+          const float ch = static_cast<float>(a / kb), cr = static_cast<float>((1.0 - a) / kb);
+          for (int i = 0; i < kb; ++i) {
+            coef[2 * (off + i)] = ch;
+            coef[2 * (off + i) + 1] = cr;
+          }
+        }
+      }
+    }
+  }
+  if (bad && coef)
+    for (int64_t i = tid; i < 2 * n_rows; i += 1024) coef[i] = NAN;
+}
+
+// =========================================================================== OPD gradient
+// d l_OPD,b / d a_z for every draft row r of request b, a its drafter logits (temperature 1):
+//   c_h (q_z - 1[z = x*]) + c_r q_z (g_z - S_g),   g_z = 1[t_z < delta] (L_z + 1),
+// with L_z = ln q_z - ln p_z, t_z = q_z L_z, c_h = alpha / k_b, c_r = (1 - alpha) / k_b, and
+// S_g = sum_y q_y g_y from the forward pass (the clip passes no gradient where it is active;
+// on t = delta exactly the clipped side is taken).  One 256-thread workgroup per row, each
+// thread 8 consecutive columns per step; the row is read once more and the gradient row
+// written once.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* row, int64_t col, int V, bool vec, float (&x)[8]) {
+  if constexpr (DT == 0) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + col;
+    if (vec && col + 8 <= V) {
+      unpack8(*reinterpret_cast<const uint4*>(p), x);
+    } else {
+      for (int e = 0; e < 8; ++e) x[e] = (col + e < V) ? bf16_at(p + e) : 0.0f;
+    }
+  } else {
+    const float* p = static_cast<const float*>(row) + col;
+    if (vec && col + 8 <= V) {
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+      for (int e = 0; e < 8; ++e) x[e] = (col + e < V) ? p[e] : 0.0f;
+    }
+  }
+}
+
+template <int DT, int GT, bool VEC>
+__global__ __launch_bounds__(256) void sv_opd_grad_kernel(GradArgs a) {
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t t = a.p_row_index ? a.p_row_index[r] : r;
+  const int V = a.V;
+  const bool ok = t >= 0 && t < a.n_target_rows;  // a void call has NaN coefficients
+  const RowStats st = a.stats[r];
+  const float ch = a.coef[2 * r], cr = a.coef[2 * r + 1];
+  const double Kq = rint(st.lzq);
+  const float kq = static_cast<float>(-Kq), fq = static_cast<float>(st.lzq - Kq);
+  const float c2 = static_cast<float>(st.lzp - st.lzq);
+  const float sg = static_cast<float>(st.sg);
+  const int x = st.top1;
+  const float ln2 = static_cast<float>(kLn2);
+  const size_t es = DT == 0 ? 2 : 4;
+  const void* prow = static_cast<const char*>(a.target) + (ok ? t : 0) * a.ld_t * es;
+  const void* qrow = static_cast<const char*>(a.draft) + r * a.ld_d * es;
+  char* grow = static_cast<char*>(a.grad) + r * a.ld_g * (GT == 0 ? 2 : 4);
+  for (int64_t col = static_cast<int64_t>(tid) * 8; col < V; col += 256 * 8) {
+    float lp[8], lq[8], g[8];
+    load8<DT>(prow, col, V, VEC, lp);
+    load8<DT>(qrow, col, V, VEC, lq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = fast_exp2(__builtin_fmaf(lq[e], kL2E, kq) - fq);
+      const float L = ln2 * __builtin_fmaf(lq[e] - lp[e], kL2E, c2);
+      const float gz = (q * L < a.delta) ? L + 1.0f : 0.0f;
+      const float onehot = (col + e == x) ? 1.0f : 0.0f;
+      g[e] = ok ? __builtin_fmaf(cr * q, gz - sg, ch * (q - onehot)) : NAN;
+    }
+    if constexpr (GT == 0) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(grow) + col;
+      if (VEC && col + 8 <= V) {
+        uint4 w;
+        w.x = bf16_rne(g[0]) | (static_cast<uint32_t>(bf16_rne(g[1])) << 16);
+        w.y = bf16_rne(g[2]) | (static_cast<uint32_t>(bf16_rne(g[3])) << 16);
+        w.z = bf16_rne(g[4]) | (static_cast<uint32_t>(bf16_rne(g[5])) << 16);
+        w.w = bf16_rne(g[6]) | (static_cast<uint32_t>(bf16_rne(g[7])) << 16);
+        *reinterpret_cast<uint4*>(o) = w;
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (col + e < V) o[e] = bf16_rne(g[e]);
+      }
+    } else {
+      float* o = reinterpret_cast<float*>(grow) + col;
+      if (VEC && col + 8 <= V) {
+        *reinterpret_cast<float4*>(o) = make_float4(g[0], g[1], g[2], g[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(g[4], g[5], g[6], g[7]);
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (col + e < V) o[e] = g[e];
       }
     }
   }
@@ -178,10 +284,6 @@ __device__ __forceinline__ float draw_mass(float lp, float lq, bool need_q, cons
   return need_q ? fmaxf(p - fast_exp2(__builtin_fmaf(lq, k.beta, k.offq) - k.lzq), 0.0f) : p;
 }
 
-__device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
-  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-}
 
 template <int DT, bool VEC>
 __device__ __forceinline__ void column_masses(const SampleArgs& a, int64_t t, int64_t d,
@@ -563,9 +665,27 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 
 hipError_t launch_opd_reduce(const int32_t* k, int64_t B, int64_t n_rows, const float* rkl,
                              const float* hard, float alpha, const int32_t* row_flags,
-                             float* opd_out, int32_t* device_status, hipStream_t st) {
+                             float* opd_out, float* coef, int32_t* device_status, hipStream_t st) {
   hipLaunchKernelGGL(sv_opd_reduce_kernel, dim3(1), dim3(1024), 0, st, k, B, n_rows, rkl, hard,
-                     alpha, row_flags, opd_out, device_status);
+                     alpha, row_flags, opd_out, coef, device_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.n_rows)), blk(256);
+  if (dtype == 0 && grad_dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_opd_grad_kernel<0, 0, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((sv_opd_grad_kernel<0, 0, false>), grid, blk, 0, st, a);
+  } else if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_opd_grad_kernel<0, 1, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((sv_opd_grad_kernel<0, 1, false>), grid, blk, 0, st, a);
+  } else if (grad_dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_opd_grad_kernel<1, 0, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((sv_opd_grad_kernel<1, 0, false>), grid, blk, 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((sv_opd_grad_kernel<1, 1, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((sv_opd_grad_kernel<1, 1, false>), grid, blk, 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ struct RowPairArgs {
   float* rkl_out;  // nullable in verification
   float* hard_out;    // rKL only, nullable: -ln q(x*), x* the target row's first argmax
   int32_t* top1_out;  // rKL only, nullable: x*
+  RowStats* stats;    // rKL only, nullable: statistics for the OPD gradient pass
   float* p_at;     // nullable
   float* q_at;     // nullable
   int32_t* device_status;
@@ -92,7 +93,22 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
 hipError_t launch_opd_reduce(const int32_t* k, int64_t B, int64_t n_rows, const float* rkl,
                              const float* hard, float alpha, const int32_t* row_flags,
-                             float* opd_out, int32_t* device_status, hipStream_t st);
+                             float* opd_out, float* coef, int32_t* device_status, hipStream_t st);
+
+// The gradient pass of the OPD loss: one workgroup per draft row.
+struct GradArgs {
+  const void* target;
+  const void* draft;
+  int64_t ld_t, ld_d, ld_g;
+  int32_t V;
+  int64_t n_rows, n_target_rows;
+  const int32_t* p_row_index;  // nullable = identity
+  float delta;
+  const RowStats* stats;
+  const float* coef;  // NaN for a void call (bad lengths): the gradient is NaN
+  void* grad;         // [n_rows, ld_g] of the gradient dtype
+};
+hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& a, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
 hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);

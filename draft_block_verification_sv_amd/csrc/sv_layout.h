@@ -54,6 +54,14 @@ struct RowDesc {
   int32_t b;  // request
 };
 
+// Per draft row, from the OPD forward pass for the gradient pass: both log2 normalisers,
+// sum_y q_y g_y (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)) and the target's top-1.
+struct RowStats {
+  double lzp, lzq, sg;
+  int32_t top1;
+  int32_t pad;
+};
+
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
   int32_t* glob;       // [4]: [0] call void (bad lengths / row count)
@@ -68,10 +76,13 @@ struct Workspace {
   float* d_lz;         // [n_d]
   int32_t* acc;        // [n_d] acceptance flag
   double* chunk_mass;  // [B * n_chunks] draw mass of each chunk of each request's draw row
+  RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
+  float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
 };
 
 struct Dims {
   int64_t B, n_t, n_d, V, n_units, n_slices, n_chunks;
+  int64_t n_grad;  // rows of the OPD gradient pass (0 otherwise)
 };
 
 // Lays out the regions (each 256-byte aligned) and returns the total byte count.
@@ -96,6 +107,8 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.d_lz = reinterpret_cast<float*>(take(d.n_d * 4));
   w.acc = reinterpret_cast<int32_t*>(take(d.n_d * 4));
   w.chunk_mass = reinterpret_cast<double*>(take(d.B * d.n_chunks * sizeof(double)));
+  w.stats = reinterpret_cast<RowStats*>(take(d.n_grad * sizeof(RowStats)));
+  w.coef = reinterpret_cast<float*>(take(d.n_grad * 2 * sizeof(float)));
   if (ws) *ws = w;
   return off;
 }

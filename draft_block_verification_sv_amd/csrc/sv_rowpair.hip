@@ -526,19 +526,28 @@ __device__ __forceinline__ float logit_at(const void* row, int64_t col) {
 // and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
 // ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p.  A lane whose bound may reach
 // delta has its columns re-read by one wave and summed entry by entry.
-template <int DT>
-__device__ __forceinline__ double lanes_clipped_rkl(const void* prow, const void* qrow, int V,
-                                                   int n_slices, double LZp, double LZq,
-                                                   float delta, const LaneAcc& A, double* direct,
-                                                   int* failed, int* s_nfail, double* red) {
+// With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
+// OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
+// form plus Q.
+struct RklSums {
+  double R, sg;
+};
+
+template <int DT, bool SG>
+__device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const void* qrow, int V,
+                                                    int n_slices, double LZp, double LZq,
+                                                    float delta, const LaneAcc& A, double* direct,
+                                                    double* direct_sg, int* failed, int* s_nfail,
+                                                    double* red) {
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double c2 = LZp - LZq;
-  double closed = 0.0;
+  double closed = 0.0, mass = 0.0;
   bool fail = false;
   if (A.sq > 0.0) {
     const double scale = kLn2 * exp2_d(static_cast<double>(A.kq) - LZq);
     closed = scale * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
+    mass = scale * A.sq / kLn2;
     const double slope = static_cast<double>(kL2E) * A.dmax + c2;
     const double bound = scale * A.sq * (slope > 0.0 ? slope : 0.0);
     fail = !(bound * 1.0001 < static_cast<double>(delta));
@@ -553,7 +562,7 @@ __device__ __forceinline__ double lanes_clipped_rkl(const void* prow, const void
     const int src = failed[f];
     const int sw = src >> 6, sl = src & 63;  // the failing lane's wave and lane
     const int n_pieces = ((n_slices - sw + kRowWaves - 1) / kRowWaves) * kGroups;
-    float part = 0.0f;
+    float part = 0.0f, gpart = 0.0f;
     for (int j = lane; j < n_pieces; j += 64) {
       const int64_t col0 = static_cast<int64_t>(sw + (j / kGroups) * kRowWaves) * kSlice +
                            (j % kGroups) * 512 + sl * 8;
@@ -566,14 +575,22 @@ __device__ __forceinline__ double lanes_clipped_rkl(const void* prow, const void
           const float q = fast_exp2(static_cast<float>(static_cast<double>(lq) * kL2E - LZq));
           const float term = q * static_cast<float>(kLn2) * __builtin_fmaf(lq - lp, kL2E, c2f);
           part += fminf(term, delta);
+          if constexpr (SG) gpart += term < delta ? term + q : 0.0f;
         }
       }
     }
     const double dsum = wave_sum_d(static_cast<double>(part));
     if (lane == 0) direct[src] = dsum;
+    if constexpr (SG) {
+      const double gsum = wave_sum_d(static_cast<double>(gpart));
+      if (lane == 0) direct_sg[src] = gsum;
+    }
   }
   __syncthreads();
-  return block_sum_d(fail ? direct[tid] : closed, red);
+  RklSums out;
+  out.R = block_sum_d(fail ? direct[tid] : closed, red);
+  out.sg = SG ? block_sum_d(fail ? direct_sg[tid] : closed + mass, red) : 0.0;
+  return out;
 }
 
 // Offsets the sampler uses to rebuild a row's p_T: p_T(y) = 2^(fma(l_y, beta, off) - lz)
@@ -595,8 +612,8 @@ struct RowCtx {
 
 template <int DT, bool VEC, bool PAIR, int MODE>
 __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
-                                             LaneAcc* lacc, double* direct, int* failed,
-                                             int* s_nfail,
+                                             LaneAcc* lacc, double* direct, double* direct_sg,
+                                             int* failed, int* s_nfail,
                                              double* red_d, float* red_f, int* red_i, int x,
                                              float lpx, float lqx) {
   const int tid = thread_index(), lane = tid & 63;
@@ -643,9 +660,23 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   const double LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
   const double LZTq = (MODE == 2) ? lanes_lz(A.ktq, A.stq, red_f, red_d) : LZ1q;
   if (a.rkl_out) {
-    const double Rk = lanes_clipped_rkl<DT>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A,
-                                            direct, failed, s_nfail, red_d);
-    if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk);
+    RklSums Rk;
+    if (MODE == 1 && a.stats)
+      Rk = lanes_clipped_rkl<DT, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
+                                       direct_sg, failed, s_nfail, red_d);
+    else
+      Rk = lanes_clipped_rkl<DT, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
+                                        direct_sg, failed, s_nfail, red_d);
+    if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk.R);
+    if (MODE == 1 && a.stats && tid == 0) {
+      RowStats st;
+      st.lzp = LZ1p;
+      st.lzq = LZ1q;
+      st.sg = Rk.sg;
+      st.top1 = argp;
+      st.pad = 0;
+      a.stats[ctx.d] = st;
+    }
   }
   if constexpr (MODE == 1) {
     // hard-label cross-entropy against the target's top-1 (AdaFlash paper, Section 3.1):
@@ -683,6 +714,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_
 void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ LaneAcc lacc[kRowThreads];
   __shared__ double direct[kRowThreads];
+  __shared__ double direct_sg[kRowThreads];
   __shared__ int failed[kRowThreads];
   __shared__ int s_nfail;
   __shared__ double red_d[kRowWaves];
@@ -713,10 +745,10 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (tid == 0) a.row_flags[unit] = 0;
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
-      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     } else {
-      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     }
     return;
@@ -859,13 +891,13 @@ void sv_rowpair_kernel(RowPairArgs a) {
   const int x = s_x;
   const float lpx = s_lpx, lqx = s_lqx;
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, true, 2>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, false, 0>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, lacc, direct, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   }
 }
 

@@ -187,6 +187,39 @@ sv_status sv_opd_loss(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target
                       int32_t* top1_out, float* opd_out, int32_t* device_status, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace sv_opd_loss_grad needs for n_rows row pairs; 0 if invalid. */
+size_t sv_opd_grad_workspace_size(int64_t n_rows, int64_t V, int32_t dtype);
+
+/*
+ * sv_opd_loss_grad: everything sv_opd_loss computes, plus the gradient of each request's
+ * l_OPD with respect to its drafter logits, the signal on-policy distillation trains the
+ * drafter with (AdaFlash paper, Section 3.1: the clip exists to bound the gradients of a few
+ * high-divergence entries).  For draft row r of request b, column z:
+ *     grad[r, z] = alpha/k_b (q_z - 1[z = x*_r]) + (1 - alpha)/k_b q_z (g_z - sum_y q_y g_y),
+ *     g_y = 1[t_y < delta] (ln q_y - ln p_y + 1),  t_y = q_y ln(q_y / p_y),
+ * temperature 1; where an entry sits exactly on the clip (t = delta) the clipped side's
+ * derivative, 0, is taken.  Two passes over each row pair: the forward (sv_opd_loss's kernel,
+ * which also keeps per-row statistics in the workspace) and the gradient pass, which reads the
+ * pair again and writes the gradient row once.
+ *
+ *   k               int32[B] (required): draft rows per request, packed, sum = n_rows.
+ *   grad_dtype      SV_BF16 (rounded to nearest even) or SV_F32.
+ *   ld_grad         row stride of grad_out in elements (>= V); columns [V, ld_grad) untouched.
+ *   grad_out        device [n_rows, ld_grad] of grad_dtype; must not overlap any input.
+ *   other arguments as sv_opd_loss (opd_out and top1_out may be NULL).
+ * A request set with bad lengths (SV_DEV_BAD_LENGTH / SV_DEV_ROWS_MISMATCH from k) gets NaN
+ * gradients everywhere; a row whose p_row_index entry is out of range gets a NaN row.
+ * Workspace: sv_opd_grad_workspace_size(n_rows, V, dtype) bytes, 256-byte aligned.
+ */
+sv_status sv_opd_loss_grad(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_target_rows,
+                           int64_t V, int64_t ld_target, int64_t ld_draft,
+                           const void* target_logits, const void* draft_logits,
+                           const int32_t* p_row_index, const int32_t* k, float delta, float alpha,
+                           float* rkl_out, float* hard_ce_out, int32_t* top1_out, float* opd_out,
+                           int32_t grad_dtype, int64_t ld_grad, void* grad_out,
+                           int32_t* device_status, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Static text for a status code. */
 const char* sv_status_string(sv_status s);
 

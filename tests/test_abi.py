@@ -120,3 +120,23 @@ def test_opd_argument_errors(L):
     assert call(rkl=None) == 1
     assert call(ws=None, wsb=1 << 30) == 5
     assert call(k=None, opd=None, ws=None, wsb=1 << 30) == 5  # per-row outputs only: k optional
+
+
+def test_opd_grad_argument_errors(L):
+    def call(dtype=1, B=1, n=2, nt=2, V=10, ldt=10, ldd=10, tp=8, dp=8, idx=None, k=8,
+             delta=1.0, alpha=0.8, rkl=8, hard=8, top1=None, opd=None, gdt=1, ldg=10, g=8,
+             st=8, ws=None, wsb=0):
+        return L.sv_opd_loss_grad(dtype, B, n, nt, V, ldt, ldd, tp, dp, idx, k, delta, alpha, rkl,
+                                  hard, top1, opd, gdt, ldg, g, st, ws, wsb, None)
+
+    assert call(g=None) == 1
+    assert call(k=None) == 1
+    assert call(hard=None) == 1
+    assert call(ldg=9) == 2
+    assert call(B=0) == 2
+    assert call(gdt=7) == 3
+    assert call(alpha=-0.1) == 4
+    assert call(delta=float("nan")) == 4
+    assert call(ws=None, wsb=1 << 30) == 5
+    assert L.sv_opd_grad_workspace_size(2, 10, 1) > L.sv_rkl_workspace_size(2, 10, 1)
+    assert L.sv_opd_grad_workspace_size(0, 10, 1) == 0
