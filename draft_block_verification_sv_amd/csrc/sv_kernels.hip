@@ -19,6 +19,15 @@
 
 #include "sv_device.h"
 
+#ifndef SV_GRAD_NT_LOAD
+#define SV_GRAD_NT_LOAD 1
+#endif
+#ifndef SV_GRAD_NT_STORE
+#define SV_GRAD_NT_STORE 0
+#endif
+#ifndef SV_GRAD_GROUPS
+#define SV_GRAD_GROUPS 1
+#endif
 #ifndef SV_MASS_WAVES_PER_EU
 #define SV_MASS_WAVES_PER_EU 5
 #endif
@@ -176,22 +185,46 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte loads and stores that bypass cache retention: every byte is touched once.
+__device__ __forceinline__ uint4 nt_load(const void* p) {
+#if SV_GRAD_NT_LOAD
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  uint4 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ void nt_store(void* p, const uint4& w) {
+#if SV_GRAD_NT_STORE
+  u32x4_t v;
+  __builtin_memcpy(&v, &w, 16);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+#else
+  *reinterpret_cast<uint4*>(p) = w;
+#endif
+}
+
 template <int DT>
 __device__ __forceinline__ void load8(const void* row, int64_t col, int V, bool vec, float (&x)[8]) {
   if constexpr (DT == 0) {
     const uint16_t* p = static_cast<const uint16_t*>(row) + col;
     if (vec && col + 8 <= V) {
-      unpack8(*reinterpret_cast<const uint4*>(p), x);
+      unpack8(nt_load(p), x);
     } else {
       for (int e = 0; e < 8; ++e) x[e] = (col + e < V) ? bf16_at(p + e) : 0.0f;
     }
   } else {
     const float* p = static_cast<const float*>(row) + col;
     if (vec && col + 8 <= V) {
-      const float4 a = *reinterpret_cast<const float4*>(p);
-      const float4 b = *reinterpret_cast<const float4*>(p + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      const uint4 a = nt_load(p), b = nt_load(p + 4);
+      x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+      x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+      x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+      x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     } else {
       for (int e = 0; e < 8; ++e) x[e] = (col + e < V) ? p[e] : 0.0f;
     }
@@ -217,10 +250,8 @@ __global__ __launch_bounds__(256) void sv_opd_grad_kernel(GradArgs a) {
   const void* prow = static_cast<const char*>(a.target) + (ok ? t : 0) * a.ld_t * es;
   const void* qrow = static_cast<const char*>(a.draft) + r * a.ld_d * es;
   char* grow = static_cast<char*>(a.grad) + r * a.ld_g * (GT == 0 ? 2 : 4);
-  for (int64_t col = static_cast<int64_t>(tid) * 8; col < V; col += 256 * 8) {
-    float lp[8], lq[8], g[8];
-    load8<DT>(prow, col, V, VEC, lp);
-    load8<DT>(qrow, col, V, VEC, lq);
+  auto grad8 = [&](int64_t col, const float (&lp)[8], const float (&lq)[8]) {
+    float g[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float q = fast_exp2(__builtin_fmaf(lq[e], kL2E, kq) - fq);
@@ -237,7 +268,7 @@ __global__ __launch_bounds__(256) void sv_opd_grad_kernel(GradArgs a) {
         w.y = bf16_rne(g[2]) | (static_cast<uint32_t>(bf16_rne(g[3])) << 16);
         w.z = bf16_rne(g[4]) | (static_cast<uint32_t>(bf16_rne(g[5])) << 16);
         w.w = bf16_rne(g[6]) | (static_cast<uint32_t>(bf16_rne(g[7])) << 16);
-        *reinterpret_cast<uint4*>(o) = w;
+        nt_store(o, w);
       } else {
         for (int e = 0; e < 8; ++e)
           if (col + e < V) o[e] = bf16_rne(g[e]);
@@ -245,13 +276,33 @@ __global__ __launch_bounds__(256) void sv_opd_grad_kernel(GradArgs a) {
     } else {
       float* o = reinterpret_cast<float*>(grow) + col;
       if (VEC && col + 8 <= V) {
-        *reinterpret_cast<float4*>(o) = make_float4(g[0], g[1], g[2], g[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(g[4], g[5], g[6], g[7]);
+        nt_store(o, make_uint4(__float_as_uint(g[0]), __float_as_uint(g[1]),
+                               __float_as_uint(g[2]), __float_as_uint(g[3])));
+        nt_store(o + 4, make_uint4(__float_as_uint(g[4]), __float_as_uint(g[5]),
+                                   __float_as_uint(g[6]), __float_as_uint(g[7])));
       } else {
         for (int e = 0; e < 8; ++e)
           if (col + e < V) o[e] = g[e];
       }
     }
+  };
+  // two groups of 8 columns per step, 2048 columns apart, with all four loads issued first
+  constexpr int64_t kStep = 256 * 8;
+  int64_t col = static_cast<int64_t>(tid) * 8;
+  for (; SV_GRAD_GROUPS == 2 && col + kStep < V; col += 2 * kStep) {
+    float lp0[8], lq0[8], lp1[8], lq1[8];
+    load8<DT>(prow, col, V, VEC, lp0);
+    load8<DT>(qrow, col, V, VEC, lq0);
+    load8<DT>(prow, col + kStep, V, VEC, lp1);
+    load8<DT>(qrow, col + kStep, V, VEC, lq1);
+    grad8(col, lp0, lq0);
+    grad8(col + kStep, lp1, lq1);
+  }
+  for (; col < V; col += kStep) {
+    float lp0[8], lq0[8];
+    load8<DT>(prow, col, V, VEC, lp0);
+    load8<DT>(qrow, col, V, VEC, lq0);
+    grad8(col, lp0, lq0);
   }
 }
 
