@@ -204,13 +204,77 @@ def bench_opd(args, w, grad=False):
     print(json.dumps(res), flush=True)
 
 
+def bench_greedy(args, w):
+    """Every request greedy (T_b = 0): sv_verify_block_greedy, target rows only."""
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+
+    pkg.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16 if w.dtype == "bf16" else None
+
+    def up(a, dt=None):
+        if dt is torch.bfloat16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    target = up(w.target, bf)
+    k, toks = up(w.k.astype(np.int32)), up(w.draft_tokens.astype(np.int32))
+    code = pkg.SV_BF16 if w.dtype == "bf16" else pkg.SV_F32
+    ws = pkg.alloc_workspace(pkg.workspace_size(w.B, w.k_max, w.V, code), dev)
+    n_d, B, V = w.n_draft_rows, w.B, w.V
+    out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "out_tokens": torch.empty(n_d + B, dtype=torch.int32, device=dev),
+           "device_status": torch.empty(1, dtype=torch.int32, device=dev)}
+
+    def step():
+        pkg.verify_block_greedy(target, k, toks, k_max=w.k_max, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(out["device_status"].item()) == 0
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
+    rows_bytes = (n_d + B) * V * (2 if w.dtype == "bf16" else 4)  # every target logit once
+    achieved = rows_bytes / (kernels["sv_greedy"] * 1e-6) / 1e9
+    res = {
+        "metric": "verified draft positions/sec, greedy verification (target rows only)",
+        "value": round(n_d / (ms_per_step * 1e-3), 1), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded logits shaped like the pages' workloads)",
+        "config": {"workload": w.name, "op": "greedy", "B": B, "k": int(w.k_max), "V": V,
+                   "input_dtype": w.dtype, "algorithmic_bytes_per_step": rows_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--op", choices=("verify", "opd", "opd_grad"), default="verify")
+    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad"), default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -246,6 +310,8 @@ def main():
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
     if args.op in ("opd", "opd_grad"):
         return bench_opd(args, w, grad=(args.op == "opd_grad"))
+    if args.op == "greedy":
+        return bench_greedy(args, w)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")

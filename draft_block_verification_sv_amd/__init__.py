@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     profile_read,
     profile_reset,
     verify_block,
+    verify_block_greedy,
     version,
     workspace_size,
 )

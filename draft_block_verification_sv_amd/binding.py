@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
                               _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                               _c_sz, _c_p]
     L.sv_opd_loss.restype = _c_i32
+    L.sv_verify_block_greedy.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_p,
+                                         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_verify_block_greedy.restype = _c_i32
     L.sv_opd_grad_workspace_size.argtypes = [_c_i64, _c_i64, _c_i32]
     L.sv_opd_grad_workspace_size.restype = _c_sz
     L.sv_opd_loss_grad.argtypes = [_c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
@@ -190,6 +193,49 @@ def verify_block(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
         _ptr(out.get("p_at_draft")), _ptr(out.get("q_at_draft")), _ptr(out["device_status"]),
         _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "sv_verify_block")
+    return out
+
+
+def verify_block_greedy(target: torch.Tensor, k: torch.Tensor, draft_tokens: torch.Tensor, *,
+                        k_max: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                        out: Optional[dict] = None, stream=None) -> dict:
+    """sv_verify_block_greedy: every request greedy; reads only the target logits
+    [n_draft_rows + B, V].  Returns accept_len, out_tokens and device_status."""
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    code = _dtype_code(target)
+    if target.dim() != 2 or target.stride(1) != 1:
+        raise ValueError("target must be 2-D with unit column stride")
+    B = int(k.numel())
+    n_d = int(draft_tokens.numel())
+    V = int(target.shape[1])
+    if int(target.shape[0]) != n_d + B:
+        raise ValueError(f"target {tuple(target.shape)} must have n_draft_rows + B rows")
+    if k_max is None:
+        k_max = max(1, min(SV_MAX_K, n_d - B + 1))
+    _need(k, "k", torch.int32, B, dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, n_d, dev)
+    if workspace is None:
+        nbytes = workspace_size(B, k_max, V, code)
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape B={B} k_max={k_max} V={V}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {
+            "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty(n_d + B, dtype=torch.int32, device=dev),
+            "device_status": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    else:
+        _need(out["accept_len"], "accept_len", torch.int32, B, dev)
+        _need(out["out_tokens"], "out_tokens", torch.int32, n_d + B, dev)
+        _need(out["device_status"], "device_status", torch.int32, 1, dev)
+    st = lib().sv_verify_block_greedy(code, B, k_max, V, target.stride(0), n_d, _ptr(target),
+                                      _ptr(k), _ptr(draft_tokens), _ptr(out["accept_len"]),
+                                      _ptr(out["out_tokens"]), _ptr(out["device_status"]),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sv_verify_block_greedy")
     return out
 
 

@@ -17,11 +17,12 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 12;
+constexpr int kNumKernels = 15;
 const char* const kKernelNames[kNumKernels] = {
-    "sv_plan",        "sv_rowpair",     "sv_sample_mass", "sv_sample",
-    "sv_rkl_rowpair", "sv_rkl_status",  "sv_opd_rowpair", "sv_opd_status",
-    "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad"};
+    "sv_plan",        "sv_rowpair",      "sv_sample_mass", "sv_sample",
+    "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
+    "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
+    "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -34,7 +35,10 @@ enum {
   K_OPD_REDUCE,
   K_GRAD_ROWPAIR,
   K_GRAD_REDUCE,
-  K_GRAD
+  K_GRAD,
+  K_GREEDY_PLAN,
+  K_GREEDY,
+  K_GREEDY_PICK
 };
 
 // ------------------------------------------------------------------ profiling
@@ -420,6 +424,91 @@ sv_status sv_opd_loss_grad(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_t
   const bool vec = vec_ok(dtype, ld_target, target_logits) &&
                    vec_ok(dtype, ld_draft, draft_logits) && vec_ok(grad_dtype, ld_grad, grad_out);
   if (timed(K_GRAD, st, [&] { return sv::launch_opd_grad(dtype, grad_dtype, vec, ga, st); }) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_t V,
+                                 int64_t ld_target, int64_t n_draft_rows,
+                                 const void* target_logits, const int32_t* k,
+                                 const int32_t* draft_tokens, int32_t* accept_len,
+                                 int32_t* out_tokens, int32_t* device_status, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || !shape_ok(V, ld_target, V))
+    return SV_ERR_SHAPE;
+  if (n_draft_rows < B || n_draft_rows > static_cast<int64_t>(B) * k_max) return SV_ERR_SHAPE;
+  const Dims dm = verify_dims(B, k_max, V);
+  if (!target_logits || !k || !draft_tokens || !accept_len || !out_tokens || !device_status)
+    return SV_ERR_NULL;
+  const size_t need = sv::carve(dm, nullptr, nullptr);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
+    return SV_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Workspace ws{};
+  sv::carve(dm, &ws, static_cast<char*>(workspace));
+  const int64_t n_d = n_draft_rows, n_t = n_draft_rows + B;
+  const bool vec = vec_ok(dtype, ld_target, target_logits);
+  const bool inline_plan = B <= sv::kInlinePlanMaxB;
+  if (!inline_plan) {
+    sv::PlanArgs pa{};
+    pa.B = B;
+    pa.k_max = k_max;
+    pa.n_d = n_d;
+    pa.k = k;
+    pa.ws = ws;
+    pa.device_status = device_status;
+    if (timed(K_GREEDY_PLAN, st, [&] { return sv::launch_plan(pa, st); }) != hipSuccess)
+      return SV_ERR_HIP;
+  }
+  sv::RowPairArgs ra{};
+  ra.target = target_logits;
+  ra.ld_t = ld_target;
+  ra.V = static_cast<int32_t>(V);
+  ra.n_slices = dm.n_slices;
+  ra.n_units = n_t;
+  ra.B = B;
+  ra.k_max = k_max;
+  ra.n_d = n_d;
+  ra.k = k;
+  ra.tokens = draft_tokens;
+  ra.desc = inline_plan ? nullptr : ws.desc;
+  ra.glob = ws.glob;
+  ra.off_t = ws.off_t;
+  ra.device_status = device_status;
+  ra.row_flags = ws.row_flags;
+  ra.t_arg = ws.t_arg;
+  ra.acc = ws.acc;
+  if (timed(K_GREEDY, st, [&] { return sv::launch_greedy(dtype, vec, ra, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+
+  sv::SampleArgs sa{};
+  sa.target = target_logits;
+  sa.ld_t = ld_target;
+  sa.V = static_cast<int32_t>(V);
+  sa.n_chunks = dm.n_chunks;
+  sa.B = B;
+  sa.n_t = n_t;
+  sa.glob = ws.glob;
+  sa.off_t = ws.off_t;
+  sa.k = k;
+  sa.tokens = draft_tokens;
+  sa.row_flags = ws.row_flags;
+  sa.t_off = ws.t_off;
+  sa.t_lz = ws.t_lz;
+  sa.t_beta = ws.t_beta;
+  sa.t_arg = ws.t_arg;
+  sa.d_off = ws.d_off;
+  sa.d_lz = ws.d_lz;
+  sa.acc = ws.acc;
+  sa.chunk_mass = ws.chunk_mass;
+  sa.force_greedy = true;
+  sa.accept_len = accept_len;
+  sa.out_tokens = out_tokens;
+  sa.device_status = device_status;
+  if (timed(K_GREEDY_PICK, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) !=
       hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

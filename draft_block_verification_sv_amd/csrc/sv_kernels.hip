@@ -392,7 +392,7 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
   r.k.beta = r.k.offp = r.k.lzp = r.k.offq = r.k.lzq = 0.f;
   r.targ = 0;
   r.void_call = a.glob[0];
-  r.T = a.temperature ? a.temperature[b] : 1.0f;
+  r.T = a.force_greedy ? 0.0f : (a.temperature ? a.temperature[b] : 1.0f);
   r.kb = a.k[b];
   r.off = a.off_t[b];
   const int64_t t = r.off + lane, d = r.off - b + lane;
@@ -407,7 +407,7 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
       offp = a.t_off[t];
       lzp = a.t_lz[t];
       targ = a.t_arg[t];
-      u = a.uniforms[t];
+      if (a.uniforms) u = a.uniforms[t];
     }
     if (lane < r.kb) {
       rej = !a.acc[d];
@@ -419,7 +419,7 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
   r.ufin = r.kb < 64 ? __shfl(u, r.kb < 0 ? 0 : r.kb, 64) : 0.f;
   if (r.kb >= 64 && !r.void_call) {  // k_b = 64: the 65th row
     if (lane == 0) f |= a.row_flags[r.off + 64];
-    r.ufin = a.uniforms[r.off + 64];
+    if (a.uniforms) r.ufin = a.uniforms[r.off + 64];
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) f |= __shfl_xor(f, m, 64);

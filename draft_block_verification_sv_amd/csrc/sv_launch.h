@@ -81,6 +81,7 @@ struct SampleArgs {
   const float* d_lz;
   const int32_t* acc;
   double* chunk_mass;   // [B * n_chunks], written by sv_sample_mass, read by sv_sample
+  bool force_greedy;    // every request greedy (sv_verify_block_greedy): T_b = 0
   int32_t mass_blocks;  // sv_sample_mass workgroups per request
   int32_t* accept_len;
   int32_t* out_tokens;
@@ -110,6 +111,7 @@ struct GradArgs {
 };
 hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& a, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
+hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
 hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 

@@ -709,54 +709,15 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   }
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_ROWS_WAVES_PER_EU)))
-void sv_rowpair_kernel(RowPairArgs a) {
-  __shared__ LaneAcc lacc[kRowThreads];
-  __shared__ double direct[kRowThreads];
-  __shared__ double direct_sg[kRowThreads];
-  __shared__ int failed[kRowThreads];
-  __shared__ int s_nfail;
-  __shared__ double red_d[kRowWaves];
-  __shared__ float red_f[kRowWaves];
-  __shared__ int red_i[kRowWaves];
-  __shared__ int s_req, s_off, s_t, s_void, s_x;
-  __shared__ float s_lpx, s_lqx;
-  const int tid = thread_index();
-  const int64_t unit = block_index();
-
-  RowCtx ctx;
-  if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
-    ctx.d = unit;
-    ctx.t = a.p_row_index ? a.p_row_index[unit] : unit;
-    ctx.b = -1;
-    ctx.mode = 0;
-    ctx.beta = kL2E;
-    ctx.row_flags = 0;
-    if (ctx.t < 0 || ctx.t >= a.n_target_rows) {
-      if (tid == 0) {
-        store_nan(a.rkl_out + unit);
-        if (a.hard_out) store_nan(a.hard_out + unit);
-        if (a.top1_out) a.top1_out[unit] = -1;
-        a.row_flags[unit] = 2;  // SV_DEV_ROWS_MISMATCH
-      }
-      return;
-    }
-    if (tid == 0) a.row_flags[unit] = 0;
-    if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
-      ctx.mode = 1;
-      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
-                                     0, 0.0f, 0.0f);
-    } else {
-      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
-                                     0, 0.0f, 0.0f);
-    }
-    return;
-  }
-
-  // ---- verification: units 0 .. n_d-1 are the draft rows (each with its target row),
-  // units n_d .. n_d+B-1 the bonus rows; the half-size bonus units run last and fill
-  // the tail of the grid.
+// Verification layout: which target row a workgroup owns.  Units 0 .. n_d-1 are the draft
+// rows (each with its target row), units n_d .. n_d+B-1 the bonus rows; the half-size bonus
+// units run last and fill the tail of the grid.  Large batches read the plan's descriptors;
+// otherwise every workgroup scans k itself (8 requests per thread), and unit 0 publishes the
+// call's validity.  Returns false when the workgroup has nothing more to do (a void call,
+// whose outputs it has written).
+__device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit, int tid,
+                                             int* red_i, int& s_req, int& s_off, int& s_t,
+                                             int& s_void) {
   if (a.desc) {  // large batch: descriptors and offsets from sv_plan
     if (a.glob[0]) {
       if (tid == 0 && unit < a.n_d) {
@@ -764,7 +725,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
         if (a.p_at) store_nan(a.p_at + unit);
         if (a.q_at) store_nan(a.q_at + unit);
       }
-      return;
+      return false;
     }
     if (tid == 0) {
       const RowDesc rd = a.desc[unit];
@@ -845,10 +806,58 @@ void sv_rowpair_kernel(RowPairArgs a) {
         if (a.p_at) store_nan(a.p_at + unit);
         if (a.q_at) store_nan(a.q_at + unit);
       }
-      return;
+      return false;
     }
   }
-  if (s_req < 0) return;  // unreachable when the layout is valid
+  return s_req >= 0;  // false only when the layout is invalid, which the scan reports
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_ROWS_WAVES_PER_EU)))
+void sv_rowpair_kernel(RowPairArgs a) {
+  __shared__ LaneAcc lacc[kRowThreads];
+  __shared__ double direct[kRowThreads];
+  __shared__ double direct_sg[kRowThreads];
+  __shared__ int failed[kRowThreads];
+  __shared__ int s_nfail;
+  __shared__ double red_d[kRowWaves];
+  __shared__ float red_f[kRowWaves];
+  __shared__ int red_i[kRowWaves];
+  __shared__ int s_req, s_off, s_t, s_void, s_x;
+  __shared__ float s_lpx, s_lqx;
+  const int tid = thread_index();
+  const int64_t unit = block_index();
+
+  RowCtx ctx;
+  if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
+    ctx.d = unit;
+    ctx.t = a.p_row_index ? a.p_row_index[unit] : unit;
+    ctx.b = -1;
+    ctx.mode = 0;
+    ctx.beta = kL2E;
+    ctx.row_flags = 0;
+    if (ctx.t < 0 || ctx.t >= a.n_target_rows) {
+      if (tid == 0) {
+        store_nan(a.rkl_out + unit);
+        if (a.hard_out) store_nan(a.hard_out + unit);
+        if (a.top1_out) a.top1_out[unit] = -1;
+        a.row_flags[unit] = 2;  // SV_DEV_ROWS_MISMATCH
+      }
+      return;
+    }
+    if (tid == 0) a.row_flags[unit] = 0;
+    if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
+      ctx.mode = 1;
+      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+                                     0, 0.0f, 0.0f);
+    } else {
+      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+                                     0, 0.0f, 0.0f);
+    }
+    return;
+  }
+
+  if (!resolve_unit(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
   const int64_t b = s_req;
   const int64_t off = s_off;
   const int kb = a.k[b];
@@ -899,6 +908,109 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
     if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   }
+}
+
+// ----------------------------------------------------------------------------- greedy
+// Greedy verification (every T_b = 0; the paper's default decoding, Appendix B.1): only the
+// target rows' first argmax is needed (DFlash notes, Section 5.2, worked example #4), so one
+// workgroup streams one target row and nothing else.  Per lane, the running maximum and the
+// slice where it first appeared; the lanes holding the row maximum then look again at that one
+// slice for the first column.  Writes t_arg, the acceptance flag x_i == argmax (draft-position
+// rows) and the row's token flag; the pick kernel then scans and emits.
+template <int DT, bool VEC>
+__device__ __forceinline__ void stream_max(const void* prow, int V, int n_slices, int wave,
+                                           int lane, float& best, int& best_s) {
+  const int n_full = V / kSlice;
+  int s = wave;
+  if constexpr (DT == 0 && VEC) {
+    const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
+    PackedRow ra, rb;
+    if (s < n_full) ra.load(P + static_cast<int64_t>(s) * kSlice);
+    while (s < n_full) {
+      const int s2 = s + kRowWaves;
+      if (s2 < n_full) rb.load(P + static_cast<int64_t>(s2) * kSlice);
+      float m = ra.max();
+      if (m > best) {
+        best = m;
+        best_s = s;
+      }
+      if (s2 >= n_full) {
+        s = s2;
+        break;
+      }
+      const int s3 = s2 + kRowWaves;
+      if (s3 < n_full) ra.load(P + static_cast<int64_t>(s3) * kSlice);
+      m = rb.max();
+      if (m > best) {
+        best = m;
+        best_s = s2;
+      }
+      s = s3;
+    }
+  }
+  for (; s < n_slices; s += kRowWaves) {
+    FloatRow f;
+    f.template load<DT, VEC>(prow, static_cast<int64_t>(s) * kSlice + lane * 8, V);
+    const float m = f.max();
+    if (m > best) {
+      best = m;
+      best_s = s;
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void sv_greedy_kernel(RowPairArgs a) {
+  __shared__ float red_f[kRowWaves];
+  __shared__ int red_i[kRowWaves];
+  __shared__ int s_req, s_off, s_t, s_void;
+  const int tid = thread_index(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t unit = block_index();
+  if (!resolve_unit(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
+  const int64_t b = s_req, off = s_off, t = s_t;
+  const int kb = a.k[b];
+  const int i = static_cast<int>(t - off);
+  const int64_t d = (i < kb) ? (off - b + i) : -1;
+  if (i == 0 && tid == 0 && !a.desc) a.off_t[b] = static_cast<int32_t>(off);
+  const void* prow = static_cast<const char*>(a.target) + t * a.ld_t * (DT == 0 ? 2 : 4);
+
+  float best = -INFINITY;
+  int best_s = -1;
+  stream_max<DT, VEC>(prow, a.V, static_cast<int>(a.n_slices), wave, lane, best, best_s);
+  const float Mx = block_max_f(best, red_f);
+  int col = 0x7fffffff;
+  if (best == Mx && best_s >= 0) {  // first column of the maximum inside that slice
+    FloatRow f;
+    f.template load<DT, VEC>(prow, static_cast<int64_t>(best_s) * kSlice + lane * 8, a.V);
+#pragma unroll
+    for (int e = kElemsPerLane - 1; e >= 0; --e)
+      if (f.at(e) == Mx) col = best_s * kSlice + (e >> 3) * 512 + lane * 8 + (e & 7);
+  }
+  const int argp = block_min_i(col, red_i);
+  if (tid == 0) {
+    a.t_arg[t] = argp;
+    int flags = 0;
+    if (d >= 0) {
+      const int32_t x = a.tokens[d];
+      if (x < 0 || x >= a.V) flags |= 4;  // SV_DEV_BAD_TOKEN
+      a.acc[d] = (flags == 0 && x == argp) ? 1 : 0;
+    }
+    a.row_flags[t] = flags;
+  }
+}
+
+hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.n_units));
+  if (a.n_units == 0) return hipSuccess;
+  if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_greedy_kernel<0, true>), grid, dim3(kRowThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_greedy_kernel<0, false>), grid, dim3(kRowThreads), 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((sv_greedy_kernel<1, true>), grid, dim3(kRowThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_greedy_kernel<1, false>), grid, dim3(kRowThreads), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------- launch

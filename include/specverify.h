@@ -136,6 +136,28 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
                           float* p_at_draft, float* q_at_draft, int32_t* device_status,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sv_verify_block_greedy: sv_verify_block for a batch whose every request decodes greedily
+ * (T_b = 0; the AdaFlash paper's default decoding, Appendix B.1).  A draft is accepted iff it
+ * equals the argmax of its target row, and the final token is the argmax of target row a_b
+ * (DFlash notes, Section 5.2, worked example #4); ties go to the lowest id.  Only the target
+ * rows are read, with no exponentials, so no draft logits, uniforms, temperatures or
+ * probability outputs appear.
+ *
+ *   dtype, B, k_max, V, ld_target, n_draft_rows, target_logits, k, draft_tokens   as
+ *                   sv_verify_block.
+ * Outputs: accept_len int32[B], out_tokens int32[n_draft_rows + B], device_status int32[1],
+ *   with sv_verify_block's meaning (SV_DEV_BAD_TOKEN for a token outside [0, V): that
+ *   request gets -1; bad lengths or a row-count mismatch void the call).
+ * Workspace: sv_workspace_size(B, k_max, V, dtype) bytes, 256-byte aligned.
+ */
+sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_t V,
+                                 int64_t ld_target, int64_t n_draft_rows,
+                                 const void* target_logits, const int32_t* k,
+                                 const int32_t* draft_tokens, int32_t* accept_len,
+                                 int32_t* out_tokens, int32_t* device_status, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace sv_clipped_rkl needs for n_rows row pairs; 0 if invalid. */
 size_t sv_rkl_workspace_size(int64_t n_rows, int64_t V, int32_t dtype);
 

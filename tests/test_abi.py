@@ -140,3 +140,20 @@ def test_opd_grad_argument_errors(L):
     assert call(ws=None, wsb=1 << 30) == 5
     assert L.sv_opd_grad_workspace_size(2, 10, 1) > L.sv_rkl_workspace_size(2, 10, 1)
     assert L.sv_opd_grad_workspace_size(0, 10, 1) == 0
+
+
+def test_greedy_argument_errors(L):
+    def call(dtype=1, B=1, kmax=2, V=10, ldt=10, nd=2, tp=8, k=8, tok=8, al=8, ot=8, st=8,
+             ws=None, wsb=0):
+        return L.sv_verify_block_greedy(dtype, B, kmax, V, ldt, nd, tp, k, tok, al, ot, st, ws,
+                                        wsb, None)
+
+    assert call(dtype=5) == 3
+    assert call(B=0) == 2
+    assert call(kmax=65) == 2
+    assert call(ldt=9) == 2
+    assert call(nd=3) == 2  # more draft rows than B * k_max
+    assert call(tp=None) == 1
+    assert call(tok=None) == 1
+    assert call(st=None) == 1
+    assert call(ws=None, wsb=1 << 30) == 5
