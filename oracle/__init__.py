@@ -12,7 +12,7 @@ Sources (cited by page title and section):
   Drafters" (arXiv 2607.19223) -- Section 2.1 (acceptance test, first-rejection
   truncation, residual resample, closed form of the expected output length),
   Section 3.1 (entry-wise clipped reverse-KL equation; the hard-label cross-entropy
-  and the mixture OPD loss), Section 3.2 (per-request
+  and the mixture OPD loss), Section 3.2 (the adaptive length head and its loss; per-request
   verification length), Section 3.3 (packed batch of total length sum k_i),
   Appendix B.1 (greedy decoding default, reverse-KL temperature 1).
 * "AdaFlash reading notes" (zhongzhuzhou.org blog) -- steps 3-4 of the basic
@@ -58,3 +58,11 @@ from .verify import (  # noqa: F401
 )
 from .rkl import clipped_rkl_row, clipped_rkl  # noqa: F401
 from .opd import hard_ce_row, opd_loss, clipped_rkl_grad_row, opd_grad  # noqa: F401
+from .length_head import (  # noqa: F401
+    length_head,
+    length_loss,
+    packed_offsets,
+    silu,
+    truncate,
+    truncation_margin,
+)
