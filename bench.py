@@ -268,13 +268,74 @@ def bench_greedy(args, w):
     print(json.dumps(res), flush=True)
 
 
+def bench_length_head(args):
+    """The adaptive length head at the drafter's shape: B=128 requests, k=15 positions,
+    H=4096, H'=256, seeded random bf16 weights and hidden states."""
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+
+    B, k, H, Hf = 128, 15, 4096, 256
+    pkg.lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(20261202)
+    h = torch.randn(B, k, H, generator=g).to(torch.bfloat16).to(dev)
+    W1 = (torch.randn(Hf, H, generator=g) / H ** 0.5).to(torch.bfloat16).to(dev)
+    b1 = (torch.randn(Hf, generator=g) * 0.5).to(dev)
+    w2 = (torch.randn(Hf, generator=g) * 3 / Hf ** 0.5).to(dev)
+    ws = pkg.alloc_workspace(int(pkg.lib().sv_length_head_workspace_size(B, Hf)), dev)
+    out = {"a_hat": torch.empty(B, device=dev), "k_hat": torch.empty(B, dtype=torch.int32, device=dev),
+           "off_t": torch.empty(B + 1, dtype=torch.int32, device=dev)}
+
+    def step():
+        pkg.length_head(h, W1, w2, b1, b2=0.1, gamma=1.0, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
+    nbytes = (B * k * H + Hf * H) * 2  # hidden states and W1 once
+    flops = 2.0 * B * k * H * Hf
+    us = kernels["sv_head_feat"]
+    res = {
+        "metric": "length-head requests/sec (projection on MFMA, SiLU, pooling, k_hat, offsets)",
+        "value": round(B / (ms_per_step * 1e-3), 1), "unit": "requests/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random hidden states and head weights)",
+        "config": {"workload": "length head: B=128 k=15 H=4096 H'=256 bf16", "op": "length_head",
+                   "B": B, "k": k, "H": H, "H_feat": Hf, "bytes": nbytes, "flops": flops},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad"), default="verify")
+    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad", "length_head"),
+                    default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -305,6 +366,8 @@ def main():
     import draft_block_verification_sv_amd as pkg
     from synth import workload
 
+    if args.op == "length_head":
+        return bench_length_head(args)
     t0 = time.perf_counter()
     w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     alloc_workspace,
     clipped_rkl,
     lib,
+    length_head,
+    length_loss,
     library_path,
     opd_loss,
     opd_loss_grad,

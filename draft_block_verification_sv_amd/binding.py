@@ -58,6 +58,13 @@ def lib() -> ctypes.CDLL:
                               _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                               _c_sz, _c_p]
     L.sv_opd_loss.restype = _c_i32
+    L.sv_length_head_workspace_size.argtypes = [_c_i32, _c_i32]
+    L.sv_length_head_workspace_size.restype = _c_sz
+    L.sv_length_head.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64, _c_p,
+                                 _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_length_head.restype = _c_i32
+    L.sv_length_loss.argtypes = [_c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
+    L.sv_length_loss.restype = _c_i32
     L.sv_verify_block_greedy.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_p,
                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_verify_block_greedy.restype = _c_i32
@@ -237,6 +244,62 @@ def verify_block_greedy(target: torch.Tensor, k: torch.Tensor, draft_tokens: tor
                                       _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "sv_verify_block_greedy")
     return out
+
+
+def length_head(h: torch.Tensor, W1: torch.Tensor, w2: torch.Tensor, b1=None, b2: float = 0.0,
+                gamma: float = 1.0, *, workspace: Optional[torch.Tensor] = None,
+                out: Optional[dict] = None, stream=None) -> dict:
+    """sv_length_head: h bfloat16 [B, k, H] (unit stride along H), W1 bfloat16 [H', H], w2 and
+    b1 float32 [H'].  Returns a_hat [B], k_hat [B] and the packed target-row offsets off_t."""
+    dev = h.device
+    if h.dtype != torch.bfloat16 or W1.dtype != torch.bfloat16:
+        raise TypeError("h and W1 must be bfloat16")
+    if h.dim() != 3 or W1.dim() != 2 or h.stride(2) != 1 or W1.stride(1) != 1:
+        raise ValueError("h must be [B, k, H] and W1 [H', H], both with unit stride along H")
+    B, k, H = (int(x) for x in h.shape)
+    Hf = int(W1.shape[0])
+    if int(W1.shape[1]) != H:
+        raise ValueError("W1 must have H columns")
+    if h.stride(0) != k * h.stride(1):
+        raise ValueError("h's positions must be packed request by request (stride(0) = k stride(1))")
+    _need(w2, "w2", torch.float32, Hf, dev)
+    if b1 is not None:
+        _need(b1, "b1", torch.float32, Hf, dev)
+    if workspace is None:
+        nbytes = int(lib().sv_length_head_workspace_size(B, Hf))
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape B={B} H'={Hf}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {"a_hat": torch.empty(B, dtype=torch.float32, device=dev),
+               "k_hat": torch.empty(B, dtype=torch.int32, device=dev),
+               "off_t": torch.empty(B + 1, dtype=torch.int32, device=dev)}
+    else:
+        _need(out["a_hat"], "a_hat", torch.float32, B, dev)
+        _need(out["k_hat"], "k_hat", torch.int32, B, dev)
+        if out.get("off_t") is not None:
+            _need(out["off_t"], "off_t", torch.int32, B + 1, dev)
+    st = lib().sv_length_head(B, k, H, Hf, _ptr(h), h.stride(1), _ptr(W1), W1.stride(0), _ptr(b1),
+                              _ptr(w2), float(b2), float(gamma), _ptr(out["a_hat"]),
+                              _ptr(out["k_hat"]), _ptr(out.get("off_t")), _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    _check(st, "sv_length_head")
+    return out
+
+
+def length_loss(a_hat: torch.Tensor, accept_len: torch.Tensor, k_hat: torch.Tensor,
+                stream=None) -> tuple:
+    """sv_length_loss: (loss [B], dloss/da_hat [B])."""
+    dev = a_hat.device
+    B = int(a_hat.numel())
+    _need(a_hat, "a_hat", torch.float32, B, dev)
+    _need(accept_len, "accept_len", torch.int32, B, dev)
+    _need(k_hat, "k_hat", torch.int32, B, dev)
+    loss = torch.empty(B, dtype=torch.float32, device=dev)
+    dloss = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(lib().sv_length_loss(B, _ptr(a_hat), _ptr(accept_len), _ptr(k_hat), _ptr(loss),
+                                _ptr(dloss), _stream(stream)), "sv_length_loss")
+    return loss, dloss
 
 
 def _row_pair_shapes(target: torch.Tensor, draft: torch.Tensor,

@@ -110,6 +110,28 @@ struct GradArgs {
   void* grad;         // [n_rows, ld_g] of the gradient dtype
 };
 hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& a, hipStream_t st);
+
+// The adaptive length head.
+struct HeadArgs {
+  int64_t B;
+  int32_t k;       // positions per request
+  int32_t H, Hf;   // hidden size (multiple of 32), features
+  const void* h;   // bf16 [B * k, ld_h]
+  int64_t ld_h;
+  const void* W1;  // bf16 [Hf, ld_w]
+  int64_t ld_w;
+  const float* b1;  // [Hf] or null
+  const float* w2;  // [Hf]
+  float b2, gamma;
+  float* pooled;    // workspace [B * Hf]
+  float* a_hat;     // [B]
+  int32_t* k_hat;   // [B]
+  int32_t* off_t;   // [B + 1] or null
+};
+hipError_t launch_head(const HeadArgs& a, hipStream_t st);
+hipError_t launch_head_out(const HeadArgs& a, hipStream_t st);
+hipError_t launch_len_loss(int64_t B, const float* a_hat, const int32_t* accept_len,
+                           const int32_t* k_hat, float* loss, float* dloss, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
 hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
 hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);

@@ -88,6 +88,7 @@ enum {
 #define SV_MAX_K 64          /* k_max <= 64                                  */
 #define SV_MAX_BATCH 65536   /* B <= 65536                                   */
 #define SV_MAX_VOCAB (1 << 19) /* 524288 */
+#define SV_MAX_HEAD_FEATURES 4096 /* H' of the length head */
 
 /* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
  * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */
@@ -241,6 +242,40 @@ sv_status sv_opd_loss_grad(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_t
                            int32_t grad_dtype, int64_t ld_grad, void* grad_out,
                            int32_t* device_status, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Bytes of workspace sv_length_head needs; 0 if invalid. */
+size_t sv_length_head_workspace_size(int32_t B, int32_t H_feat);
+
+/*
+ * sv_length_head: the adaptive length head of the AdaFlash paper, Section 3.2, and the packed
+ * layout of the verification batch it implies (Section 3.3):
+ *     a_hat_b = sigmoid(w2 . (1/k) sum_i SiLU(W1 h_{b,i} + b1) + b2)
+ *     k_hat_b = clamp(floor(a_hat_b gamma k), 1, k)          (gamma scales a_hat before the floor)
+ *     off_t[b] = sum_{c<b} (k_hat_c + 1), off_t[B] = sum_b (k_hat_b + 1)
+ * The projection runs on the matrix cores in bf16 with fp32 accumulation.
+ *
+ *   B, k            requests; positions of each request's draft block (1..SV_MAX_K).
+ *   H, H_feat       hidden size (a multiple of 32), features H' (1..SV_MAX_HEAD_FEATURES).
+ *   h               bf16 [B * k, ld_h]: request b's positions are rows b k .. b k + k - 1.
+ *   W1              bf16 [H_feat, ld_w] (row n projects onto feature n); b1 float[H_feat] or
+ *                   NULL (no bias); w2 float[H_feat]; b2, gamma (> 0) scalars.
+ *   ld_h, ld_w      row strides in elements, >= H and multiples of 8; h and W1 16-byte aligned.
+ * Outputs (device): a_hat float[B], k_hat int32[B], off_t int32[B + 1] (or NULL).
+ * Workspace: sv_length_head_workspace_size(B, H_feat) bytes, 256-byte aligned.
+ */
+sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const void* h,
+                         int64_t ld_h, const void* W1, int64_t ld_w, const float* b1,
+                         const float* w2, float b2, float gamma, float* a_hat, int32_t* k_hat,
+                         int32_t* off_t, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sv_length_loss: the length head's online loss (AdaFlash paper, Section 3.2, "Online Update"):
+ * l_b = (a_hat_b - a*_b)^2 with a*_b = accept_len_b / k_hat_b, the fraction of the verified
+ * drafts that were accepted, and dloss_b = 2 (a_hat_b - a*_b) (or NULL).  A request whose
+ * accept_len is -1 (invalid) or outside [0, k_hat_b] gets NaN.  All pointers are device [B].
+ */
+sv_status sv_length_loss(int32_t B, const float* a_hat, const int32_t* accept_len,
+                         const int32_t* k_hat, float* loss, float* dloss, void* stream);
 
 /* Static text for a status code. */
 const char* sv_status_string(sv_status s);

@@ -157,3 +157,24 @@ def test_greedy_argument_errors(L):
     assert call(tok=None) == 1
     assert call(st=None) == 1
     assert call(ws=None, wsb=1 << 30) == 5
+
+
+def test_length_head_argument_errors(L):
+    def call(B=2, k=4, H=64, Hf=16, h=16, ldh=64, W1=16, ldw=64, b1=None, w2=16, b2=0.0,
+             gamma=1.0, ah=16, kh=16, off=None, ws=None, wsb=0):
+        return L.sv_length_head(B, k, H, Hf, h, ldh, W1, ldw, b1, w2, b2, gamma, ah, kh, off, ws,
+                                wsb, None)
+
+    assert call(H=48) == 2  # not a multiple of 32
+    assert call(k=65) == 2
+    assert call(Hf=0) == 2
+    assert call(ldh=60) == 2
+    assert call(ldw=68 + 2) == 2  # not a multiple of 8
+    assert call(h=None) == 1
+    assert call(w2=None) == 1
+    assert call(h=8) == 2  # not 16-byte aligned
+    assert call(gamma=0.0) == 4
+    assert call(ws=None, wsb=1 << 30) == 5
+    assert L.sv_length_head_workspace_size(4, 256) >= 4 * 256 * 4
+    assert L.sv_length_loss(0, 8, 8, 8, 8, None, None) == 2
+    assert L.sv_length_loss(2, None, 8, 8, 8, None, None) == 1
