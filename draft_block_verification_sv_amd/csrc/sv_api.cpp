@@ -17,9 +17,9 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 18;
+constexpr int kNumKernels = 17;
 const char* const kKernelNames[kNumKernels] = {
-    "sv_plan",        "sv_rowpair",      "sv_sample_mass", "sv_sample",
+    "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
@@ -27,8 +27,7 @@ const char* const kKernelNames[kNumKernels] = {
 enum {
   K_PLAN,
   K_ROWPAIR,
-  K_SAMPLE_MASS,
-  K_SAMPLE,
+  K_DRAW,
   K_RKL_ROWPAIR,
   K_RKL_STATUS,
   K_OPD_ROWPAIR,
@@ -316,6 +315,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.d_off = ws.d_off;
   ra.d_lz = ws.d_lz;
   ra.acc = ws.acc;
+  ra.arrive = ws.arrive;
   if (timed(K_ROWPAIR, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
     return SV_ERR_HIP;
 
@@ -343,16 +343,14 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.d_lz = ws.d_lz;
   sa.acc = ws.acc;
   sa.chunk_mass = ws.chunk_mass;
+  sa.arrive = ws.arrive;
   sa.mass_blocks = static_cast<int32_t>(sv::mass_blocks_for(n_chunks));
   sa.accept_len = accept_len;
   sa.out_tokens = out_tokens;
   sa.p_at = p_at_draft;
   sa.q_at = q_at_draft;
   sa.device_status = device_status;
-  if (timed(K_SAMPLE_MASS, st, [&] { return sv::launch_sample_mass(dtype, vec, sa, st); }) !=
-      hipSuccess)
-    return SV_ERR_HIP;
-  if (timed(K_SAMPLE, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) != hipSuccess)
+  if (timed(K_DRAW, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }
@@ -508,11 +506,13 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
   sa.d_lz = ws.d_lz;
   sa.acc = ws.acc;
   sa.chunk_mass = ws.chunk_mass;
+  sa.arrive = ws.arrive;
   sa.force_greedy = true;
+  sa.mass_blocks = 1;  // greedy: one workgroup per request emits, no masses are drawn
   sa.accept_len = accept_len;
   sa.out_tokens = out_tokens;
   sa.device_status = device_status;
-  if (timed(K_GREEDY_PICK, st, [&] { return sv::launch_sample(dtype, vec, sa, st); }) !=
+  if (timed(K_GREEDY_PICK, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) !=
       hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

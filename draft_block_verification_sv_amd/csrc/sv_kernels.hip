@@ -5,14 +5,13 @@
 //                      packed-layout offsets from k (AdaFlash paper, Section 3.3: one
 //                      batch of total length sum k_b) and the request of every row.
 //   sv_rowpair         the streaming pass fused with each row's finalize (sv_rowpair.hip).
-//   sv_sample_mass     the draw masses, per kChunk-column chunk, of each request's draw
+//   sv_draw            the draw masses, per kChunk-column chunk, of each request's draw
 //                      row: the residual max(0, p_T - q_T) at the first rejected position
 //                      (reading notes, basic recipe step 4) or p_T of the bonus row (DFlash
 //                      notes, Section 3.1 step 6); a request's row is spread over several
-//                      workgroups so the whole chip takes part.
-//   sv_sample          one 1024-thread workgroup per request: the scan of its chunk masses,
-//                      the inverse CDF at u * Z, the emitted tokens; folds the request's
-//                      input checks into device_status.
+//                      workgroups so the whole chip takes part, and the last of them to
+//                      finish scans the masses, takes the inverse CDF at u * Z and emits
+//                      the tokens; it folds the request's input checks into device_status.
 // sv_clipped_rkl runs sv_rowpair alone and then sv_status.
 #include <float.h>
 #include <math.h>
@@ -77,7 +76,10 @@ __global__ __launch_bounds__(1024) void sv_plan_kernel(PlanArgs a) {
     }
     int total = 0;
     const int excl = block_excl_scan_1024(b < a.B ? kb + 1 : 0, s_waves, &total);
-    if (b < a.B) ws.off_t[b] = carry + excl;
+    if (b < a.B) {
+      ws.off_t[b] = carry + excl;
+      ws.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
+    }
     carry += total;
   }
   __syncthreads();
@@ -322,6 +324,9 @@ __global__ __launch_bounds__(256) void sv_status_kernel(const int32_t* row_flags
 
 // =========================================================================== sample
 constexpr int kReqInvalid = 4 | 8 | 16;  // SV_DEV_BAD_TOKEN | BAD_TEMPERATURE | BAD_UNIFORM
+// s_waitcnt operand that waits for every outstanding vector memory operation of the wave
+// (vmcnt = 0) and leaves the export and LDS/scalar counters at their maxima (gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Draw masses of the lane's 8 columns starting at col: the residual max(0, p_T - q_T) of
 // a row pair (need_q), else p_T.  p_T(y) = 2^(fma(l_p(y), beta, offp) - lzp): the
@@ -445,29 +450,20 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
 }
 
 
-// Fixed-order inclusive scan over a kSampleThreads-thread block in fp64: Hillis-Steele
-// inside each wave, then the wave totals in order.  `lds` holds kSampleWaves doubles.
-__device__ __forceinline__ double block_inclusive_scan(double v, double* lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int dd = 1; dd < 64; dd <<= 1) {
-    const double o = __shfl_up(v, dd, 64);
-    if (lane >= dd) v += o;
-  }
-  if (lane == 63) lds[wave] = v;
-  __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < wave; ++w) base += lds[w];
-  __syncthreads();
-  return base + v;
-}
-
 // Draw masses of chunks [c_begin, c_end) of one row into out[c]; wave w of WAVES takes
 // chunks c_begin + w, + WAVES, ...  Each lane sums its kChunkGroups groups of 8 columns
 // (groups 512 columns apart) in fp32; the lane sums are combined in fp64.  For aligned
 // bf16 rows the loads of BATCH chunks are issued before any arithmetic.
-template <int DT, bool VEC, int WAVES, int BATCH, bool NEED_Q>
+// DEVICE_OUT: out is global memory read by another workgroup of the same launch; each mass
+// is then written with a device-scope store (written through to the device's coherence
+// point, past this XCD's L2), see sv_draw.
+template <bool DEVICE_OUT>
+__device__ __forceinline__ void put_mass(double* out, int c, double v) {
+  if constexpr (DEVICE_OUT) __hip_atomic_store(out + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else out[c] = v;
+}
+
+template <int DT, bool VEC, int WAVES, int BATCH, bool NEED_Q, bool DEVICE_OUT>
 __device__ __forceinline__ void chunk_masses_t(const SampleArgs& a, int64_t t, int64_t d,
                                                const RowScale& k, int c_begin, int c_end,
                                                int wave, int lane, double* out) {
@@ -499,7 +495,7 @@ __device__ __forceinline__ void chunk_masses_t(const SampleArgs& a, int64_t t, i
           for (int e = 0; e < 8; ++e) acc += draw_mass(lp[e], NEED_Q ? lq[e] : 0.0f, NEED_Q, k);
         }
         const double cs = wave_sum_d(static_cast<double>(acc));
-        if (lane == 0) out[c0 + h * WAVES] = cs;
+        if (lane == 0) put_mass<DEVICE_OUT>(out, c0 + h * WAVES, cs);
       }
     }
   }
@@ -512,175 +508,196 @@ __device__ __forceinline__ void chunk_masses_t(const SampleArgs& a, int64_t t, i
       for (int e = 0; e < 8; ++e) acc += r[e];
     }
     const double cs = wave_sum_d(static_cast<double>(acc));
-    if (lane == 0) out[c] = cs;
+    if (lane == 0) put_mass<DEVICE_OUT>(out, c, cs);
   }
 }
 
-template <int DT, bool VEC, int WAVES, int BATCH>
+template <int DT, bool VEC, int WAVES, int BATCH, bool DEVICE_OUT>
 __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int64_t d, bool need_q,
                                              const RowScale& k, int c_begin, int c_end, int wave,
                                              int lane, double* out) {
-  if (need_q) chunk_masses_t<DT, VEC, WAVES, BATCH, true>(a, t, d, k, c_begin, c_end, wave, lane, out);
-  else chunk_masses_t<DT, VEC, WAVES, BATCH, false>(a, t, d, k, c_begin, c_end, wave, lane, out);
+  if (need_q)
+    chunk_masses_t<DT, VEC, WAVES, BATCH, true, DEVICE_OUT>(a, t, d, k, c_begin, c_end, wave, lane, out);
+  else
+    chunk_masses_t<DT, VEC, WAVES, BATCH, false, DEVICE_OUT>(a, t, d, k, c_begin, c_end, wave, lane, out);
 }
 
-// sv_sample_mass: workgroup g of request b computes the draw masses of chunks
+// sv_draw: workgroup g of request b computes the draw masses of chunks
 // [g * kMassChunksPerBlock, (g + 1) * kMassChunksPerBlock) of the request's draw row into
-// chunk_mass[b * n_chunks + c].  Each wave derives the request state itself (a few cached
-// loads), so the workgroup has no barrier.  Void calls, invalid and greedy requests write
-// nothing: sv_sample does not read their masses.  Register use is capped so that all the
-// workgroups of a B = 128 call are resident at once.
+// chunk_mass[b * n_chunks + c]; the last of the request's workgroups to finish (a ticket
+// from its arrival counter, after a device-wide fence) then draws the token from them:
+//   1. the chunk where the prefix of the masses first exceeds u * Z (u the request's last
+//      uniform, Z the total): one wave, lane l owning a run of consecutive chunks, fp64
+//      sums in chunk order and a fixed-order scan across the lanes;
+//   2. the column inside that chunk: one wave, 32 consecutive columns per lane, the fp64
+//      prefix again in column order; the row is read once more only there;
+//   3. emit: a_b accepted drafts, the final token, -1 after.
+// A residual whose masses sum to zero (rounding only) is redrawn from p_T of the same row,
+// whose chunk masses the picking workgroup then computes itself.  Greedy requests (and
+// every request of sv_verify_block_greedy) emit the target's argmax from workgroup 0; void
+// calls and invalid requests are written by workgroup 0, with their input-check bits.
+// Each wave derives the request state itself (a few cached loads), so only the pick needs
+// the workgroup's barrier.  Register use is capped so that all the workgroups of a B = 128
+// call are resident at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(SV_MASS_WAVES_PER_EU)))
-void sv_sample_mass_kernel(SampleArgs a) {
+void sv_draw_kernel(SampleArgs a) {
+  __shared__ double s_pm[kMaxChunks];  // p_T chunk masses of a zero-mass residual row
+  __shared__ int s_last;
   const int64_t b = blockIdx.x / a.mass_blocks;
   const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int tok;
-  const ReqState rq = wave_request_state(a, b, &tok);
-  if (rq.void_call || rq.T == 0.0f || (rq.flags & kReqInvalid)) return;
-  const int nc = static_cast<int>(a.n_chunks);
-  const int c_begin = g * kMassChunksPerBlock;
-  const int c_end = min(nc, c_begin + kMassChunksPerBlock);
-  chunk_masses<DT, VEC, kMassWaves, 1>(a, rq.off + rq.alen, rq.off - b + rq.alen, rq.alen < rq.kb,
-                                    rq.k, c_begin, c_end, wave, lane,
-                                    a.chunk_mass + b * a.n_chunks);
-}
-
-// sv_sample, one 1024-thread workgroup per request:
-//   1. the first-rejection scan over the request's acceptance flags (one wave, ballot);
-//   2. the chunk masses sv_sample_mass wrote, one chunk per thread; when they sum to
-//      zero (a residual emptied by rounding) the p_T masses of the same row are
-//      computed here instead, wave w taking chunks w, w + 16, ...;
-//   3. a fixed-order scan of the chunk masses; the chunk where the prefix first exceeds
-//      u * Z (u = the request's last uniform), then the column inside it (one wave,
-//      32 consecutive columns per lane, so the prefix runs in column order);
-//   4. emit: a_b accepted drafts, the final token, -1 after; device_status bits.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a) {
-  const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __shared__ double s_cr[kMaxChunks];
-  __shared__ double s_incl[kSampleThreads];
-  __shared__ double s_scan[kSampleWaves];
-  __shared__ ReqState s_req;
-  __shared__ int s_sel, s_last, s_fallback;
-  __shared__ double s_Z, s_thr_c;
+  int my_tok;  // lane i holds draft token i of the request
+  const ReqState rq = wave_request_state(a, b, &my_tok);
 
-  // this request's chunk masses, fetched before its state is known (stale for requests
-  // that turn out greedy or invalid, which never read them)
-  const int nc = static_cast<int>(a.n_chunks);
-  double v = (tid < nc) ? a.chunk_mass[b * a.n_chunks + tid] : 0.0;
-  int my_tok = -1;  // wave 0: lane i holds draft token i of the request
-  if (tid < 64) {
-    const ReqState r = wave_request_state(a, b, &my_tok);
-    if (tid == 0) s_req = r;
-  }
-  __syncthreads();
-  const ReqState rq = s_req;
-  if (rq.void_call) {  // void call
-    if (tid == 0) a.accept_len[b] = -1;
-    for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
-         t += static_cast<int64_t>(kSampleThreads) * a.B)
-      a.out_tokens[t] = -1;
+  if (rq.void_call) {  // void call: the layout is unknown, so -1 everywhere, strided by B
+    if (g == 0) {
+      if (tid == 0) a.accept_len[b] = -1;
+      for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
+           t += static_cast<int64_t>(kMassThreads) * a.B)
+        a.out_tokens[t] = -1;
+    }
     return;
   }
   const int kb = rq.kb;
   const int64_t off = rq.off;
   if (rq.flags & kReqInvalid) {
-    if (tid == 0) {
-      a.accept_len[b] = -1;
-      atomicOr(a.device_status, rq.flags & kReqInvalid);
-    }
-    for (int j = tid; j <= kb; j += kSampleThreads) a.out_tokens[off + j] = -1;
-    for (int j = tid; j < kb; j += kSampleThreads) {
-      if (a.p_at) a.p_at[off - b + j] = NAN;
-      if (a.q_at) a.q_at[off - b + j] = NAN;
+    if (g == 0) {
+      if (tid == 0) {
+        a.accept_len[b] = -1;
+        atomicOr(a.device_status, rq.flags & kReqInvalid);
+      }
+      for (int j = tid; j <= kb; j += kMassThreads) a.out_tokens[off + j] = -1;
+      for (int j = tid; j < kb; j += kMassThreads) {
+        if (a.p_at) a.p_at[off - b + j] = NAN;
+        if (a.q_at) a.q_at[off - b + j] = NAN;
+      }
     }
     return;
   }
   const int alen = rq.alen;
-  const int64_t t = off + alen;
-  const bool pair = alen < kb;
-  const int64_t d = off - b + alen;
-
   // wave 0 writes the outputs: a_b drafts (held in its lanes), the final token, then -1
   auto emit = [&](int tok) {
     if (lane == 0) a.accept_len[b] = alen;
     for (int j = lane; j <= kb; j += 64)
       a.out_tokens[off + j] = (j < alen) ? my_tok : (j == alen ? tok : -1);
   };
-
   if (rq.T == 0.0f) {  // greedy: the target argmax at the first mismatch (or the bonus row)
-    if (tid < 64) emit(rq.targ);
+    if (g == 0 && wave == 0) emit(rq.targ);
     return;
   }
-  const RowScale k = rq.k;
 
-  // ---- 3a. chunk level: fixed-order scan, one chunk per thread
+  const int64_t t = off + alen;
+  const bool pair = alen < kb;
+  const int64_t d = off - b + alen;
+  const int nc = static_cast<int>(a.n_chunks);
+  double* cm = a.chunk_mass + b * a.n_chunks;
+  {
+    const int c_begin = g * kMassChunksPerBlock;
+    const int c_end = min(nc, c_begin + kMassChunksPerBlock);
+    chunk_masses<DT, VEC, kMassWaves, 2, true>(a, t, d, pair, rq.k, c_begin, c_end, wave, lane, cm);
+  }
+  // Hand-off to the picking workgroup without cache-wide maintenance: the masses went out
+  // as device-scope stores (written through to the coherence point shared by every XCD);
+  // each wave waits until its stores are complete, the barrier joins the waves, and only
+  // then does thread 0 take a ticket with a device-scope atomic.  The workgroup holding the
+  // last ticket reads the masses back with device-scope loads, which bypass its L2.
+  // (An agent-scope fence here would write back and invalidate the XCD's whole L2 per wave.)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(a.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              a.mass_blocks - 1) ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- 1. chunk level (every wave computes the same total, so they agree on the fallback)
+  const int cpl = (nc + 63) / 64;  // chunks per lane
+  const int c_lo = min(nc, lane * cpl), c_hi = min(nc, c_lo + cpl);
+  auto mass_at = [&](int c, bool from_lds) -> double {
+    return from_lds ? s_pm[c] : __hip_atomic_load(cm + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   bool usep = false;
-  double incl = block_inclusive_scan(v, s_scan);
-  if (tid == kSampleThreads - 1) s_Z = incl;
-  __syncthreads();
-  if (!(s_Z > 0.0)) {  // zero residual mass (rounding only): draw from p_T of the same row
-    usep = true;
-    chunk_masses<DT, VEC, kSampleWaves, 2>(a, t, d, false, k, 0, nc, wave, lane, s_cr);
-    __syncthreads();
-    v = (tid < nc) ? s_cr[tid] : 0.0;
-    incl = block_inclusive_scan(v, s_scan);
-    __syncthreads();
-    if (tid == kSampleThreads - 1) s_Z = incl;
-    __syncthreads();
-  }
-  const double thr = static_cast<double>(rq.ufin) * s_Z;
-  s_incl[tid] = incl;
-  if (tid == 0) {
-    s_sel = 0x7fffffff;
-    s_last = -1;
-  }
-  __syncthreads();
-  const double excl = tid ? s_incl[tid - 1] : 0.0;  // the neighbours' intervals tile exactly
-  if (tid < nc && v > 0.0 && excl <= thr && incl > thr) atomicMin(&s_sel, tid);
-  if (tid < nc && v > 0.0) atomicMax(&s_last, tid);
-  __syncthreads();
-  if (tid == 0) {
-    s_fallback = (s_sel == 0x7fffffff) ? 1 : 0;
-    if (s_fallback) s_sel = s_last < 0 ? 0 : s_last;  // rounding: last chunk with mass
-    s_thr_c = thr - (s_sel > 0 ? s_incl[s_sel - 1] : 0.0);
-  }
-  __syncthreads();
-  if (tid >= 64) return;  // one wave scans the chosen chunk
-
-  // ---- 3b. column level: lane l owns columns cstar * kChunk + 32 l .. + 32 (cache-hot)
-  const int64_t cstar = s_sel;
-  const bool fallback = s_fallback != 0;
-  const double thr_c = s_thr_c;
-  const int64_t colL = cstar * kChunk + lane * kChunkGroups * 8;
-  float m[kChunkGroups * 8];
   double lsum = 0.0;
-#pragma unroll
-  for (int g = 0; g < kChunkGroups; ++g) {
-    float r[8];
-    column_masses<DT, VEC>(a, t, d, pair && !usep, k, colL + g * 8, r);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      m[g * 8 + e] = r[e];
-      lsum += static_cast<double>(r[e]);
-    }
+  for (int c = c_lo; c < c_hi; ++c) lsum += mass_at(c, false);
+  double Z = wave_sum_d(lsum);
+  if (!(Z > 0.0)) {  // zero residual mass (rounding only): draw from p_T of the same row
+    usep = true;
+    chunk_masses<DT, VEC, kMassWaves, 2, false>(a, t, d, false, rq.k, 0, nc, wave, lane, s_pm);
+    __syncthreads();
+    lsum = 0.0;
+    for (int c = c_lo; c < c_hi; ++c) lsum += mass_at(c, true);
+    Z = wave_sum_d(lsum);
   }
-  double lincl = lsum;
+  if (wave != 0) return;  // one wave draws
+  double incl = lsum;  // fixed-order inclusive scan of the lane sums
 #pragma unroll
   for (int dd = 1; dd < 64; dd <<= 1) {
-    const double o = __shfl_up(lincl, dd, 64);
-    if (lane >= dd) lincl += o;
+    const double o = __shfl_up(incl, dd, 64);
+    if (lane >= dd) incl += o;
   }
-  double lexcl = __shfl_up(lincl, 1, 64);
-  if (lane == 0) lexcl = 0.0;
+  double excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.0;
+  const double thr = static_cast<double>(rq.ufin) * Z;
+  // chunk c of the lane spans [s_c, s_{c+1}), s_{c_lo} = excl, s_{c+1} = s_c + m_c, and the
+  // lane's last chunk ends at incl: the intervals tile [0, Z) exactly
+  int sel = -1, last = -1;
+  double sel_start = 0.0;
+  double s_c = excl;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const double m_c = mass_at(c, usep);
+    const double e_c = (c == c_hi - 1) ? incl : s_c + m_c;
+    if (m_c > 0.0) {
+      last = c;
+      if (sel < 0 && s_c <= thr && thr < e_c) {
+        sel = c;
+        sel_start = s_c;
+      }
+    }
+    s_c = e_c;
+  }
+  const uint64_t hit_c = __ballot(sel >= 0);
+  bool fallback = false;
+  int cstar;
+  double thr_c;
+  if (hit_c) {
+    const int src = __builtin_ctzll(hit_c);
+    cstar = __shfl(sel, src, 64);
+    thr_c = thr - __shfl(sel_start, src, 64);
+  } else {  // rounding: the last chunk with mass
+    fallback = true;
+    const uint64_t has = __ballot(last >= 0);
+    cstar = has ? __shfl(last, 63 - __builtin_clzll(has), 64) : 0;
+    thr_c = 0.0;
+  }
+
+  // ---- 2. column level: lane l owns columns cstar * kChunk + 32 l .. + 32
+  const int64_t colL = static_cast<int64_t>(cstar) * kChunk + lane * kChunkGroups * 8;
+  const RowScale k = rq.k;
+  float m[kChunkGroups * 8];
+  double csum = 0.0;
+#pragma unroll
+  for (int gg = 0; gg < kChunkGroups; ++gg) {
+    float r[8];
+    column_masses<DT, VEC>(a, t, d, pair && !usep, k, colL + gg * 8, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      m[gg * 8 + e] = r[e];
+      csum += static_cast<double>(r[e]);
+    }
+  }
+  double cincl = csum;
+#pragma unroll
+  for (int dd = 1; dd < 64; dd <<= 1) {
+    const double o = __shfl_up(cincl, dd, 64);
+    if (lane >= dd) cincl += o;
+  }
+  double cexcl = __shfl_up(cincl, 1, 64);
+  if (lane == 0) cexcl = 0.0;
   int found = -1;
-  if (!fallback && lexcl <= thr_c && lincl > thr_c) {
-    double cum = lexcl;
+  if (!fallback && cexcl <= thr_c && cincl > thr_c) {
+    double cum = cexcl;
 #pragma unroll
     for (int e = 0; e < kChunkGroups * 8; ++e) {
       cum += static_cast<double>(m[e]);
@@ -691,19 +708,19 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_kernel(SampleArgs a)
       for (int e = 0; e < kChunkGroups * 8; ++e)
         if (m[e] > 0.0f) found = e;
   }
-  int last = -1;
+  int lastc = -1;
 #pragma unroll
   for (int e = 0; e < kChunkGroups * 8; ++e)
-    if (m[e] > 0.0f) last = e;
+    if (m[e] > 0.0f) lastc = e;
   const uint64_t hit = __ballot(found >= 0);
   int tok;
   if (hit) {
     const int src = __builtin_ctzll(hit);
     tok = __shfl(static_cast<int>(colL) + found, src, 64);
   } else {  // no lane claimed u * Z (rounding): the chunk's last id with positive mass
-    const uint64_t has = __ballot(last >= 0);
+    const uint64_t has = __ballot(lastc >= 0);
     const int src = has ? 63 - __builtin_clzll(has) : 0;
-    tok = __shfl(static_cast<int>(colL) + (last < 0 ? 0 : last), src, 64);
+    tok = __shfl(static_cast<int>(colL) + (lastc < 0 ? 0 : lastc), src, 64);
   }
   emit(tok);
 }
@@ -746,24 +763,13 @@ hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_st
   return hipGetLastError();
 }
 
-hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
+hipError_t launch_draw(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.mass_blocks));
   if (dtype == 0) {
-    if (vec) hipLaunchKernelGGL((sv_sample_mass_kernel<0, true>), grid, dim3(kMassThreads), 0, st, a);
-    else hipLaunchKernelGGL((sv_sample_mass_kernel<0, false>), grid, dim3(kMassThreads), 0, st, a);
+    if (vec) hipLaunchKernelGGL((sv_draw_kernel<0, true>), grid, dim3(kMassThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_draw_kernel<0, false>), grid, dim3(kMassThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL((sv_sample_mass_kernel<1, false>), grid, dim3(kMassThreads), 0, st, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B));
-  if (dtype == 0) {
-    if (vec) hipLaunchKernelGGL((sv_sample_kernel<0, true>), grid, dim3(kSampleThreads), 0, st, a);
-    else hipLaunchKernelGGL((sv_sample_kernel<0, false>), grid, dim3(kSampleThreads), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((sv_sample_kernel<1, false>), grid, dim3(kSampleThreads), 0, st, a);
+    hipLaunchKernelGGL((sv_draw_kernel<1, false>), grid, dim3(kMassThreads), 0, st, a);
   }
   return hipGetLastError();
 }

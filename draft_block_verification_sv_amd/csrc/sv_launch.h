@@ -56,6 +56,7 @@ struct RowPairArgs {
   float* d_off;
   float* d_lz;
   int32_t* acc;
+  int32_t* arrive;  // nullable: per-request draw counters, zeroed here for the draw kernel
 };
 
 struct SampleArgs {
@@ -80,9 +81,10 @@ struct SampleArgs {
   const float* d_off;
   const float* d_lz;
   const int32_t* acc;
-  double* chunk_mass;   // [B * n_chunks], written by sv_sample_mass, read by sv_sample
+  double* chunk_mass;   // [B * n_chunks]: each draw workgroup's chunk masses
+  int32_t* arrive;      // [B]: draw workgroups of the request done; the last one picks
   bool force_greedy;    // every request greedy (sv_verify_block_greedy): T_b = 0
-  int32_t mass_blocks;  // sv_sample_mass workgroups per request
+  int32_t mass_blocks;  // draw workgroups per request
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_at;
@@ -134,7 +136,6 @@ hipError_t launch_len_loss(int64_t B, const float* a_hat, const int32_t* accept_
                            const int32_t* k_hat, float* loss, float* dloss, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
 hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
-hipError_t launch_sample_mass(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
-hipError_t launch_sample(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
+hipError_t launch_draw(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 
 }  // namespace sv

@@ -28,18 +28,16 @@ constexpr int kMaxSlices = 512;
 // writes per-row descriptors first.
 constexpr int kInlinePerThread = 8;
 constexpr int kInlinePlanMaxB = kRowThreads * kInlinePerThread;
-// The sampler works on chunks of kChunk columns (one wave, kChunkGroups groups of 8 per
-// lane).  sv_sample_mass: 256-thread workgroups of kMassChunksPerBlock chunks each, so a
-// request's row is spread over ceil(n_chunks / kMassChunksPerBlock) workgroups.  sv_sample:
-// one 1024-thread workgroup per request, one chunk per thread (V <= kMaxChunks * kChunk).
+// The draw works on chunks of kChunk columns (one wave, kChunkGroups groups of 8 per
+// lane).  sv_draw: 256-thread workgroups of kMassChunksPerBlock chunks each, so a request's
+// row is spread over ceil(n_chunks / kMassChunksPerBlock) workgroups; the last of them to
+// finish scans the request's chunk masses with one wave (V <= kMaxChunks * kChunk).
 constexpr int kChunkGroups = 4;
 constexpr int kChunk = 64 * 8 * kChunkGroups;
 constexpr int kMassWaves = 4;
 constexpr int kMassThreads = 64 * kMassWaves;
 constexpr int kMassChunksPerBlock = 2 * kMassWaves;
-constexpr int kSampleWaves = 16;
-constexpr int kSampleThreads = 64 * kSampleWaves;
-constexpr int kMaxChunks = kSampleThreads;
+constexpr int kMaxChunks = 1024;
 
 inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 inline int64_t n_chunks_for(int64_t V) { return (V + kChunk - 1) / kChunk; }
@@ -76,6 +74,7 @@ struct Workspace {
   float* d_lz;         // [n_d]
   int32_t* acc;        // [n_d] acceptance flag
   double* chunk_mass;  // [B * n_chunks] draw mass of each chunk of each request's draw row
+  int32_t* arrive;     // [B] draw workgroups of each request done (zeroed by the streaming pass)
   RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
   float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
 };
@@ -107,6 +106,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.d_lz = reinterpret_cast<float*>(take(d.n_d * 4));
   w.acc = reinterpret_cast<int32_t*>(take(d.n_d * 4));
   w.chunk_mass = reinterpret_cast<double*>(take(d.B * d.n_chunks * sizeof(double)));
+  w.arrive = reinterpret_cast<int32_t*>(take(d.B * sizeof(int32_t)));
   w.stats = reinterpret_cast<RowStats*>(take(d.n_grad * sizeof(RowStats)));
   w.coef = reinterpret_cast<float*>(take(d.n_grad * 2 * sizeof(float)));
   if (ws) *ws = w;

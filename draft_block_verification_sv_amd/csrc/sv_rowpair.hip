@@ -878,7 +878,10 @@ void sv_rowpair_kernel(RowPairArgs a) {
     ctx.beta = kL2E / T;
   }
   if (!uniform_ok(a.uniforms[ctx.t])) flags |= 16;
-  if (i == 0 && tid == 0 && !a.desc) a.off_t[b] = static_cast<int32_t>(off);
+  if (i == 0 && tid == 0 && !a.desc) {
+    a.off_t[b] = static_cast<int32_t>(off);
+    if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
+  }
   // the draft token and the two logits at it, fetched before the stream starts
   if (tid == 0) {
     s_x = -1;
@@ -972,7 +975,10 @@ __global__ __launch_bounds__(kRowThreads) void sv_greedy_kernel(RowPairArgs a) {
   const int kb = a.k[b];
   const int i = static_cast<int>(t - off);
   const int64_t d = (i < kb) ? (off - b + i) : -1;
-  if (i == 0 && tid == 0 && !a.desc) a.off_t[b] = static_cast<int32_t>(off);
+  if (i == 0 && tid == 0 && !a.desc) {
+    a.off_t[b] = static_cast<int32_t>(off);
+    if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
+  }
   const void* prow = static_cast<const char*>(a.target) + t * a.ld_t * (DT == 0 ? 2 : 4);
 
   float best = -INFINITY;
