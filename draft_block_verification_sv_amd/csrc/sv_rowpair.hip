@@ -62,6 +62,12 @@ __device__ __forceinline__ int64_t block_index() {
 constexpr uint32_t kNaNBits = 0x7fc00000u;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Raw buffer resources (stride 0, byte-addressed, 32-bit data format word) for the
+// bounds-checked loads of the streaming loop; the loads stream (nontemporal) like the
+// plain ones.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufAux = SV_ROWS_NT ? 2 : 0;
+
 __device__ __forceinline__ void store_nan(float* p) { *reinterpret_cast<uint32_t*>(p) = kNaNBits; }
 
 // Uniform valid iff in [0, 1) (-0 allowed); decided on the bits.
@@ -111,17 +117,30 @@ struct PackedRow {
   }
   // Running maxima across slices: raw words (high elements, masked at the end) into mh,
   // low elements into ml.
+  // Written as chains of three-input maxima (one v_max3_f32 per two elements).
   __device__ __forceinline__ void fold_max(float& mh, float& ml) const {
 #pragma unroll
     for (int i = 0; i < kElemsPerLane / 2; i += 2) {
-      mh = fmaxf(mh, fmaxf(__uint_as_float(w[i]), __uint_as_float(w[i + 1])));
-      ml = fmaxf(ml, fmaxf(bf16_lo(w[i]), bf16_lo(w[i + 1])));
+      mh = fmaxf(fmaxf(mh, __uint_as_float(w[i])), __uint_as_float(w[i + 1]));
+      ml = fmaxf(fmaxf(ml, bf16_lo(w[i])), bf16_lo(w[i + 1]));
     }
   }
   __device__ __forceinline__ void load(const uint16_t* p) {  // p: this lane's first column
 #pragma unroll
     for (int c = 0; c < kGroups; ++c) {
       const uint4 v = stream_load(reinterpret_cast<const uint4*>(p + c * 512));
+      w[c * 4 + 0] = v.x;
+      w[c * 4 + 1] = v.y;
+      w[c * 4 + 2] = v.z;
+      w[c * 4 + 3] = v.w;
+    }
+  }
+  // Bounds-checked form: byte offset off of the lane's first column inside the buffer r;
+  // words past the buffer's end read as zero and touch no memory.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off) {
+#pragma unroll
+    for (int c = 0; c < kGroups; ++c) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + c * 1024, 0, kBufAux);
       w[c * 4 + 0] = v.x;
       w[c * 4 + 1] = v.y;
       w[c * 4 + 2] = v.z;
@@ -145,7 +164,7 @@ struct FloatRow {
   __device__ __forceinline__ void fold_max(float& mh, float& ml) const {
     (void)mh;
 #pragma unroll
-    for (int j = 0; j < kElemsPerLane; j += 2) ml = fmaxf(ml, fmaxf(x[j], x[j + 1]));
+    for (int j = 0; j < kElemsPerLane; j += 2) ml = fmaxf(fmaxf(ml, x[j]), x[j + 1]);
   }
   // Columns >= V read as -inf.  VEC: the row allows 16-byte loads.
   template <int DT, bool VEC>
@@ -281,20 +300,22 @@ template <bool PAIR, int MODE, bool MASK, class Row>
 __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq, float beta,
                                                     int64_t col_lane, int V, const LaneAcc& A) {
   const float op = -A.kp, oq = -A.kq, otp = -A.ktp, otq = -A.ktq;
-  float sp0 = 0.f, sp1 = 0.f, sq0 = 0.f, sq1 = 0.f, w0 = 0.f, w1 = 0.f;
-  float stp0 = 0.f, stp1 = 0.f, stq0 = 0.f, stq1 = 0.f;
-  float dm0 = -INFINITY, dm1 = -INFINITY;
+  // Two chains per sum, each started from its first term (no add of zero); the maxima of
+  // l_q - l_p as chains of three-input maxima.
+  float sp0, sp1, sq0, sq1, w0, w1, stp0, stp1, stq0, stq1, dm0, dm1;
+  auto acc = [](float& s, float v, bool first) { s = first ? v : s + v; };
 #pragma unroll
   for (int e = 0; e < kElemsPerLane; e += 2) {
+    const bool first = (e == 0);
     float t[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float xp = rp.at(e + h);
       const float ep = fast_exp2(__builtin_fmaf(xp, kL2E, op));
-      if (h) sp1 += ep; else sp0 += ep;
+      acc(h ? sp1 : sp0, ep, first);
       if constexpr (MODE == 2) {
         const float etp = fast_exp2(__builtin_fmaf(xp, beta, otp));
-        if (h) stp1 += etp; else stp0 += etp;
+        acc(h ? stp1 : stp0, etp, first);
       }
       if constexpr (PAIR) {
         const float xq = rq.at(e + h);
@@ -304,23 +325,20 @@ __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq
           const int ee = e + h;
           if (col_lane + (ee >> 3) * 512 + (ee & 7) >= V) diff = 0.0f;
         }
-        if (h) {
-          sq1 += eq;
-          w1 = __builtin_fmaf(eq, diff, w1);
-        } else {
-          sq0 += eq;
-          w0 = __builtin_fmaf(eq, diff, w0);
-        }
+        float& sq = h ? sq1 : sq0;
+        float& w = h ? w1 : w0;
+        acc(sq, eq, first);
+        w = first ? eq * diff : __builtin_fmaf(eq, diff, w);
         t[h] = diff;
         if constexpr (MODE == 2) {
           const float etq = fast_exp2(__builtin_fmaf(xq, beta, otq));
-          if (h) stq1 += etq; else stq0 += etq;
+          acc(h ? stq1 : stq0, etq, first);
         }
       }
     }
     if constexpr (PAIR) {
-      if (e & 2) dm1 = fmaxf(dm1, fmaxf(t[0], t[1]));
-      else dm0 = fmaxf(dm0, fmaxf(t[0], t[1]));
+      float& dm = (e & 2) ? dm1 : dm0;
+      dm = (e < 4) ? fmaxf(t[0], t[1]) : fmaxf(fmaxf(dm, t[0]), t[1]);
     }
   }
   SlicePart P;
@@ -406,35 +424,40 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
     }
   }
   if constexpr (DT == 0 && VEC && SV_ROWS_PREFETCH) {
-    const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
-    const uint16_t* Q = static_cast<const uint16_t*>(qrow) + lane * 8;
+    // The row's full slices as bounds-checked buffers: the prefetch of a slice past the
+    // last one reads zeros without touching memory, so every prefetch is issued without a
+    // branch and the wait before a slice's arithmetic covers that slice's loads alone (a
+    // load issued under a branch makes the wait at the join count it as well).
+    const int full_bytes = n_full * kSlice * 2;
+    const __amdgpu_buffer_rsrc_t RP =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(prow), 0, full_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t RQ =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(qrow), 0, PAIR ? full_bytes : 0, kBufWord3);
+    const int lane_off = lane * 16;
     PackedRow ap, aq, bp, bq;
+    auto load_pair = [&](PackedRow& rp, PackedRow& rq, int sl) {
+      rp.load(RP, lane_off + sl * (kSlice * 2));
+      if constexpr (PAIR) rq.load(RQ, lane_off + sl * (kSlice * 2));
+    };
     if (s < n_full) {
-      ap.load(P + static_cast<int64_t>(s) * kSlice);
-      if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s) * kSlice);
+      load_pair(ap, aq, s);
       lane_init<PAIR, MODE>(ap, aq, beta, A);
       fresh = false;
-    }
-    while (s < n_full) {
-      const int s2 = s + kRowWaves;
-      if (s2 < n_full) {
-        bp.load(P + static_cast<int64_t>(s2) * kSlice);
-        if constexpr (PAIR) bq.load(Q + static_cast<int64_t>(s2) * kSlice);
+      while (true) {
+        load_pair(bp, bq, s + kRowWaves);
+        slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
+                                            static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
+        if (s + kRowWaves >= n_full) {
+          s += kRowWaves;
+          break;
+        }
+        load_pair(ap, aq, s + 2 * kRowWaves);
+        slice_accumulate<PAIR, MODE, false>(bp, bq, beta,
+                                            static_cast<int64_t>(s + kRowWaves) * kSlice + lane * 8,
+                                            V, A);
+        s += 2 * kRowWaves;
+        if (s >= n_full) break;
       }
-      slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
-                                          static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
-      if (s2 >= n_full) {
-        s = s2;
-        break;
-      }
-      const int s3 = s2 + kRowWaves;
-      if (s3 < n_full) {
-        ap.load(P + static_cast<int64_t>(s3) * kSlice);
-        if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s3) * kSlice);
-      }
-      slice_accumulate<PAIR, MODE, false>(bp, bq, beta,
-                                          static_cast<int64_t>(s2) * kSlice + lane * 8, V, A);
-      s = s3;
     }
   }
   for (; s < n_slices; s += kRowWaves) {  // every slice not handled above
