@@ -46,6 +46,9 @@
 #ifndef SV_ROWS_WAVES_PER_EU
 #define SV_ROWS_WAVES_PER_EU 1
 #endif
+#ifndef SV_ROWS_DEPTH
+#define SV_ROWS_DEPTH 1  // slices prefetched ahead of the one being reduced (1 or 2)
+#endif
 
 namespace sv {
 
@@ -439,6 +442,32 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
       rp.load(RP, lane_off + sl * (kSlice * 2));
       if constexpr (PAIR) rq.load(RQ, lane_off + sl * (kSlice * 2));
     };
+#if SV_ROWS_DEPTH == 2
+    // two slices in flight ahead of the one being reduced
+    PackedRow cp, cq;
+    auto add = [&](const PackedRow& rp, const PackedRow& rq, int sl) {
+      slice_accumulate<PAIR, MODE, false>(rp, rq, beta, static_cast<int64_t>(sl) * kSlice + lane * 8,
+                                          V, A);
+    };
+    if (s < n_full) {
+      load_pair(ap, aq, s);
+      load_pair(bp, bq, s + kRowWaves);
+      lane_init<PAIR, MODE>(ap, aq, beta, A);
+      fresh = false;
+      while (true) {
+        load_pair(cp, cq, s + 2 * kRowWaves);
+        add(ap, aq, s);
+        if (s + kRowWaves >= n_full) { s += kRowWaves; break; }
+        load_pair(ap, aq, s + 3 * kRowWaves);
+        add(bp, bq, s + kRowWaves);
+        if (s + 2 * kRowWaves >= n_full) { s += 2 * kRowWaves; break; }
+        load_pair(bp, bq, s + 4 * kRowWaves);
+        add(cp, cq, s + 2 * kRowWaves);
+        s += 3 * kRowWaves;
+        if (s >= n_full) break;
+      }
+    }
+#else
     if (s < n_full) {
       load_pair(ap, aq, s);
       lane_init<PAIR, MODE>(ap, aq, beta, A);
@@ -459,6 +488,7 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
         if (s >= n_full) break;
       }
     }
+#endif
   }
   for (; s < n_slices; s += kRowWaves) {  // every slice not handled above
     const int64_t col_lane = static_cast<int64_t>(s) * kSlice + lane * 8;
