@@ -284,7 +284,7 @@ def bench_length_head(args):
     W1 = (torch.randn(Hf, H, generator=g) / H ** 0.5).to(torch.bfloat16).to(dev)
     b1 = (torch.randn(Hf, generator=g) * 0.5).to(dev)
     w2 = (torch.randn(Hf, generator=g) * 3 / Hf ** 0.5).to(dev)
-    ws = pkg.alloc_workspace(int(pkg.lib().sv_length_head_workspace_size(B, Hf)), dev)
+    ws = pkg.alloc_workspace(int(pkg.lib().sv_length_head_workspace_size(B, k, H, Hf)), dev)
     out = {"a_hat": torch.empty(B, device=dev), "k_hat": torch.empty(B, dtype=torch.int32, device=dev),
            "off_t": torch.empty(B + 1, dtype=torch.int32, device=dev)}
 

@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
                               _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                               _c_sz, _c_p]
     L.sv_opd_loss.restype = _c_i32
-    L.sv_length_head_workspace_size.argtypes = [_c_i32, _c_i32]
+    L.sv_length_head_workspace_size.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
     L.sv_length_head_workspace_size.restype = _c_sz
     L.sv_length_head.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64, _c_p,
                                  _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
@@ -266,7 +266,7 @@ def length_head(h: torch.Tensor, W1: torch.Tensor, w2: torch.Tensor, b1=None, b2
     if b1 is not None:
         _need(b1, "b1", torch.float32, Hf, dev)
     if workspace is None:
-        nbytes = int(lib().sv_length_head_workspace_size(B, Hf))
+        nbytes = int(lib().sv_length_head_workspace_size(B, k, H, Hf))
         if nbytes == 0:
             raise SpecVerifyError(f"invalid shape B={B} H'={Hf}")
         workspace = alloc_workspace(nbytes, dev)

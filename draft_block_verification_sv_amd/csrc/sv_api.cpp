@@ -17,13 +17,13 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 17;
+constexpr int kNumKernels = 18;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
-    "sv_head_out",    "sv_len_loss"};
+    "sv_head_pool",   "sv_head_out",     "sv_len_loss"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -40,6 +40,7 @@ enum {
   K_GREEDY,
   K_GREEDY_PICK,
   K_HEAD_FEAT,
+  K_HEAD_POOL,
   K_HEAD_OUT,
   K_LEN_LOSS
 };
@@ -518,32 +519,33 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
   return SV_OK;
 }
 
-size_t sv_length_head_workspace_size(int32_t B, int32_t H_feat) {
-  if (B < 1 || B > SV_MAX_BATCH || H_feat < 1 || H_feat > SV_MAX_HEAD_FEATURES) return 0;
-  return ((static_cast<size_t>(B) * H_feat * sizeof(float)) + 255) & ~size_t(255);
+namespace {
+bool head_shape_ok(int32_t B, int32_t k, int32_t H, int32_t H_feat) {
+  return B >= 1 && B <= SV_MAX_BATCH && k >= 1 && k <= SV_MAX_K && H >= 32 && H % 32 == 0 &&
+         H_feat >= 1 && H_feat <= SV_MAX_HEAD_FEATURES;
+}
+}  // namespace
+
+size_t sv_length_head_workspace_size(int32_t B, int32_t k, int32_t H, int32_t H_feat) {
+  if (!head_shape_ok(B, k, H, H_feat)) return 0;
+  return (sv::head_partial_bytes(sv::head_split(B, k, H, H_feat)) + 255) & ~size_t(255);
 }
 
 sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const void* h,
                          int64_t ld_h, const void* W1, int64_t ld_w, const float* b1,
                          const float* w2, float b2, float gamma, float* a_hat, int32_t* k_hat,
                          int32_t* off_t, void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 1 || B > SV_MAX_BATCH || k < 1 || k > SV_MAX_K || H < 32 || H % 32 != 0 ||
-      H_feat < 1 || H_feat > SV_MAX_HEAD_FEATURES || ld_h < H || ld_w < H || ld_h % 8 != 0 ||
-      ld_w % 8 != 0)
+  if (!head_shape_ok(B, k, H, H_feat) || ld_h < H || ld_w < H || ld_h % 8 != 0 || ld_w % 8 != 0)
     return SV_ERR_SHAPE;
   if (!h || !W1 || !w2 || !a_hat || !k_hat) return SV_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(h) % 16) != 0 || (reinterpret_cast<uintptr_t>(W1) % 16) != 0)
     return SV_ERR_SHAPE;
   if (!(std::isfinite(gamma) && gamma > 0.0f) || !std::isfinite(b2)) return SV_ERR_VALUE;
-  const size_t need = sv_length_head_workspace_size(B, H_feat);
+  const size_t need = sv_length_head_workspace_size(B, k, H, H_feat);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
     return SV_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  sv::HeadArgs ha{};
-  ha.B = B;
-  ha.k = k;
-  ha.H = H;
-  ha.Hf = H_feat;
+  sv::HeadArgs ha = sv::head_split(B, k, H, H_feat);
   ha.h = h;
   ha.ld_h = ld_h;
   ha.W1 = W1;
@@ -552,11 +554,13 @@ sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const 
   ha.w2 = w2;
   ha.b2 = b2;
   ha.gamma = gamma;
-  ha.pooled = static_cast<float*>(workspace);
+  ha.partial = static_cast<float*>(workspace);
   ha.a_hat = a_hat;
   ha.k_hat = k_hat;
   ha.off_t = off_t;
   if (timed(K_HEAD_FEAT, st, [&] { return sv::launch_head(ha, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+  if (timed(K_HEAD_POOL, st, [&] { return sv::launch_head_pool(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;
   if (timed(K_HEAD_OUT, st, [&] { return sv::launch_head_out(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;

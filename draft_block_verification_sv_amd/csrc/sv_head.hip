@@ -2,21 +2,27 @@
 // and "Online Update of the Length Head"; Section 3.3 "Adaptive Request Scheduling" for the
 // packed layout), on gfx950 matrix cores.
 //
-//   sv_head_feat   per request b and 16-feature slab: the k x 16 block of W1 h_b^T on MFMA
-//                  (v_mfma_f32_16x16x32_bf16, 16-position tiles, K = H in steps of 32 split
-//                  four ways across the waves, eight steps of loads in flight, partial tiles
-//                  summed in LDS in wave order), then + b1, SiLU and the mean over the k
-//                  positions, written as the pooled features of b (fp32).
-//   sv_head_out    one workgroup: a_hat_b = sigmoid(w2 . pooled_b + b2) (fp64 dot, fixed
-//                  combination order), k_hat_b = clamp(floor(a_hat_b gamma k), 1, k) in fp64, and the
-//                  packed target-row offsets off_t[b] = sum_{c<b} (k_hat_c + 1).
+//   sv_head_feat   the projection z = W1 h^T as a split-K GEMM on v_mfma_f32_16x16x32_bf16.
+//                  A request's positions form ceil(k / 16) blocks of 16 rows; a workgroup
+//                  takes four blocks (one per wave) against one 64-feature tile (four MFMA
+//                  tiles) over one K-chunk, four K steps of loads in flight, and writes the
+//                  fp32 partial sums of that chunk.
+//   sv_head_pool   one workgroup per request: z = sum of the K-chunks' partials in chunk order
+//                  + b1, SiLU, the mean over the k positions, a_hat = sigmoid(w2 . pooled + b2)
+//                  (fp64 dot, fixed combination order) and k_hat = clamp(floor(a_hat gamma k),
+//                  1, k) in fp64.
+//   sv_head_out    one workgroup: the packed target-row offsets
+//                  off_t[b] = sum_{c<b} (k_hat_c + 1).
 //   sv_len_loss    l_len_b = (a_hat_b - a_b / k_hat_b)^2 and its derivative in a_hat.
 //
 // MFMA lane layout of the 16x16x32 bf16 instruction (checked on the device): lane l holds
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e = 0..7, and its four results
 // are D[4 (l / 16) + i][l % 16], i = 0..3.  A is the 16-row tile of h (positions x H), B the
 // transposed 16-column tile of W1 (H x features), so both operands are 16-byte loads of 8
-// consecutive elements of one row.
+// consecutive elements of one row.  Rows past a request's k (and past the last request) and
+// features past H' are read from clamped, in-bounds rows: an MFMA output row depends only
+// on its own A row and an output column only on its own B column, so those rows and columns
+// are simply never used, and every load is issued without a condition.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -35,74 +41,121 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& w) {
   return v;
 }
 
-constexpr int kHeadCols = 16;   // features per workgroup (one 16 x 16 MFMA tile)
-constexpr int kHeadSplit = 4;   // the workgroup's waves split K four ways
-constexpr int kHeadUnroll = 8;  // K steps whose loads are in flight together
+#ifndef SV_HEAD_UNROLL
+#define SV_HEAD_UNROLL 8
+#endif
+constexpr int kHeadUnroll = SV_HEAD_UNROLL;  // K steps whose loads are in flight together
 
-// One workgroup: request b, features n0 .. n0 + 15.  Wave w accumulates the w-th quarter of
-// the K steps of every 16-position tile; the four partial tiles are summed in LDS
-// in wave order, then wave 0 adds b1, applies SiLU and pools over the k positions.
-__global__ __launch_bounds__(64 * kHeadSplit) void sv_head_feat_kernel(HeadArgs a) {
-  __shared__ float part[kHeadSplit][64][4];
+// One workgroup: blocks 4 g .. 4 g + 3 (wave w takes block 4 g + w), features n0 .. n0 + 63,
+// K-chunk c.  Writes partial[((c NB + blk) 16 + row) H' + n] for n < H'.
+__global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + wave;
+  const int64_t n_rows = a.B * static_cast<int64_t>(a.k);
+  const int r = lane & 15, kg = (lane >> 4) * 8;  // operand row / column, k offset
+  // this lane's A row: position 16 j + r of request b (clamped in bounds, see above)
+  const int64_t b = blk / a.R;
+  const int pos = static_cast<int>(blk - b * a.R) * 16 + r;
+  int64_t hrow = b * a.k + pos;
+  if (pos >= a.k || hrow >= n_rows) hrow = n_rows - 1;
+  const uint16_t* Hrow = static_cast<const uint16_t*>(a.h) + hrow * a.ld_h + kg;
+  const int n0 = blockIdx.y * kHeadTileN;
+  const uint16_t* Wrow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = min(n0 + 16 * t + r, a.Hf - 1);
+    Wrow[t] = static_cast<const uint16_t*>(a.W1) + static_cast<int64_t>(n) * a.ld_w + kg;
+  }
+  const int c = blockIdx.z;
+  const int steps = a.H / 32;
+  const int k_lo = 32 * ((c * steps) / a.S);
+  const int k_hi = 32 * (((c + 1) * steps) / a.S);
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int kk = k_lo;
+  for (; kk + 32 * kHeadUnroll <= k_hi; kk += 32 * kHeadUnroll) {
+    uint4 av[kHeadUnroll], bv[4][kHeadUnroll];
+#pragma unroll
+    for (int u = 0; u < kHeadUnroll; ++u) {
+      av[u] = *reinterpret_cast<const uint4*>(Hrow + kk + 32 * u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bv[t][u] = *reinterpret_cast<const uint4*>(Wrow[t] + kk + 32 * u);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before the MFMAs
+#pragma unroll
+    for (int u = 0; u < kHeadUnroll; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[t][u]),
+                                                         acc[t], 0, 0, 0);
+  }
+  for (; kk < k_hi; kk += 32) {
+    const uint4 av = *reinterpret_cast<const uint4*>(Hrow + kk);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(Wrow[t] + kk);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
+    }
+  }
+  if (blk >= a.NB) return;
+  // lane holds D[4 (l/16) + i][l % 16] of each feature tile t
+  float* P = a.partial + ((static_cast<int64_t>(c) * a.NB + blk) * 16 + 4 * (lane >> 4)) * a.Hf;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = n0 + 16 * t + r;
+    if (n < a.Hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P[static_cast<int64_t>(i) * a.Hf + n] = acc[t][i];
+  }
+}
+
+// One workgroup per request: thread t takes features t, t + 256, ...; z summed over the
+// K-chunks in order, then + b1, SiLU and the sum over the k positions; the dot with w2 in fp64
+// over the thread's features, then over the threads in a fixed order.  The partials of four
+// positions (every K-chunk, up to kHeadMaxSplit) are loaded before any is used; indices past k
+// or S are clamped in bounds and their values dropped, so no load sits under a branch.
+__global__ __launch_bounds__(256) void sv_head_pool_kernel(HeadArgs a) {
+  __shared__ double s_w[4];
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.y * kHeadCols;
-  const int r = lane & 15, kg = (lane >> 4) * 8;  // operand row / column, k offset
-  const int n = n0 + r;                            // the W1 row this lane loads
-  const bool n_ok = n < a.Hf;
-  const int steps = a.H / 32;  // MFMA K steps (H is a multiple of 32), shared out in order
-  const int k_lo = 32 * ((wave * steps) / kHeadSplit);
-  const int k_hi = 32 * (((wave + 1) * steps) / kHeadSplit);
-  const uint16_t* Wrow = static_cast<const uint16_t*>(a.W1) + (n_ok ? n : 0) * a.ld_w + kg;
-  float colsum = 0.0f;
-  for (int r0 = 0; r0 < a.k; r0 += 16) {
-    const int pos = r0 + r;
-    const bool p_ok = pos < a.k;
-    const uint16_t* Hrow =
-        static_cast<const uint16_t*>(a.h) + (b * a.k + (p_ok ? pos : 0)) * a.ld_h + kg;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    int kk = k_lo;
-    for (; kk + 32 * kHeadUnroll <= k_hi; kk += 32 * kHeadUnroll) {
-      uint4 av[kHeadUnroll], bv[kHeadUnroll];
+  const int64_t chunk_stride = a.NB * 16 * static_cast<int64_t>(a.Hf);
+  double dot = 0.0;
+  for (int n = tid; n < a.Hf; n += 256) {
+    const float bias = a.b1 ? a.b1[n] : 0.0f;
+    float colsum = 0.0f;
+    for (int i0 = 0; i0 < a.k; i0 += 4) {
+      float v[4][kHeadMaxSplit];
 #pragma unroll
-      for (int u = 0; u < kHeadUnroll; ++u) {
-        av[u] = p_ok ? *reinterpret_cast<const uint4*>(Hrow + kk + 32 * u) : make_uint4(0, 0, 0, 0);
-        bv[u] = n_ok ? *reinterpret_cast<const uint4*>(Wrow + kk + 32 * u) : make_uint4(0, 0, 0, 0);
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = min(i0 + ii, a.k - 1);
+        const float* P = a.partial + ((b * a.R + i / 16) * 16 + (i % 16)) * a.Hf + n;
+#pragma unroll
+        for (int c = 0; c < kHeadMaxSplit; ++c) v[ii][c] = P[min(c, a.S - 1) * chunk_stride];
       }
 #pragma unroll
-      for (int u = 0; u < kHeadUnroll; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u]), acc, 0,
-                                                     0, 0);
-    }
-    for (; kk + 32 <= k_hi; kk += 32) {
-      const uint4 av = p_ok ? *reinterpret_cast<const uint4*>(Hrow + kk) : make_uint4(0, 0, 0, 0);
-      const uint4 bv = n_ok ? *reinterpret_cast<const uint4*>(Wrow + kk) : make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][lane][i] = acc[i];
-    __syncthreads();
-    if (wave == 0) {
-      // lane holds D[4 (l/16) + i][l % 16]: positions r0 + 4 (l/16) + i, feature n0 + l % 16
-      const float bias = (a.b1 && n0 + (lane & 15) < a.Hf) ? a.b1[n0 + (lane & 15)] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int ii = 0; ii < 4; ++ii) {
         float z = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kHeadSplit; ++w) z += part[w][lane][i];
+        for (int c = 0; c < kHeadMaxSplit; ++c)
+          if (c < a.S) z += v[ii][c];
         z += bias;
-        const int p = r0 + 4 * (lane >> 4) + i;
-        if (p < a.k) colsum += z / (1.0f + __expf(-z));
+        if (i0 + ii < a.k) colsum += z / (1.0f + __expf(-z));
       }
     }
-    __syncthreads();
+    const float pooled = colsum / static_cast<float>(a.k);
+    dot += static_cast<double>(pooled) * static_cast<double>(a.w2[n]);
   }
-  if (wave == 0) {
-    // the four lanes of a feature column (l, l + 16, l + 32, l + 48) hold its row groups
-    colsum += __shfl_xor(colsum, 16, 64);
-    colsum += __shfl_xor(colsum, 32, 64);
-    const int fc = n0 + (lane & 15);
-    if (lane < 16 && fc < a.Hf) a.pooled[b * a.Hf + fc] = colsum / static_cast<float>(a.k);
+  dot = wave_sum_d(dot);
+  if (lane == 0) s_w[wave] = dot;
+  __syncthreads();
+  if (tid == 0) {
+    const double z = s_w[0] + s_w[1] + s_w[2] + s_w[3] + static_cast<double>(a.b2);
+    const double ah = 1.0 / (1.0 + exp(-z));
+    double t = floor(ah * static_cast<double>(a.gamma) * static_cast<double>(a.k));
+    t = t < 1.0 ? 1.0 : (t > a.k ? static_cast<double>(a.k) : t);
+    a.a_hat[b] = static_cast<float>(ah);
+    a.k_hat[b] = static_cast<int>(t);
   }
 }
 
@@ -126,27 +179,10 @@ __device__ __forceinline__ int block_excl_scan_1024_head(int v, int* lds_waves, 
   return base + x - v;
 }
 
-// One workgroup of 16 waves.  a_hat and k_hat: wave w takes requests w, w + 16, ..., its
-// lanes stride the features (coalesced), fp64 partial dots combined by a fixed butterfly.
-// Then the fixed-order scan of k_hat + 1 gives the packed offsets.
+// One workgroup: the fixed-order scan of k_hat + 1 gives the packed offsets.
 __global__ __launch_bounds__(1024) void sv_head_out_kernel(HeadArgs a) {
   __shared__ int s_waves[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int64_t b = wave; b < a.B; b += 16) {
-    const float* pb = a.pooled + b * a.Hf;
-    double dot = 0.0;
-    for (int n = lane; n < a.Hf; n += 64) dot += static_cast<double>(pb[n]) * static_cast<double>(a.w2[n]);
-    dot = wave_sum_d(dot) + static_cast<double>(a.b2);
-    if (lane == 0) {
-      const double ah = 1.0 / (1.0 + exp(-dot));
-      double t = floor(ah * static_cast<double>(a.gamma) * static_cast<double>(a.k));
-      t = t < 1.0 ? 1.0 : (t > a.k ? static_cast<double>(a.k) : t);
-      a.a_hat[b] = static_cast<float>(ah);
-      a.k_hat[b] = static_cast<int>(t);
-    }
-  }
-  if (!a.off_t) return;
-  __syncthreads();  // k_hat written by this workgroup, read back below
+  const int tid = threadIdx.x;
   int carry = 0;
   for (int64_t base = 0; base < a.B; base += 1024) {
     const int64_t b = base + tid;
@@ -173,14 +209,20 @@ __global__ __launch_bounds__(256) void sv_len_loss_kernel(int64_t B, const float
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B), static_cast<unsigned>((a.Hf + kHeadCols - 1) / kHeadCols));
-  hipLaunchKernelGGL(sv_head_feat_kernel, grid, dim3(64 * kHeadSplit), 0, st, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((a.NB + kHeadBlocks - 1) / kHeadBlocks),
+                  static_cast<unsigned>((a.Hf + kHeadTileN - 1) / kHeadTileN),
+                  static_cast<unsigned>(a.S));
+  hipLaunchKernelGGL(sv_head_feat_kernel, grid, dim3(64 * kHeadBlocks), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_pool(const HeadArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(sv_head_pool_kernel, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_head_out(const HeadArgs& a, hipStream_t st) {
+  if (!a.off_t) return hipSuccess;
   hipLaunchKernelGGL(sv_head_out_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

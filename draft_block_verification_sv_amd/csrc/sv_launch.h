@@ -125,12 +125,44 @@ struct HeadArgs {
   const float* b1;  // [Hf] or null
   const float* w2;  // [Hf]
   float b2, gamma;
-  float* pooled;    // workspace [B * Hf]
+  int32_t R;        // 16-row blocks per request: ceil(k / 16)
+  int64_t NB;       // blocks in all: B R
+  int32_t S;        // K-chunks of the split-K projection
+  float* partial;   // workspace [S][NB * 16][Hf]: the chunks' partial sums of W1 h^T
   float* a_hat;     // [B]
   int32_t* k_hat;   // [B]
   int32_t* off_t;   // [B + 1] or null
 };
+#ifndef SV_HEAD_SPLIT_TARGET
+#define SV_HEAD_SPLIT_TARGET 512  // workgroups the projection's K split aims for
+#endif
+// Blocks per workgroup and features per workgroup of the projection.
+constexpr int kHeadBlocks = 4;
+constexpr int kHeadTileN = 64;
+constexpr int kHeadMaxSplit = 8;  // K-chunks at most
+// The split of the projection for a head call: K-chunks so that the grid has about
+// SV_HEAD_SPLIT_TARGET workgroups (at most kHeadMaxSplit chunks, at least one K step of 32
+// each).
+inline HeadArgs head_split(int64_t B, int32_t k, int32_t H, int32_t Hf) {
+  HeadArgs a{};
+  a.B = B;
+  a.k = k;
+  a.H = H;
+  a.Hf = Hf;
+  a.R = (k + 15) / 16;
+  a.NB = B * a.R;
+  const int64_t tiles = ((a.NB + kHeadBlocks - 1) / kHeadBlocks) * ((Hf + kHeadTileN - 1) / kHeadTileN);
+  int64_t S = (SV_HEAD_SPLIT_TARGET + tiles - 1) / tiles;
+  S = S < 1 ? 1 : (S > kHeadMaxSplit ? kHeadMaxSplit : S);
+  if (S > H / 32) S = H / 32;
+  a.S = static_cast<int32_t>(S);
+  return a;
+}
+inline size_t head_partial_bytes(const HeadArgs& a) {
+  return static_cast<size_t>(a.S) * static_cast<size_t>(a.NB) * 16 * static_cast<size_t>(a.Hf) * sizeof(float);
+}
 hipError_t launch_head(const HeadArgs& a, hipStream_t st);
+hipError_t launch_head_pool(const HeadArgs& a, hipStream_t st);
 hipError_t launch_head_out(const HeadArgs& a, hipStream_t st);
 hipError_t launch_len_loss(int64_t B, const float* a_hat, const int32_t* accept_len,
                            const int32_t* k_hat, float* loss, float* dloss, hipStream_t st);

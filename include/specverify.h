@@ -243,8 +243,9 @@ sv_status sv_opd_loss_grad(int32_t dtype, int32_t B, int64_t n_rows, int64_t n_t
                            int32_t* device_status, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* Bytes of workspace sv_length_head needs; 0 if invalid. */
-size_t sv_length_head_workspace_size(int32_t B, int32_t H_feat);
+/* Bytes of workspace sv_length_head needs for this shape (the projection's split-K partial
+ * sums); 0 if the shape is invalid. */
+size_t sv_length_head_workspace_size(int32_t B, int32_t k, int32_t H, int32_t H_feat);
 
 /*
  * sv_length_head: the adaptive length head of the AdaFlash paper, Section 3.2, and the packed
@@ -261,7 +262,7 @@ size_t sv_length_head_workspace_size(int32_t B, int32_t H_feat);
  *                   NULL (no bias); w2 float[H_feat]; b2, gamma (> 0) scalars.
  *   ld_h, ld_w      row strides in elements, >= H and multiples of 8; h and W1 16-byte aligned.
  * Outputs (device): a_hat float[B], k_hat int32[B], off_t int32[B + 1] (or NULL).
- * Workspace: sv_length_head_workspace_size(B, H_feat) bytes, 256-byte aligned.
+ * Workspace: sv_length_head_workspace_size(B, k, H, H_feat) bytes, 256-byte aligned.
  */
 sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const void* h,
                          int64_t ld_h, const void* W1, int64_t ld_w, const float* b1,

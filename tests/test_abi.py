@@ -175,6 +175,8 @@ def test_length_head_argument_errors(L):
     assert call(h=8) == 2  # not 16-byte aligned
     assert call(gamma=0.0) == 4
     assert call(ws=None, wsb=1 << 30) == 5
-    assert L.sv_length_head_workspace_size(4, 256) >= 4 * 256 * 4
+    assert L.sv_length_head_workspace_size(4, 15, 4096, 256) >= 4 * 16 * 256 * 4
+    assert L.sv_length_head_workspace_size(4, 65, 4096, 256) == 0
+    assert L.sv_length_head_workspace_size(4, 15, 48, 256) == 0
     assert L.sv_length_loss(0, 8, 8, 8, 8, None, None) == 2
     assert L.sv_length_loss(2, None, 8, 8, 8, None, None) == 1
