@@ -89,13 +89,15 @@ _OPD = None  # (target rows, draft rows, pairing, delta), inherited by forked wo
 def _oracle_opd_request(b):
     import oracle
 
-    tl, dl, idx, off, k, delta = _OPD
+    tl, dl, idx, off, k, delta, grad = _OPD
     sl = slice(int(off[b]), int(off[b + 1]))
     oracle.opd_loss(tl[idx[sl]], dl[sl], [int(k[b])], delta, 0.8)
+    if grad:
+        oracle.opd_grad(tl[idx[sl]], dl[sl], [int(k[b])], delta, 0.8)
     return int(k[b])
 
 
-def cpu_baseline_opd(w, idx, n_requests: int) -> dict:
+def cpu_baseline_opd(w, idx, n_requests: int, grad: bool = False) -> dict:
     import multiprocessing as mp
 
     import oracle
@@ -103,16 +105,48 @@ def cpu_baseline_opd(w, idx, n_requests: int) -> dict:
     global _OPD
     tl = oracle.widen_logits(w.target[:, : w.V], w.dtype)
     dl = oracle.widen_logits(w.draft[:, : w.V], w.dtype)
-    _OPD = (tl, dl, idx, w.draft_offsets, w.k, w.delta)
+    _OPD = (tl, dl, idx, w.draft_offsets, w.k, w.delta, grad)
     cores = max(1, min(16, os.cpu_count() or 1))
     reqs = list(range(min(n_requests, w.B)))
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(cores) as pool:
         rows = sum(pool.map(_oracle_opd_request, reqs, chunksize=1))
     dt = time.perf_counter() - t0
+    what = "hard CE, clipped rKL, OPD loss" + (" and its gradient rows" if grad else "")
     return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(reqs)} of {w.B} requests ({rows} row pairs: hard CE, clipped rKL, "
-                      f"OPD loss), float64 NumPy, {cores} worker processes, {dt:.2f} s wall"}
+            "sample": f"{len(reqs)} of {w.B} requests ({rows} row pairs: {what}), float64 NumPy, "
+                      f"{cores} worker processes, {dt:.2f} s wall"}
+
+
+def _oracle_greedy_request(b):
+    import numpy as np
+
+    import oracle
+
+    w = _W
+    oracle.verify_block(target=w.target, draft=w.draft, dtype=w.dtype, V=w.V, k=w.k,
+                        draft_tokens=w.draft_tokens, uniforms=w.uniforms,
+                        temperature=np.zeros(w.B), delta=w.delta, requests=[b], with_rkl=False)
+    return int(w.k[b])
+
+
+def cpu_baseline_greedy(w, n_requests: int) -> dict:
+    """The oracle at temperature 0, without the reverse-KL (it also forms the reported
+    probabilities and per-position acceptance rates)."""
+    import multiprocessing as mp
+
+    global _W
+    _W = w
+    cores = max(1, min(16, os.cpu_count() or 1))
+    reqs = list(range(min(n_requests, w.B)))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        positions = sum(pool.map(_oracle_greedy_request, reqs, chunksize=1))
+    dt = time.perf_counter() - t0
+    return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions at "
+                      f"temperature 0, no rKL), float64 NumPy, {cores} worker processes, "
+                      f"{dt:.2f} s wall"}
 
 
 def bench_opd(args, w, grad=False):
@@ -125,7 +159,7 @@ def bench_opd(args, w, grad=False):
                              for b in range(w.B)]).astype(np.int32)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_opd(w, idx_np, args.cpu_requests)
+        cpu = cpu_baseline_opd(w, idx_np, args.cpu_requests, grad=grad)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} rows/s")
     pkg.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -211,6 +245,10 @@ def bench_greedy(args, w):
 
     import draft_block_verification_sv_amd as pkg
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_greedy(w, args.cpu_requests)
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} positions/s")
     pkg.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -263,7 +301,7 @@ def bench_greedy(args, w):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
         "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
@@ -277,13 +315,29 @@ def bench_length_head(args):
     import draft_block_verification_sv_amd as pkg
 
     B, k, H, Hf = 128, 15, 4096, 256
+    g = torch.Generator(device="cpu").manual_seed(20261202)
+    h_c = torch.randn(B, k, H, generator=g).to(torch.bfloat16)
+    W1_c = (torch.randn(Hf, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    b1_c = torch.randn(Hf, generator=g) * 0.5
+    w2_c = torch.randn(Hf, generator=g) * 3 / Hf ** 0.5
+    cpu = None
+    if not args.no_cpu_baseline:  # the oracle, float64, on every request
+        import oracle
+
+        nb = B
+        hh = h_c[:nb].float().numpy().astype(np.float64)
+        WW = W1_c.float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.length_head(hh, WW, b1_c.numpy().astype(np.float64), w2_c.numpy().astype(np.float64),
+                           0.1)
+        dt = time.perf_counter() - t0
+        cpu = {"value": nb / dt, "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nb} of {B} requests (projection, SiLU, pooling, a_hat), float64 "
+                         f"NumPy, one process, {dt:.2f} s wall"}
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} requests/s")
     pkg.lib()
     dev = torch.device("cuda:0")
-    g = torch.Generator(device="cpu").manual_seed(20261202)
-    h = torch.randn(B, k, H, generator=g).to(torch.bfloat16).to(dev)
-    W1 = (torch.randn(Hf, H, generator=g) / H ** 0.5).to(torch.bfloat16).to(dev)
-    b1 = (torch.randn(Hf, generator=g) * 0.5).to(dev)
-    w2 = (torch.randn(Hf, generator=g) * 3 / Hf ** 0.5).to(dev)
+    h, W1, b1, w2 = h_c.to(dev), W1_c.to(dev), b1_c.to(dev), w2_c.to(dev)
     ws = pkg.alloc_workspace(int(pkg.lib().sv_length_head_workspace_size(B, k, H, Hf)), dev)
     out = {"a_hat": torch.empty(B, device=dev), "k_hat": torch.empty(B, dtype=torch.int32, device=dev),
            "off_t": torch.empty(B + 1, dtype=torch.int32, device=dev)}
@@ -323,7 +377,7 @@ def bench_length_head(args):
                      "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
         "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 2),
         "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
