@@ -19,6 +19,9 @@ Sources (cited by page title and section):
   speculative-decoding recipe (normalised residual max(0, p - q)); Algorithm 2
   (entry-wise clipped reverse-KL); the complete numeric example for one toy
   position.
+* "D3D: Decoupled Diffusion Drafting for Asynchronous Speculative Decoding" review page --
+  Methodology, inference paragraph (prepared successor blocks, the packed budget
+  B((C - 1) F + 2), cache hits on a matching verified prefix).
 * "DFlash: Block Diffusion for Flash Speculative Decoding" notes
   (zhangshuibai.github.io) -- Section 3.1 step 6 (a bonus token when every draft
   is accepted, m + 1 tokens per round); Section 5.2 (rejection sampling with the
@@ -66,3 +69,4 @@ from .length_head import (  # noqa: F401
     truncate,
     truncation_margin,
 )
+from .branch import branch_lookup, final_tokens  # noqa: F401
