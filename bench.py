@@ -382,13 +382,84 @@ def bench_length_head(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_branch(args):
+    """The prepared-branch lookup after verification at the high-concurrency shape (B=128,
+    k=15) with D3D's main budget shape (coverage 12, fan-out 2: 24 keys per request), on
+    seeded synthetic verification outcomes."""
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+
+    B, k_max, n_branch = 128, 15, 24
+    rng = np.random.default_rng(20261202)
+    k = np.full(B, k_max, dtype=np.int32)
+    al = rng.integers(0, k_max + 1, size=B).astype(np.int32)
+    out = rng.integers(0, 151936, size=B * (k_max + 1)).astype(np.int32)
+    pos = rng.integers(0, k_max + 1, size=(B, n_branch)).astype(np.int32)
+    tok = rng.integers(-1, 151936, size=(B, n_branch)).astype(np.int32)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            oracle.branch_lookup(al, oracle.final_tokens(out, al, k), pos, tok)
+        dt = (time.perf_counter() - t0) / reps
+        cpu = {"value": B / dt, "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"all {B} requests, {n_branch} keys each, {reps} repetitions, one "
+                         f"process, {dt * 1e3:.2f} ms per call"}
+    pkg.lib()
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(v).to(dev) for n, v in
+         (("k", k), ("al", al), ("out", out), ("pos", pos), ("tok", tok))}
+
+    def step():
+        pkg.branch_lookup(t["k"], t["al"], t["out"], t["pos"], t["tok"], k_max=k_max)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
+    nbytes = 4 * (2 * B + B + 2 * B * n_branch + B)  # k, a_b, the emitted token, keys, hit
+    us = kernels["sv_branch"]
+    res = {
+        "metric": "prepared-branch lookups/sec after verification (requests)",
+        "value": round(B / (ms_per_step * 1e-3), 1), "unit": "requests/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic (seeded verification outcomes and keys)",
+        "config": {"workload": "branch lookup: B=128 k=15, 24 keys per request", "op": "branch",
+                   "B": B, "k": k_max, "n_branch": n_branch, "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 6), "traffic": None},
+        "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad", "length_head"),
+    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad", "length_head", "branch"),
                     default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
@@ -422,6 +493,8 @@ def main():
 
     if args.op == "length_head":
         return bench_length_head(args)
+    if args.op == "branch":
+        return bench_branch(args)
     t0 = time.perf_counter()
     w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")

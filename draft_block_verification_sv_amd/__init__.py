@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SV_F32,
     SpecVerifyError,
     alloc_workspace,
+    branch_lookup,
     clipped_rkl,
     lib,
     length_head,

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
                                    _c_p, _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p,
                                    _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_opd_loss_grad.restype = _c_i32
+    L.sv_branch_lookup.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                   _c_p, _c_p]
+    L.sv_branch_lookup.restype = _c_i32
     L.sv_status_string.argtypes = [_c_i32]
     L.sv_status_string.restype = ctypes.c_char_p
     L.sv_version.argtypes = []
@@ -300,6 +303,32 @@ def length_loss(a_hat: torch.Tensor, accept_len: torch.Tensor, k_hat: torch.Tens
     _check(lib().sv_length_loss(B, _ptr(a_hat), _ptr(accept_len), _ptr(k_hat), _ptr(loss),
                                 _ptr(dloss), _stream(stream)), "sv_length_loss")
     return loss, dloss
+
+
+def branch_lookup(k: torch.Tensor, accept_len: torch.Tensor, out_tokens: torch.Tensor,
+                  branch_pos: torch.Tensor, branch_tok: torch.Tensor, *, k_max: Optional[int] = None,
+                  stream=None) -> torch.Tensor:
+    """sv_branch_lookup: hit [B], the first prepared branch whose key (branch_pos, branch_tok;
+    int32 [B, n_branch], token -1 = any) matches the verification outcome (accept_len, the
+    token after the accepted drafts in the packed out_tokens), -1 for a miss."""
+    dev = k.device
+    B = int(k.numel())
+    if branch_pos.dim() != 2 or int(branch_pos.shape[0]) != B:
+        raise ValueError("branch_pos must be [B, n_branch]")
+    n_branch = int(branch_pos.shape[1])
+    _need(k, "k", torch.int32, B, dev)
+    _need(accept_len, "accept_len", torch.int32, B, dev)
+    _need(branch_pos, "branch_pos", torch.int32, B * n_branch, dev)
+    _need(branch_tok, "branch_tok", torch.int32, B * n_branch, dev)
+    n_tokens = int(out_tokens.numel())
+    _need(out_tokens, "out_tokens", torch.int32, n_tokens, dev)
+    if k_max is None:
+        k_max = int(k.max().item())
+    hit = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib().sv_branch_lookup(B, int(k_max), n_branch, n_tokens, _ptr(k), _ptr(accept_len),
+                                  _ptr(out_tokens), _ptr(branch_pos), _ptr(branch_tok), _ptr(hit),
+                                  _stream(stream)), "sv_branch_lookup")
+    return hit
 
 
 def _row_pair_shapes(target: torch.Tensor, draft: torch.Tensor,

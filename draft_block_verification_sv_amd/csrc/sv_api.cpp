@@ -17,13 +17,14 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 18;
+constexpr int kNumKernels = 19;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
-    "sv_head_pool",   "sv_head_out",     "sv_len_loss"};
+    "sv_head_pool",   "sv_head_out",     "sv_len_loss",
+    "sv_branch"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -42,7 +43,8 @@ enum {
   K_HEAD_FEAT,
   K_HEAD_POOL,
   K_HEAD_OUT,
-  K_LEN_LOSS
+  K_LEN_LOSS,
+  K_BRANCH
 };
 
 // ------------------------------------------------------------------ profiling
@@ -564,6 +566,30 @@ sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const 
     return SV_ERR_HIP;
   if (timed(K_HEAD_OUT, st, [&] { return sv::launch_head_out(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;
+  return SV_OK;
+}
+
+sv_status sv_branch_lookup(int32_t B, int32_t k_max, int32_t n_branch, int64_t n_tokens,
+                           const int32_t* k, const int32_t* accept_len, const int32_t* out_tokens,
+                           const int32_t* branch_pos, const int32_t* branch_tok, int32_t* hit,
+                           void* stream) {
+  if (B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || n_branch < 1 ||
+      n_branch > SV_MAX_BRANCHES || n_tokens < 1)
+    return SV_ERR_SHAPE;
+  if (!k || !accept_len || !out_tokens || !branch_pos || !branch_tok || !hit) return SV_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  sv::BranchArgs a{};
+  a.B = B;
+  a.k_max = k_max;
+  a.n_branch = n_branch;
+  a.n_tokens = n_tokens;
+  a.k = k;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.branch_pos = branch_pos;
+  a.branch_tok = branch_tok;
+  a.hit = hit;
+  if (timed(K_BRANCH, st, [&] { return sv::launch_branch(a, st); }) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -725,6 +725,62 @@ void sv_draw_kernel(SampleArgs a) {
   emit(tok);
 }
 
+// =========================================================================== branch lookup
+// After verification: which prepared successor block a request can reuse (D3D review page,
+// Methodology, inference paragraph: a verified prefix that matches a prepared branch is a
+// cache hit).  A branch is keyed by (accept length, token emitted after the accepted drafts),
+// token -1 matching any; the hit is the first matching branch in the request's list, -1 for
+// none.  A workgroup takes 16 requests, one wave each: the rows before its first request
+// (sum of k_c + 1 over valid lengths) by a reduction over k, then each wave reads its a_b,
+// the token at row off_t[b] + a_b, and compares 64 keys per step (ballot, lowest index).
+// A request with k_b or a_b out of range, or a row past n_tokens, gets -1.
+constexpr int kBranchWaves = 16;
+__global__ __launch_bounds__(64 * kBranchWaves) void sv_branch_kernel(BranchArgs a) {
+  __shared__ long long s_red[kBranchWaves];
+  __shared__ long long s_off[kBranchWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kBranchWaves;
+  auto rows_of = [&](int64_t c) -> long long {
+    const int kc = a.k[c];
+    return (kc >= 1 && kc <= a.k_max) ? kc + 1 : 0;
+  };
+  long long part = 0;
+  for (int64_t c = tid; c < b0; c += 64 * kBranchWaves) part += rows_of(c);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
+  if (lane == 0) s_red[wave] = part;
+  __syncthreads();
+  if (tid == 0) {
+    long long base = 0;
+    for (int w = 0; w < kBranchWaves; ++w) base += s_red[w];
+    for (int i = 0; i < kBranchWaves; ++i) {
+      s_off[i] = base;
+      if (b0 + i < a.B) base += rows_of(b0 + i);
+    }
+  }
+  __syncthreads();
+  const int64_t b = b0 + wave;
+  if (b >= a.B) return;
+  const int kb = a.k[b], al = a.accept_len[b];
+  const long long row = s_off[wave] + al;
+  int hit = -1;
+  if (kb >= 1 && kb <= a.k_max && al >= 0 && al <= kb && row < a.n_tokens) {
+    const int y = a.out_tokens[row];
+    const int32_t* pos = a.branch_pos + b * a.n_branch;
+    const int32_t* tok = a.branch_tok + b * a.n_branch;
+    for (int j0 = 0; j0 < a.n_branch; j0 += 64) {
+      const int j = j0 + lane;
+      const bool match = j < a.n_branch && pos[j] == al && (tok[j] == y || tok[j] == -1);
+      const uint64_t m = __ballot(match);
+      if (m) {
+        hit = j0 + __builtin_ctzll(m);
+        break;
+      }
+    }
+  }
+  if (lane == 0) a.hit[b] = hit;
+}
+
 // =========================================================================== launchers
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(sv_plan_kernel, dim3(1), dim3(1024), 0, st, a);
@@ -760,6 +816,12 @@ hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& 
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status,
                          hipStream_t st) {
   hipLaunchKernelGGL(sv_status_kernel, dim3(1), dim3(256), 0, st, row_flags, n, device_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_branch(const BranchArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.B + kBranchWaves - 1) / kBranchWaves));
+  hipLaunchKernelGGL(sv_branch_kernel, grid, dim3(64 * kBranchWaves), 0, st, a);
   return hipGetLastError();
 }
 

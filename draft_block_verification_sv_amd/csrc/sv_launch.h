@@ -170,4 +170,18 @@ hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_st
 hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t st);
 hipError_t launch_draw(int dtype, bool vec, const SampleArgs& a, hipStream_t st);
 
+// Lookup of a prepared successor block after verification.
+struct BranchArgs {
+  int64_t B;
+  int32_t k_max, n_branch;
+  int64_t n_tokens;
+  const int32_t* k;
+  const int32_t* accept_len;
+  const int32_t* out_tokens;
+  const int32_t* branch_pos;  // [B, n_branch]
+  const int32_t* branch_tok;  // [B, n_branch]
+  int32_t* hit;               // [B]
+};
+hipError_t launch_branch(const BranchArgs& a, hipStream_t st);
+
 }  // namespace sv

@@ -89,6 +89,7 @@ enum {
 #define SV_MAX_BATCH 65536   /* B <= 65536                                   */
 #define SV_MAX_VOCAB (1 << 19) /* 524288 */
 #define SV_MAX_HEAD_FEATURES 4096 /* H' of the length head */
+#define SV_MAX_BRANCHES 4096 /* prepared successor blocks per request */
 
 /* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
  * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */
@@ -277,6 +278,36 @@ sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const 
  */
 sv_status sv_length_loss(int32_t B, const float* a_hat, const int32_t* accept_len,
                          const int32_t* k_hat, float* loss, float* dloss, void* stream);
+
+/*
+ * sv_branch_lookup: which prepared successor block each request can reuse after verification
+ * (review page "D3D: Decoupled Diffusion Drafting for Asynchronous Speculative Decoding",
+ * Methodology, inference paragraph: while the target verifies, a drafter pass prepares blocks
+ * for selected rejection positions and the full-acceptance case; a verified prefix that
+ * matches a prepared branch is a cache hit and reuses it).
+ * A branch is keyed by the verification outcome that fixes the next prefix: the accept length
+ * (0..k_b; k_b = every draft accepted) and the token emitted after the accepted drafts (the
+ * residual draw, the greedy replacement or the bonus token); a key token of -1 matches any.
+ * hit[b] is the first branch j, in list order, with branch_pos[b, j] == accept_len[b] and
+ * branch_tok[b, j] in {that token, -1}; -1 for a miss.
+ *
+ *   B, k_max        requests; upper bound on every k_b (1..SV_MAX_K).
+ *   n_branch        keys per request (1..SV_MAX_BRANCHES), row-major [B, n_branch] arrays.
+ *   n_tokens        length of out_tokens, sum_b (k_b + 1).
+ *   k, accept_len   int32 [B]: the lengths and accept lengths of the verification call.
+ *   out_tokens      int32 [n_tokens]: its packed output (request b at rows
+ *                   sum_{c<b} (k_c + 1) .. + k_b).
+ *   branch_pos, branch_tok   int32 [B, n_branch]: the prepared keys.
+ *   hit             int32 [B] (out).
+ * All pointers are device memory owned by the caller; nothing is allocated.  A request whose
+ * k_b or accept length is out of range (e.g. -1 from an invalid verification), or whose row
+ * falls past n_tokens, gets -1.  Shape and NULL errors return synchronously; otherwise the work
+ * is enqueued on `stream`.
+ */
+sv_status sv_branch_lookup(int32_t B, int32_t k_max, int32_t n_branch, int64_t n_tokens,
+                           const int32_t* k, const int32_t* accept_len, const int32_t* out_tokens,
+                           const int32_t* branch_pos, const int32_t* branch_tok, int32_t* hit,
+                           void* stream);
 
 /* Static text for a status code. */
 const char* sv_status_string(sv_status s);

@@ -180,3 +180,18 @@ def test_length_head_argument_errors(L):
     assert L.sv_length_head_workspace_size(4, 15, 48, 256) == 0
     assert L.sv_length_loss(0, 8, 8, 8, 8, None, None) == 2
     assert L.sv_length_loss(2, None, 8, 8, 8, None, None) == 1
+
+
+def test_branch_lookup_argument_errors(L):
+    def call(B=2, k_max=15, n_branch=24, n_tokens=32, k=16, al=16, out=16, pos=16, tok=16, hit=16):
+        return L.sv_branch_lookup(B, k_max, n_branch, n_tokens, k, al, out, pos, tok, hit, None)
+
+    assert call(B=0) == 2
+    assert call(k_max=65) == 2
+    assert call(n_branch=0) == 2
+    assert call(n_branch=4097) == 2
+    assert call(n_tokens=0) == 2
+    assert call(k=None) == 1
+    assert call(out=None) == 1
+    assert call(tok=None) == 1
+    assert call(hit=None) == 1
