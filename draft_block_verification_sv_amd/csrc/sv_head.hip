@@ -5,8 +5,8 @@
 //   sv_head_feat   the projection z = W1 h^T as a split-K GEMM on v_mfma_f32_16x16x32_bf16.
 //                  A request's positions form ceil(k / 16) blocks of 16 rows; a workgroup
 //                  takes four blocks (one per wave) against one 64-feature tile (four MFMA
-//                  tiles) over one K-chunk, four K steps of loads in flight, and writes the
-//                  fp32 partial sums of that chunk.
+//                  tiles) over one K-chunk, staged through LDS 32 columns at a time with
+//                  several stages in flight, and writes the fp32 partial sums of that chunk.
 //   sv_head_pool   one workgroup per request: z = sum of the K-chunks' partials in chunk order
 //                  + b1, SiLU, the mean over the k positions, a_hat = sigmoid(w2 . pooled + b2)
 //                  (fp64 dot, fixed combination order) and k_hat = clamp(floor(a_hat gamma k),
@@ -41,63 +41,103 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& w) {
   return v;
 }
 
-#ifndef SV_HEAD_UNROLL
-#define SV_HEAD_UNROLL 8
-#endif
-constexpr int kHeadUnroll = SV_HEAD_UNROLL;  // K steps whose loads are in flight together
+constexpr int kHeadStages = 8;  // 32-column K stages whose loads are in flight
+constexpr int kLdsRow = 32 + 8;  // bf16 per LDS row: one K stage plus 16 B of padding
 
-// One workgroup: blocks 4 g .. 4 g + 3 (wave w takes block 4 g + w), features n0 .. n0 + 63,
-// K-chunk c.  Writes partial[((c NB + blk) 16 + row) H' + n] for n < H'.
+__device__ __forceinline__ void fetch_stage(uint4& ra, uint4& rb, const uint16_t* gA,
+                                            const uint16_t* gB, int col) {
+  ra = *reinterpret_cast<const uint4*>(gA + col);
+  rb = *reinterpret_cast<const uint4*>(gB + col);
+}
+
+// One workgroup: blocks 4 g .. 4 g + 3 (64 rows; wave w computes block 4 g + w), features
+// n0 .. n0 + 63, K-chunk c, in stages of 32 columns.  Each thread copies one 16-byte piece of
+// the A stage (row tid / 4) and one of the B stage (feature row tid / 4): the 64 rows x 64
+// bytes of a stage are read in full 64-byte runs.  kHeadStages stages are in flight in
+// registers; a stage is written to one of two LDS buffers (rows padded to 80 bytes, so the
+// 16 rows a fragment read touches fall on distinct banks), the workgroup barrier publishes it,
+// the next stage's loads are issued, and each wave reads its A fragment and four B
+// fragments from LDS for four MFMAs.  Stage indices past the chunk are clamped (the last
+// stage again, from cache; never used).  Writes partial[((c NB + blk) 16 + row) H' + n].
 __global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs a) {
+  __shared__ __align__(16) uint16_t sA[2][64 * kLdsRow];
+  __shared__ __align__(16) uint16_t sB[2][64 * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + wave;
   const int64_t n_rows = a.B * static_cast<int64_t>(a.k);
-  const int r = lane & 15, kg = (lane >> 4) * 8;  // operand row / column, k offset
-  // this lane's A row: position 16 j + r of request b (clamped in bounds, see above)
-  const int64_t b = blk / a.R;
-  const int pos = static_cast<int>(blk - b * a.R) * 16 + r;
-  int64_t hrow = b * a.k + pos;
-  if (pos >= a.k || hrow >= n_rows) hrow = n_rows - 1;
-  const uint16_t* Hrow = static_cast<const uint16_t*>(a.h) + hrow * a.ld_h + kg;
+  // this thread's copy piece: row cr of the stage, 16 bytes at column cc
+  const int cr = tid >> 2, cc = (tid & 3) * 8;
+  const int64_t cblk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + cr / 16;
+  const int64_t cb = cblk / a.R;
+  const int cpos = static_cast<int>(cblk - cb * a.R) * 16 + (cr & 15);
+  int64_t hrow = cb * a.k + cpos;
+  if (cpos >= a.k || hrow >= n_rows) hrow = n_rows - 1;  // clamped: row never used
   const int n0 = blockIdx.y * kHeadTileN;
-  const uint16_t* Wrow[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = min(n0 + 16 * t + r, a.Hf - 1);
-    Wrow[t] = static_cast<const uint16_t*>(a.W1) + static_cast<int64_t>(n) * a.ld_w + kg;
-  }
+  const int wrow = min(n0 + cr, a.Hf - 1);                 // clamped: column never stored
+  const uint16_t* gA = static_cast<const uint16_t*>(a.h) + hrow * a.ld_h + cc;
+  const uint16_t* gB = static_cast<const uint16_t*>(a.W1) + static_cast<int64_t>(wrow) * a.ld_w + cc;
+  const int lds_w = cr * kLdsRow + cc;
+  // this lane's fragment reads: row r of its wave's block / of each feature tile, k offset kg
+  const int r = lane & 15, kg = (lane >> 4) * 8;
+  const int ldsA = (wave * 16 + r) * kLdsRow + kg;
+  const int ldsB = r * kLdsRow + kg;
+
   const int c = blockIdx.z;
   const int steps = a.H / 32;
-  const int k_lo = 32 * ((c * steps) / a.S);
-  const int k_hi = 32 * (((c + 1) * steps) / a.S);
+  const int s_lo = (c * steps) / a.S, s_hi = ((c + 1) * steps) / a.S;
+  const int n_st = s_hi - s_lo;
   f32x4_t acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int kk = k_lo;
-  for (; kk + 32 * kHeadUnroll <= k_hi; kk += 32 * kHeadUnroll) {
-    uint4 av[kHeadUnroll], bv[4][kHeadUnroll];
-#pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u) {
-      av[u] = *reinterpret_cast<const uint4*>(Hrow + kk + 32 * u);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bv[t][u] = *reinterpret_cast<const uint4*>(Wrow[t] + kk + 32 * u);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before the MFMAs
-#pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[t][u]),
-                                                         acc[t], 0, 0, 0);
+  // the ring of stages in flight, as named registers (an array here would live in scratch)
+  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
+#define SV_HEAD_COL(st) (32 * (s_lo + min((st), n_st - 1)))
+  fetch_stage(ra0, rb0, gA, gB, SV_HEAD_COL(0));
+  fetch_stage(ra1, rb1, gA, gB, SV_HEAD_COL(1));
+  fetch_stage(ra2, rb2, gA, gB, SV_HEAD_COL(2));
+  fetch_stage(ra3, rb3, gA, gB, SV_HEAD_COL(3));
+  fetch_stage(ra4, rb4, gA, gB, SV_HEAD_COL(4));
+  fetch_stage(ra5, rb5, gA, gB, SV_HEAD_COL(5));
+  fetch_stage(ra6, rb6, gA, gB, SV_HEAD_COL(6));
+  fetch_stage(ra7, rb7, gA, gB, SV_HEAD_COL(7));
+  // stage i: publish it in LDS buffer i % 2, refill its ring slot with stage i + 8, then
+  // four MFMAs from LDS.  Full rounds of eight stages run without a condition (a load under a
+  // branch would make the wait at the join count the refills too); the last partial round is
+  // guarded by its stage index, uniform across the workgroup.
+#define SV_HEAD_STEP(J)                                                                     \
+  {                                                                                         \
+    *reinterpret_cast<uint4*>(&sA[(J) & 1][lds_w]) = ra##J;                                 \
+    *reinterpret_cast<uint4*>(&sB[(J) & 1][lds_w]) = rb##J;                                 \
+    __syncthreads();                                                                        \
+    fetch_stage(ra##J, rb##J, gA, gB, SV_HEAD_COL(i0 + (J) + kHeadStages));                 \
+    const uint4 av = *reinterpret_cast<const uint4*>(&sA[(J) & 1][ldsA]);                   \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+      const uint4 bv = *reinterpret_cast<const uint4*>(&sB[(J) & 1][ldsB + t * 16 * kLdsRow]); \
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0); \
+    }                                                                                       \
   }
-  for (; kk < k_hi; kk += 32) {
-    const uint4 av = *reinterpret_cast<const uint4*>(Hrow + kk);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint4 bv = *reinterpret_cast<const uint4*>(Wrow[t] + kk);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
-    }
+  int i0 = 0;
+  for (; i0 + kHeadStages <= n_st; i0 += kHeadStages) {
+    SV_HEAD_STEP(0)
+    SV_HEAD_STEP(1)
+    SV_HEAD_STEP(2)
+    SV_HEAD_STEP(3)
+    SV_HEAD_STEP(4)
+    SV_HEAD_STEP(5)
+    SV_HEAD_STEP(6)
+    SV_HEAD_STEP(7)
   }
+  if (i0 < n_st) {
+    SV_HEAD_STEP(0)
+    if (i0 + 1 < n_st) SV_HEAD_STEP(1)
+    if (i0 + 2 < n_st) SV_HEAD_STEP(2)
+    if (i0 + 3 < n_st) SV_HEAD_STEP(3)
+    if (i0 + 4 < n_st) SV_HEAD_STEP(4)
+    if (i0 + 5 < n_st) SV_HEAD_STEP(5)
+    if (i0 + 6 < n_st) SV_HEAD_STEP(6)
+  }
+#undef SV_HEAD_STEP
+#undef SV_HEAD_COL
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + wave;
   if (blk >= a.NB) return;
   // lane holds D[4 (l/16) + i][l % 16] of each feature tile t
   float* P = a.partial + ((static_cast<int64_t>(c) * a.NB + blk) * 16 + 4 * (lane >> 4)) * a.Hf;
