@@ -17,13 +17,13 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 19;
+constexpr int kNumKernels = 18;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
-    "sv_head_pool",   "sv_head_out",     "sv_len_loss",
+    "sv_head_pool",   "sv_len_loss",
     "sv_branch"};
 enum {
   K_PLAN,
@@ -42,7 +42,6 @@ enum {
   K_GREEDY_PICK,
   K_HEAD_FEAT,
   K_HEAD_POOL,
-  K_HEAD_OUT,
   K_LEN_LOSS,
   K_BRANCH
 };
@@ -530,7 +529,7 @@ bool head_shape_ok(int32_t B, int32_t k, int32_t H, int32_t H_feat) {
 
 size_t sv_length_head_workspace_size(int32_t B, int32_t k, int32_t H, int32_t H_feat) {
   if (!head_shape_ok(B, k, H, H_feat)) return 0;
-  return (sv::head_partial_bytes(sv::head_split(B, k, H, H_feat)) + 255) & ~size_t(255);
+  return sv::head_workspace_bytes(sv::head_split(B, k, H, H_feat));
 }
 
 sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const void* h,
@@ -557,14 +556,13 @@ sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const 
   ha.b2 = b2;
   ha.gamma = gamma;
   ha.partial = static_cast<float*>(workspace);
+  ha.ticket = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + sv::head_ticket_offset(ha));
   ha.a_hat = a_hat;
   ha.k_hat = k_hat;
   ha.off_t = off_t;
   if (timed(K_HEAD_FEAT, st, [&] { return sv::launch_head(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;
   if (timed(K_HEAD_POOL, st, [&] { return sv::launch_head_pool(ha, st); }) != hipSuccess)
-    return SV_ERR_HIP;
-  if (timed(K_HEAD_OUT, st, [&] { return sv::launch_head_out(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

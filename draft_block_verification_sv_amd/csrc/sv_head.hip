@@ -10,9 +10,8 @@
 //   sv_head_pool   one workgroup per request: z = sum of the K-chunks' partials in chunk order
 //                  + b1, SiLU, the mean over the k positions, a_hat = sigmoid(w2 . pooled + b2)
 //                  (fp64 dot, fixed combination order) and k_hat = clamp(floor(a_hat gamma k),
-//                  1, k) in fp64.
-//   sv_head_out    one workgroup: the packed target-row offsets
-//                  off_t[b] = sum_{c<b} (k_hat_c + 1).
+//                  1, k) in fp64; the workgroup that finishes last writes the packed
+//                  target-row offsets off_t[b] = sum_{c<b} (k_hat_c + 1).
 //   sv_len_loss    l_len_b = (a_hat_b - a_b / k_hat_b)^2 and its derivative in a_hat.
 //
 // MFMA lane layout of the 16x16x32 bf16 instruction (checked on the device): lane l holds
@@ -81,6 +80,7 @@ __global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs
   const int ldsA = (wave * 16 + r) * kLdsRow + kg;
   const int ldsB = r * kLdsRow + kg;
 
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *a.ticket = 0;
   const int c = blockIdx.z;
   const int steps = a.H / 32;
   const int s_lo = (c * steps) / a.S, s_hi = ((c + 1) * steps) / a.S;
@@ -150,39 +150,87 @@ __global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs
   }
 }
 
-// One workgroup per request: thread t takes features t, t + 256, ...; z summed over the
-// K-chunks in order, then + b1, SiLU and the sum over the k positions; the dot with w2 in fp64
-// over the thread's features, then over the threads in a fixed order.  The partials of four
-// positions (every K-chunk, up to kHeadMaxSplit) are loaded before any is used; indices past k
-// or S are clamped in bounds and their values dropped, so no load sits under a branch.
+// s_waitcnt operand that waits for every outstanding vector memory operation of the wave
+// (vmcnt = 0) and leaves the export and LDS/scalar counters at their maxima (gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Fixed-order exclusive scan of k_hat + 1 over all requests by one 256-thread workgroup: each
+// thread sums a contiguous run of requests, the run totals are scanned in thread order, then
+// each thread writes its run's offsets.  k_hat is read with device-scope loads (it was written
+// by other workgroups of the same launch).
+__device__ void head_offsets(const HeadArgs& a, int* s_tot) {
+  const int tid = threadIdx.x;
+  const int64_t per = (a.B + 255) / 256;
+  const int64_t lo = min<int64_t>(a.B, tid * per), hi = min<int64_t>(a.B, lo + per);
+  int tot = 0;
+  for (int64_t b = lo; b < hi; ++b)
+    tot += __hip_atomic_load(a.k_hat + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  s_tot[tid] = tot;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = s_tot[t];
+      s_tot[t] = run;
+      run += v;
+    }
+    a.off_t[a.B] = run;
+  }
+  __syncthreads();
+  int off = s_tot[tid];
+  for (int64_t b = lo; b < hi; ++b) {
+    a.off_t[b] = off;
+    off += __hip_atomic_load(a.k_hat + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  }
+}
+
+// One workgroup per request: thread t takes features t, t + 256, ...; for each, the partials
+// of 32 / SP positions x SP chunk slots (SP = 4 when S <= 4, else 8) are loaded before any is
+// used, indices past k or S clamped in bounds and their values dropped, so no load sits under
+// a branch; z of a position is the sum of its chunks in chunk order, then + b1, SiLU, summed
+// over the positions.  The dot with w2 is taken in fp64 over the thread's features, then over
+// the threads in a fixed order.  With off_t, the workgroup that takes the last ticket of the
+// launch (a device-scope counter the projection kernel zeroes) scans k_hat into the packed
+// offsets; k_hat goes out as device-scope stores before the ticket.
+template <int SP>
+__device__ __forceinline__ float pool_feature(const HeadArgs& a, int64_t b, int n, float bias,
+                                              int64_t chunk_stride) {
+  constexpr int RP = 32 / SP;  // positions per round
+  float colsum = 0.0f;
+  for (int i0 = 0; i0 < a.k; i0 += RP) {
+    float v[RP][SP];
+#pragma unroll
+    for (int ii = 0; ii < RP; ++ii) {
+      const int i = min(i0 + ii, a.k - 1);
+      const float* P = a.partial + ((b * a.R + i / 16) * 16 + (i % 16)) * a.Hf + n;
+#pragma unroll
+      for (int c = 0; c < SP; ++c) v[ii][c] = P[min(c, a.S - 1) * chunk_stride];
+    }
+#pragma unroll
+    for (int ii = 0; ii < RP; ++ii) {
+      float z = 0.0f;
+#pragma unroll
+      for (int c = 0; c < SP; ++c)
+        if (c < a.S) z += v[ii][c];
+      z += bias;
+      if (i0 + ii < a.k) colsum += z / (1.0f + __expf(-z));
+    }
+  }
+  return colsum;
+}
+
 __global__ __launch_bounds__(256) void sv_head_pool_kernel(HeadArgs a) {
   __shared__ double s_w[4];
+  __shared__ int s_tot[256];
+  __shared__ int s_last;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t chunk_stride = a.NB * 16 * static_cast<int64_t>(a.Hf);
   double dot = 0.0;
   for (int n = tid; n < a.Hf; n += 256) {
     const float bias = a.b1 ? a.b1[n] : 0.0f;
-    float colsum = 0.0f;
-    for (int i0 = 0; i0 < a.k; i0 += 4) {
-      float v[4][kHeadMaxSplit];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = min(i0 + ii, a.k - 1);
-        const float* P = a.partial + ((b * a.R + i / 16) * 16 + (i % 16)) * a.Hf + n;
-#pragma unroll
-        for (int c = 0; c < kHeadMaxSplit; ++c) v[ii][c] = P[min(c, a.S - 1) * chunk_stride];
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float z = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kHeadMaxSplit; ++c)
-          if (c < a.S) z += v[ii][c];
-        z += bias;
-        if (i0 + ii < a.k) colsum += z / (1.0f + __expf(-z));
-      }
-    }
+    const float colsum = a.S <= 4 ? pool_feature<4>(a, b, n, bias, chunk_stride)
+                                  : pool_feature<kHeadMaxSplit>(a, b, n, bias, chunk_stride);
     const float pooled = colsum / static_cast<float>(a.k);
     dot += static_cast<double>(pooled) * static_cast<double>(a.w2[n]);
   }
@@ -195,44 +243,16 @@ __global__ __launch_bounds__(256) void sv_head_pool_kernel(HeadArgs a) {
     double t = floor(ah * static_cast<double>(a.gamma) * static_cast<double>(a.k));
     t = t < 1.0 ? 1.0 : (t > a.k ? static_cast<double>(a.k) : t);
     a.a_hat[b] = static_cast<float>(ah);
-    a.k_hat[b] = static_cast<int>(t);
+    __hip_atomic_store(a.k_hat + b, static_cast<int>(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.off_t) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // k_hat is out before the ticket
+      s_last = (__hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                a.B - 1) ? 1 : 0;
+    }
   }
-}
-
-__device__ __forceinline__ int block_excl_scan_1024_head(int v, int* lds_waves, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(x, d, 64);
-    if (lane >= d) x += o;
-  }
-  if (lane == 63) lds_waves[wave] = x;
+  if (!a.off_t) return;
   __syncthreads();
-  int base = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) base += lds_waves[w];
-    tot += lds_waves[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
-// One workgroup: the fixed-order scan of k_hat + 1 gives the packed offsets.
-__global__ __launch_bounds__(1024) void sv_head_out_kernel(HeadArgs a) {
-  __shared__ int s_waves[16];
-  const int tid = threadIdx.x;
-  int carry = 0;
-  for (int64_t base = 0; base < a.B; base += 1024) {
-    const int64_t b = base + tid;
-    const int kh = b < a.B ? a.k_hat[b] : 0;
-    int total = 0;
-    const int excl = block_excl_scan_1024_head(b < a.B ? kh + 1 : 0, s_waves, &total);
-    if (b < a.B) a.off_t[b] = carry + excl;
-    carry += total;
-  }
-  if (tid == 0) a.off_t[a.B] = carry;
+  if (s_last) head_offsets(a, s_tot);
 }
 
 __global__ __launch_bounds__(256) void sv_len_loss_kernel(int64_t B, const float* a_hat,
@@ -258,12 +278,6 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
 
 hipError_t launch_head_pool(const HeadArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(sv_head_pool_kernel, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_head_out(const HeadArgs& a, hipStream_t st) {
-  if (!a.off_t) return hipSuccess;
-  hipLaunchKernelGGL(sv_head_out_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

@@ -129,6 +129,7 @@ struct HeadArgs {
   int64_t NB;       // blocks in all: B R
   int32_t S;        // K-chunks of the split-K projection
   float* partial;   // workspace [S][NB * 16][Hf]: the chunks' partial sums of W1 h^T
+  int32_t* ticket;  // workspace: pooling workgroups done (zeroed by the projection kernel)
   float* a_hat;     // [B]
   int32_t* k_hat;   // [B]
   int32_t* off_t;   // [B + 1] or null
@@ -161,9 +162,11 @@ inline HeadArgs head_split(int64_t B, int32_t k, int32_t H, int32_t Hf) {
 inline size_t head_partial_bytes(const HeadArgs& a) {
   return static_cast<size_t>(a.S) * static_cast<size_t>(a.NB) * 16 * static_cast<size_t>(a.Hf) * sizeof(float);
 }
+// Workspace: the partial sums, then (256-byte aligned) the pooling ticket.
+inline size_t head_ticket_offset(const HeadArgs& a) { return (head_partial_bytes(a) + 255) & ~size_t(255); }
+inline size_t head_workspace_bytes(const HeadArgs& a) { return head_ticket_offset(a) + 256; }
 hipError_t launch_head(const HeadArgs& a, hipStream_t st);
 hipError_t launch_head_pool(const HeadArgs& a, hipStream_t st);
-hipError_t launch_head_out(const HeadArgs& a, hipStream_t st);
 hipError_t launch_len_loss(int64_t B, const float* a_hat, const int32_t* accept_len,
                            const int32_t* k_hat, float* loss, float* dloss, hipStream_t st);
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status, hipStream_t st);
