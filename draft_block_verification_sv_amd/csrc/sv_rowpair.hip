@@ -979,29 +979,46 @@ __device__ __forceinline__ void stream_max(const void* prow, int V, int n_slices
   const int n_full = V / kSlice;
   int s = wave;
   if constexpr (DT == 0 && VEC) {
-    const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
-    PackedRow ra, rb;
-    if (s < n_full) ra.load(P + static_cast<int64_t>(s) * kSlice);
-    while (s < n_full) {
-      const int s2 = s + kRowWaves;
-      if (s2 < n_full) rb.load(P + static_cast<int64_t>(s2) * kSlice);
-      float m = ra.max();
+    // Four slices in flight through bounds-checked buffer loads (past the row's last full
+    // slice they read zeros without touching memory).  Every round takes four slices and
+    // refills four, with one exit at the bottom: a slice past the row counts as -inf through a
+    // select, so no load sits under a branch and no wait has to cover a refill.  Each refill
+    // is pinned where it stands (the compiler would otherwise sink it next to its use).
+    const __amdgpu_buffer_rsrc_t RP = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(prow), 0, n_full * kSlice * 2, kBufWord3);
+    const int lane_off = lane * 16;
+    auto at = [&](int sl) { return lane_off + sl * (kSlice * 2); };
+    auto pin = [] { asm volatile("" ::: "memory"); };
+    auto take = [&](const PackedRow& r, int sl) {
+      const float m = sl < n_full ? r.max() : -INFINITY;
       if (m > best) {
         best = m;
-        best_s = s;
+        best_s = sl;
       }
-      if (s2 >= n_full) {
-        s = s2;
-        break;
-      }
-      const int s3 = s2 + kRowWaves;
-      if (s3 < n_full) ra.load(P + static_cast<int64_t>(s3) * kSlice);
-      m = rb.max();
-      if (m > best) {
-        best = m;
-        best_s = s2;
-      }
-      s = s3;
+    };
+    PackedRow r0, r1, r2, r3;
+    if (s < n_full) {
+      r0.load(RP, at(s));
+      r1.load(RP, at(s + kRowWaves));
+      r2.load(RP, at(s + 2 * kRowWaves));
+      r3.load(RP, at(s + 3 * kRowWaves));
+      do {
+        take(r0, s);
+        r0.load(RP, at(s + 4 * kRowWaves));
+        pin();
+        take(r1, s + kRowWaves);
+        r1.load(RP, at(s + 5 * kRowWaves));
+        pin();
+        take(r2, s + 2 * kRowWaves);
+        r2.load(RP, at(s + 6 * kRowWaves));
+        pin();
+        take(r3, s + 3 * kRowWaves);
+        r3.load(RP, at(s + 7 * kRowWaves));
+        pin();
+        s += 4 * kRowWaves;
+      } while (s < n_full);
+      // s is now the first slice index of this wave past the full slices
+      s = n_full + ((wave - n_full) % kRowWaves + kRowWaves) % kRowWaves;
     }
   }
   for (; s < n_slices; s += kRowWaves) {
