@@ -70,3 +70,4 @@ from .length_head import (  # noqa: F401
     truncation_margin,
 )
 from .branch import branch_lookup, final_tokens  # noqa: F401
+from .tree import tree_valid, verify_tree_block, verify_tree_greedy  # noqa: F401
