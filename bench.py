@@ -453,13 +453,123 @@ def bench_branch(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_tree(args):
+    """Greedy verification of EAGLE-shaped draft trees (60 nodes each, the tree size the DFlash
+    notes quote) for 32 requests at V=151936 bf16: the argmax of every target row (root and
+    nodes), then the walk.  Seeded synthetic trees and logits whose row argmaxes follow a child's
+    token with probability 0.7."""
+    import numpy as np
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+    from synth import bf16_bits_from_f64
+
+    B, n_per, V = 32, 60, 151936
+    rng = np.random.default_rng(20261202)
+    parent, tokens, amax = [], [], []
+    for b in range(B):
+        par, tok = [], []
+        for j in range(n_per):
+            u = rng.random()
+            p = (j - 1) if u < 0.5 else (int(rng.integers(-1, j)) if u < 0.9 else -1)
+            used = {tok[i] for i in range(j) if par[i] == p}
+            t = int(rng.integers(0, V))
+            while t in used:
+                t = int(rng.integers(0, V))
+            par.append(p)
+            tok.append(t)
+        am = rng.integers(0, V, size=n_per + 1)
+        for j in reversed(range(n_per)):  # the first child's token wins
+            if rng.random() < 0.7:
+                am[par[j] + 1] = tok[j]
+        parent += par
+        tokens += tok
+        amax.append(am)
+    rows = B * (n_per + 1)
+    L = rng.normal(size=(rows, V)) * 2.0
+    r = 0
+    for am in amax:
+        for a in am:
+            L[r, a] = L[r].max() + 0.5
+            r += 1
+    bits = bf16_bits_from_f64(L)
+    del L
+    n = np.full(B, n_per, np.int32)
+    parent = np.array(parent, np.int32)
+    tokens = np.array(tokens, np.int32)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        nb = 8
+        t0 = time.perf_counter()
+        oracle.verify_tree_block(target=bits[: nb * (n_per + 1)], dtype="bf16", V=V,
+                                 n_nodes=n[:nb], parent=parent[: nb * n_per],
+                                 tokens=tokens[: nb * n_per])
+        dt = time.perf_counter() - t0
+        cpu = {"value": nb * n_per / dt, "unit": "tree nodes/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nb} of {B} requests ({nb * n_per} nodes), float64 NumPy, one process, "
+                         f"{dt:.2f} s wall"}
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} nodes/s")
+    pkg.lib()
+    dev = torch.device("cuda:0")
+    target = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    d = {k: torch.from_numpy(v).to(dev) for k, v in (("n", n), ("par", parent), ("tok", tokens))}
+    ws = pkg.alloc_workspace(int(pkg.lib().sv_tree_workspace_size(B, int(n.sum()))), dev)
+    out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "out_tokens": torch.empty(rows, dtype=torch.int32, device=dev),
+           "out_nodes": torch.empty(B * n_per, dtype=torch.int32, device=dev),
+           "device_status": torch.empty(1, dtype=torch.int32, device=dev)}
+
+    def step():
+        pkg.verify_tree_greedy(target, d["n"], d["par"], d["tok"], max_nodes=n_per, workspace=ws,
+                               out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(out["device_status"].item()) == 0
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    kernels = {name: 1e3 * ms / cnt for name, (cnt, ms) in kt.items()}
+    nbytes = rows * V * 2  # every target logit once
+    us = kernels["sv_tree_argmax"]
+    mean_len = float(out["accept_len"].float().mean().item())
+    res = {
+        "metric": "draft-tree nodes verified/sec, greedy (target rows only)",
+        "value": round(B * n_per / (ms_per_step * 1e-3), 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded trees and logits)",
+        "config": {"workload": "draft trees: B=32, 60 nodes each, V=151936 bf16", "op": "tree",
+                   "B": B, "nodes": n_per, "V": V, "bytes": nbytes, "mean_accept_len": mean_len},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels_us": {kk: round(v, 2) for kk, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad", "length_head", "branch"),
+    ap.add_argument("--op", choices=("verify", "greedy", "opd", "opd_grad", "length_head", "branch",
+                                         "tree"),
                     default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
@@ -495,6 +605,8 @@ def main():
         return bench_length_head(args)
     if args.op == "branch":
         return bench_branch(args)
+    if args.op == "tree":
+        return bench_tree(args)
     t0 = time.perf_counter()
     w = workload(args.workload)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     profile_reset,
     verify_block,
     verify_block_greedy,
+    verify_tree_greedy,
     version,
     workspace_size,
 )

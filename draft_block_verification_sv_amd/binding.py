@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
                                    _c_p, _c_p, _c_p, _c_f32, _c_f32, _c_p, _c_p, _c_p, _c_p,
                                    _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_opd_loss_grad.restype = _c_i32
+    L.sv_tree_workspace_size.argtypes = [_c_i32, _c_i64]
+    L.sv_tree_workspace_size.restype = _c_sz
+    L.sv_verify_tree_greedy.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                        _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.sv_verify_tree_greedy.restype = _c_i32
     L.sv_branch_lookup.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                    _c_p, _c_p]
     L.sv_branch_lookup.restype = _c_i32
@@ -329,6 +334,53 @@ def branch_lookup(k: torch.Tensor, accept_len: torch.Tensor, out_tokens: torch.T
                                   _ptr(out_tokens), _ptr(branch_pos), _ptr(branch_tok), _ptr(hit),
                                   _stream(stream)), "sv_branch_lookup")
     return hit
+
+
+def verify_tree_greedy(target: torch.Tensor, n_nodes: torch.Tensor, parent: torch.Tensor,
+                       tree_tokens: torch.Tensor, *, max_nodes: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                       stream=None) -> dict:
+    """sv_verify_tree_greedy: target [sum_b (n_b + 1), V] (bf16 or fp32, unit column stride;
+    request b's rows are its root then its nodes), n_nodes int32 [B], parent and tree_tokens
+    int32 [sum_b n_b].  Returns accept_len [B], out_tokens [sum_b (n_b + 1)], out_nodes
+    [sum_b n_b] and device_status [1]."""
+    dev = target.device
+    code = _dtype_code(target)
+    if target.dim() != 2 or target.stride(1) != 1:
+        raise ValueError("target must be a 2-D tensor with unit column stride")
+    B = int(n_nodes.numel())
+    n_tot = int(parent.numel())
+    V = int(target.shape[1])
+    if int(target.shape[0]) != n_tot + B:
+        raise ValueError("target must have sum_b (n_b + 1) rows")
+    _need(n_nodes, "n_nodes", torch.int32, B, dev)
+    _need(parent, "parent", torch.int32, n_tot, dev)
+    _need(tree_tokens, "tree_tokens", torch.int32, n_tot, dev)
+    if max_nodes is None:
+        max_nodes = int(n_nodes.max().item())
+    if workspace is None:
+        nbytes = int(lib().sv_tree_workspace_size(B, n_tot))
+        if nbytes == 0:
+            raise SpecVerifyError(f"invalid shape B={B} nodes={n_tot}")
+        workspace = alloc_workspace(nbytes, dev)
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty(n_tot + B, dtype=torch.int32, device=dev),
+               "out_nodes": torch.empty(n_tot, dtype=torch.int32, device=dev),
+               "device_status": torch.empty(1, dtype=torch.int32, device=dev)}
+    else:
+        _need(out["accept_len"], "accept_len", torch.int32, B, dev)
+        _need(out["out_tokens"], "out_tokens", torch.int32, n_tot + B, dev)
+        if out.get("out_nodes") is not None:
+            _need(out["out_nodes"], "out_nodes", torch.int32, n_tot, dev)
+        _need(out["device_status"], "device_status", torch.int32, 1, dev)
+    st = lib().sv_verify_tree_greedy(code, B, int(max_nodes), V, target.stride(0), n_tot,
+                                     _ptr(target), _ptr(n_nodes), _ptr(parent), _ptr(tree_tokens),
+                                     _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+                                     _ptr(out.get("out_nodes")), _ptr(out["device_status"]),
+                                     _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sv_verify_tree_greedy")
+    return out
 
 
 def _row_pair_shapes(target: torch.Tensor, draft: torch.Tensor,

@@ -17,14 +17,14 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 18;
+constexpr int kNumKernels = 20;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
     "sv_head_pool",   "sv_len_loss",
-    "sv_branch"};
+    "sv_branch",      "sv_tree_argmax",  "sv_tree_walk"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -43,7 +43,9 @@ enum {
   K_HEAD_FEAT,
   K_HEAD_POOL,
   K_LEN_LOSS,
-  K_BRANCH
+  K_BRANCH,
+  K_TREE_ARGMAX,
+  K_TREE_WALK
 };
 
 // ------------------------------------------------------------------ profiling
@@ -563,6 +565,63 @@ sv_status sv_length_head(int32_t B, int32_t k, int32_t H, int32_t H_feat, const 
   if (timed(K_HEAD_FEAT, st, [&] { return sv::launch_head(ha, st); }) != hipSuccess)
     return SV_ERR_HIP;
   if (timed(K_HEAD_POOL, st, [&] { return sv::launch_head_pool(ha, st); }) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+size_t sv_tree_workspace_size(int32_t B, int64_t n_nodes_total) {
+  if (B < 1 || B > SV_MAX_BATCH || n_nodes_total < B ||
+      n_nodes_total > static_cast<int64_t>(B) * SV_MAX_TREE_NODES)
+    return 0;
+  return ((static_cast<size_t>(n_nodes_total + B) * sizeof(int32_t)) + 255) & ~size_t(255);
+}
+
+sv_status sv_verify_tree_greedy(int32_t dtype, int32_t B, int32_t max_nodes, int64_t V,
+                                int64_t ld_target, int64_t n_nodes_total,
+                                const void* target_logits, const int32_t* n_nodes,
+                                const int32_t* parent, const int32_t* tree_tokens,
+                                int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                int32_t* device_status, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+  if (B < 1 || B > SV_MAX_BATCH || max_nodes < 1 || max_nodes > SV_MAX_TREE_NODES ||
+      !shape_ok(V, ld_target, ld_target) || n_nodes_total < B ||
+      n_nodes_total > static_cast<int64_t>(B) * max_nodes)
+    return SV_ERR_SHAPE;
+  if (!target_logits || !n_nodes || !parent || !tree_tokens || !accept_len || !out_tokens ||
+      !device_status)
+    return SV_ERR_NULL;
+  const size_t need = sv_tree_workspace_size(B, n_nodes_total);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
+    return SV_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* arg = static_cast<int32_t*>(workspace);
+  sv::ArgmaxArgs am{};
+  am.target = target_logits;
+  am.ld_t = ld_target;
+  am.V = static_cast<int32_t>(V);
+  am.n_slices = sv::n_slices_for(V);
+  am.n_rows = n_nodes_total + B;
+  am.arg = arg;
+  am.zero_status = device_status;
+  const bool vec = vec_ok(dtype, ld_target, target_logits);
+  if (timed(K_TREE_ARGMAX, st, [&] { return sv::launch_row_argmax(dtype, vec, am, st); }) !=
+      hipSuccess)
+    return SV_ERR_HIP;
+  sv::TreeArgs ta{};
+  ta.B = B;
+  ta.max_nodes = max_nodes;
+  ta.V = static_cast<int32_t>(V);
+  ta.n_nodes_total = n_nodes_total;
+  ta.n_nodes = n_nodes;
+  ta.parent = parent;
+  ta.tokens = tree_tokens;
+  ta.arg = arg;
+  ta.accept_len = accept_len;
+  ta.out_tokens = out_tokens;
+  ta.out_nodes = out_nodes;
+  ta.device_status = device_status;
+  if (timed(K_TREE_WALK, st, [&] { return sv::launch_tree_walk(ta, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

@@ -781,6 +781,137 @@ __global__ __launch_bounds__(64 * kBranchWaves) void sv_branch_kernel(BranchArgs
   if (lane == 0) a.hit[b] = hit;
 }
 
+// =========================================================================== tree walk
+// Greedy verification of a draft tree per request (DFlash notes, Sections 5.1-5.2; AdaFlash
+// paper, Appendix B.1), after sv_row_argmax has written the argmax of every target row (the
+// root's row and one per node).  A workgroup takes 16 requests, one wave each.  Every workgroup
+// checks the whole call (each n_b in [1, max_nodes], sum n_b = n_nodes_total) and sums n_c over
+// the requests before its own for their first node and row.  A wave keeps its request's
+// parents and tokens in registers (16 per lane), checks them (a parent must be -1 or an earlier
+// node; a token must lie in [0, V)), then walks: from the root, the lowest-index child whose
+// token is the current row's argmax (a wave minimum), until no child matches; that node's
+// argmax is the final token.  device_status was zeroed by the argmax kernel; bits are OR-ed in.
+constexpr int kTreeWaves = 16;
+constexpr int kTreeMaxNodes = 1024;  // SV_MAX_TREE_NODES
+constexpr int kTreePerLane = kTreeMaxNodes / 64;
+__global__ __launch_bounds__(64 * kTreeWaves) void sv_tree_walk_kernel(TreeArgs a) {
+  __shared__ int s_args[kTreeWaves * (kTreeMaxNodes + 1)];
+  __shared__ long long s_before[kTreeWaves], s_total[kTreeWaves];
+  __shared__ int s_bad[kTreeWaves];
+  __shared__ long long s_off[kTreeWaves];
+  __shared__ int s_void;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kTreeWaves;
+  long long before = 0, total = 0;
+  int bad = 0;
+  for (int64_t c = tid; c < a.B; c += 64 * kTreeWaves) {
+    const int nc = a.n_nodes[c];
+    if (nc < 1 || nc > a.max_nodes) {
+      bad = 1;
+    } else {
+      total += nc;
+      if (c < b0) before += nc;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    before += __shfl_xor(before, m, 64);
+    total += __shfl_xor(total, m, 64);
+    bad |= __shfl_xor(bad, m, 64);
+  }
+  if (lane == 0) {
+    s_before[wave] = before;
+    s_total[wave] = total;
+    s_bad[wave] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long bsum = 0, tsum = 0;
+    int anybad = 0;
+    for (int w = 0; w < kTreeWaves; ++w) {
+      bsum += s_before[w];
+      tsum += s_total[w];
+      anybad |= s_bad[w];
+    }
+    s_void = anybad ? 1 : (tsum != a.n_nodes_total ? 2 : 0);
+    if (!s_void)
+      for (int i = 0; i < kTreeWaves; ++i) {
+        s_off[i] = bsum;
+        if (b0 + i < a.B) bsum += a.n_nodes[b0 + i];
+      }
+    if (s_void && blockIdx.x == 0) atomicOr(a.device_status, s_void);
+  }
+  __syncthreads();
+  if (s_void) {  // the layout is unknown: -1 everywhere, strided over the grid
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 64 * kTreeWaves;
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * 64 * kTreeWaves + tid; t < a.n_nodes_total + a.B;
+         t += stride) {
+      a.out_tokens[t] = -1;
+      if (a.out_nodes && t < a.n_nodes_total) a.out_nodes[t] = -1;
+    }
+    for (int64_t b = b0 + tid; b < min<int64_t>(a.B, b0 + kTreeWaves); b += 64 * kTreeWaves)
+      a.accept_len[b] = -1;
+    return;
+  }
+  const int64_t b = b0 + wave;
+  if (b >= a.B) return;
+  const int n = a.n_nodes[b];
+  const int64_t on = s_off[wave], ot = on + b;  // first node, first target row
+  int pr[kTreePerLane], tk[kTreePerLane];
+  int flags = 0;
+#pragma unroll
+  for (int m = 0; m < kTreePerLane; ++m) {
+    const int j = lane + 64 * m;
+    pr[m] = -2;
+    tk[m] = -1;
+    if (j < n) {
+      pr[m] = a.parent[on + j];
+      tk[m] = a.tokens[on + j];
+      if (pr[m] < -1 || pr[m] >= j) flags |= 32;  // SV_DEV_BAD_PARENT
+      if (tk[m] < 0 || tk[m] >= a.V) flags |= 4;  // SV_DEV_BAD_TOKEN
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) flags |= __shfl_xor(flags, m, 64);
+  if (flags) {
+    if (lane == 0) {
+      a.accept_len[b] = -1;
+      atomicOr(a.device_status, flags);
+    }
+    for (int j = lane; j <= n; j += 64) a.out_tokens[ot + j] = -1;
+    if (a.out_nodes)
+      for (int j = lane; j < n; j += 64) a.out_nodes[on + j] = -1;
+    return;
+  }
+  // the request's row argmaxes (root, then nodes) staged in this wave's LDS slice, so each step
+  // of the walk reads LDS instead of waiting on a global load
+  int* s_arg = s_args + wave * (kTreeMaxNodes + 1);
+  for (int j = lane; j <= n; j += 64) s_arg[j] = a.arg[ot + j];
+  int cur = -1, len = 0, g;
+  while (true) {
+    g = s_arg[cur + 1];
+    int best = 0x7fffffff;
+#pragma unroll
+    for (int m = kTreePerLane - 1; m >= 0; --m)
+      if (pr[m] == cur && tk[m] == g) best = lane + 64 * m;
+    const int nxt = wave_min_int(best);
+    if (nxt == 0x7fffffff) break;
+    if (lane == 0) {
+      a.out_tokens[ot + len] = g;
+      if (a.out_nodes) a.out_nodes[on + len] = nxt;
+    }
+    ++len;
+    cur = nxt;
+  }
+  if (lane == 0) {
+    a.out_tokens[ot + len] = g;
+    a.accept_len[b] = len;
+  }
+  for (int j = len + 1 + lane; j <= n; j += 64) a.out_tokens[ot + j] = -1;
+  if (a.out_nodes)
+    for (int j = len + lane; j < n; j += 64) a.out_nodes[on + j] = -1;
+}
+
 // =========================================================================== launchers
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(sv_plan_kernel, dim3(1), dim3(1024), 0, st, a);
@@ -816,6 +947,12 @@ hipError_t launch_opd_grad(int dtype, int grad_dtype, bool vec, const GradArgs& 
 hipError_t launch_status(const int32_t* row_flags, int64_t n, int32_t* device_status,
                          hipStream_t st) {
   hipLaunchKernelGGL(sv_status_kernel, dim3(1), dim3(256), 0, st, row_flags, n, device_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_walk(const TreeArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.B + kTreeWaves - 1) / kTreeWaves));
+  hipLaunchKernelGGL(sv_tree_walk_kernel, grid, dim3(64 * kTreeWaves), 0, st, a);
   return hipGetLastError();
 }
 

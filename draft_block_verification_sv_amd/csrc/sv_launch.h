@@ -187,4 +187,31 @@ struct BranchArgs {
 };
 hipError_t launch_branch(const BranchArgs& a, hipStream_t st);
 
+// Greedy tree verification: the argmax of every target row, then the walk.
+struct ArgmaxArgs {
+  const void* target;
+  int64_t ld_t;
+  int32_t V;
+  int64_t n_slices;
+  int64_t n_rows;
+  int32_t* arg;            // [n_rows]
+  int32_t* zero_status;    // nullable: set to 0 by the first workgroup (for a later kernel)
+};
+hipError_t launch_row_argmax(int dtype, bool vec, const ArgmaxArgs& a, hipStream_t st);
+struct TreeArgs {
+  int64_t B;
+  int32_t max_nodes;
+  int32_t V;
+  int64_t n_nodes_total;
+  const int32_t* n_nodes;
+  const int32_t* parent;
+  const int32_t* tokens;
+  const int32_t* arg;  // argmax of every target row
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int32_t* out_nodes;  // nullable
+  int32_t* device_status;
+};
+hipError_t launch_tree_walk(const TreeArgs& a, hipStream_t st);
+
 }  // namespace sv

@@ -1089,6 +1089,48 @@ hipError_t launch_greedy(int dtype, bool vec, const RowPairArgs& a, hipStream_t 
   return hipGetLastError();
 }
 
+// First argmax (lowest id among the maxima) of every row: one workgroup per row, the greedy
+// stream, then the lanes holding the row maximum look at that one slice again.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void sv_row_argmax_kernel(ArgmaxArgs a) {
+  __shared__ float red_f[kRowWaves];
+  __shared__ int red_i[kRowWaves];
+  const int tid = thread_index(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t = block_index();
+  const void* prow = static_cast<const char*>(a.target) + t * a.ld_t * (DT == 0 ? 2 : 4);
+  float best = -INFINITY;
+  int best_s = -1;
+  stream_max<DT, VEC>(prow, a.V, static_cast<int>(a.n_slices), wave, lane, best, best_s);
+  const float Mx = block_max_f(best, red_f);
+  int col = 0x7fffffff;
+  if (best == Mx && best_s >= 0) {
+    FloatRow f;
+    f.template load<DT, VEC>(prow, static_cast<int64_t>(best_s) * kSlice + lane * 8, a.V);
+#pragma unroll
+    for (int e = kElemsPerLane - 1; e >= 0; --e)
+      if (f.at(e) == Mx) col = best_s * kSlice + (e >> 3) * 512 + lane * 8 + (e & 7);
+  }
+  const int arg = block_min_i(col, red_i);
+  if (tid == 0) {
+    a.arg[t] = arg;
+    if (t == 0 && a.zero_status) *a.zero_status = 0;
+  }
+}
+
+hipError_t launch_row_argmax(int dtype, bool vec, const ArgmaxArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.n_rows));
+  if (a.n_rows == 0) return hipSuccess;
+  if (dtype == 0) {
+    if (vec) hipLaunchKernelGGL((sv_row_argmax_kernel<0, true>), grid, dim3(kRowThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_row_argmax_kernel<0, false>), grid, dim3(kRowThreads), 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((sv_row_argmax_kernel<1, true>), grid, dim3(kRowThreads), 0, st, a);
+    else hipLaunchKernelGGL((sv_row_argmax_kernel<1, false>), grid, dim3(kRowThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- launch
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.n_units));

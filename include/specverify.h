@@ -81,7 +81,8 @@ enum {
   SV_DEV_ROWS_MISMATCH = 2,    /* sum_b k_b != n_draft_rows: the whole call is void       */
   SV_DEV_BAD_TOKEN = 4,        /* a draft token outside [0, V)                            */
   SV_DEV_BAD_TEMPERATURE = 8,  /* a T_b negative, not finite, or positive below FLT_MIN   */
-  SV_DEV_BAD_UNIFORM = 16      /* a uniform outside [0, 1) or NaN                         */
+  SV_DEV_BAD_UNIFORM = 16,     /* a uniform outside [0, 1) or NaN                         */
+  SV_DEV_BAD_PARENT = 32       /* a tree node whose parent is not an earlier node or -1   */
 };
 
 /* Limits checked on the host. */
@@ -90,6 +91,7 @@ enum {
 #define SV_MAX_VOCAB (1 << 19) /* 524288 */
 #define SV_MAX_HEAD_FEATURES 4096 /* H' of the length head */
 #define SV_MAX_BRANCHES 4096 /* prepared successor blocks per request */
+#define SV_MAX_TREE_NODES 1024 /* draft-tree nodes per request */
 
 /* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
  * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */
@@ -308,6 +310,51 @@ sv_status sv_branch_lookup(int32_t B, int32_t k_max, int32_t n_branch, int64_t n
                            const int32_t* k, const int32_t* accept_len, const int32_t* out_tokens,
                            const int32_t* branch_pos, const int32_t* branch_tok, int32_t* hit,
                            void* stream);
+
+/* Bytes of workspace sv_verify_tree_greedy needs; 0 if invalid. */
+size_t sv_tree_workspace_size(int32_t B, int64_t n_nodes_total);
+
+/*
+ * sv_verify_tree_greedy: greedy (temperature 0) verification of one draft tree per request in
+ * one pass over the target rows (DFlash notes, Section 5.1: EAGLE-2/3 propose a dynamic draft
+ * tree and verify it with one target pass; Section 5.2, worked example #4: greedy verification
+ * accepts a draft iff it equals the target argmax at its prefix; AdaFlash paper, Appendix B.1:
+ * greedy decoding is the default).
+ * Node j of request b holds a drafted token and its parent: -1 (the root, i.e. the verified
+ * anchor) or an earlier node of the same request.  The target scores the root and every node:
+ * request b's target rows are root, node 0, ..., node n_b - 1.  From the root, the walk moves to
+ * the lowest-index child whose token is the argmax (lowest id on ties) of the current node's
+ * row; it stops at a node none of whose children matches and emits that node's argmax after
+ * the accepted path.  A chain (parent j - 1) is exactly sv_verify_block_greedy.
+ *
+ *   dtype           SV_BF16 or SV_F32.
+ *   B, max_nodes    requests; upper bound on every n_b (1..SV_MAX_TREE_NODES).
+ *   V, ld_target    vocabulary; row stride in elements (>= V).
+ *   n_nodes_total   sum_b n_b.
+ *   target_logits   [n_nodes_total + B, ld_target]: request b's n_b + 1 rows start at row
+ *                   sum_{c<b} (n_c + 1).
+ *   n_nodes         int32 [B]: n_b.
+ *   parent, tree_tokens   int32 [n_nodes_total]: request b's nodes start at sum_{c<b} n_c.
+ * Outputs (device):
+ *   accept_len      int32 [B]: accepted path length, -1 for an invalid request or a void call.
+ *   out_tokens      int32 [n_nodes_total + B], following the target rows: the path's tokens,
+ *                   the final token, then -1.
+ *   out_nodes       int32 [n_nodes_total] or NULL, following the nodes: the accepted node
+ *                   indices in path order (what a KV cache commits), then -1.
+ *   device_status   int32 [1]: SV_DEV_BAD_LENGTH / SV_DEV_ROWS_MISMATCH (n_b out of range, or
+ *                   the n_b do not sum to n_nodes_total: the call is void), SV_DEV_BAD_TOKEN,
+ *                   SV_DEV_BAD_PARENT (that request is invalid).
+ * Workspace: sv_tree_workspace_size(B, n_nodes_total) bytes, 256-byte aligned.  All pointers are
+ * device memory owned by the caller; nothing is allocated.  Host-checkable errors return
+ * synchronously; the work is enqueued on `stream`.
+ */
+sv_status sv_verify_tree_greedy(int32_t dtype, int32_t B, int32_t max_nodes, int64_t V,
+                                int64_t ld_target, int64_t n_nodes_total,
+                                const void* target_logits, const int32_t* n_nodes,
+                                const int32_t* parent, const int32_t* tree_tokens,
+                                int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                                int32_t* device_status, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Static text for a status code. */
 const char* sv_status_string(sv_status s);

@@ -195,3 +195,23 @@ def test_branch_lookup_argument_errors(L):
     assert call(out=None) == 1
     assert call(tok=None) == 1
     assert call(hit=None) == 1
+
+
+def test_tree_argument_errors(L):
+    def call(dtype=0, B=2, mx=60, V=1000, ld=1000, n=10, tgt=16, nn=16, par=16, tok=16, al=16,
+             out=16, nodes=None, st=16, ws=None, wsb=0):
+        return L.sv_verify_tree_greedy(dtype, B, mx, V, ld, n, tgt, nn, par, tok, al, out, nodes, st,
+                                       ws, wsb, None)
+
+    assert call(dtype=7) == 3
+    assert call(B=0) == 2
+    assert call(mx=1025) == 2
+    assert call(n=1) == 2  # fewer nodes than requests
+    assert call(n=200) == 2  # more than B * max_nodes
+    assert call(ld=999) == 2
+    assert call(tgt=None) == 1
+    assert call(par=None) == 1
+    assert call(st=None) == 1
+    assert call(ws=None, wsb=1 << 30) == 5
+    assert L.sv_tree_workspace_size(2, 10) >= 12 * 4
+    assert L.sv_tree_workspace_size(2, 1) == 0
