@@ -17,14 +17,15 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 20;
+constexpr int kNumKernels = 22;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
     "sv_head_pool",   "sv_len_loss",
-    "sv_branch",      "sv_tree_argmax",  "sv_tree_walk"};
+    "sv_branch",      "sv_tree_argmax",  "sv_tree_walk",    "sv_rowpair_part",
+    "sv_rowpair_fin"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -45,7 +46,9 @@ enum {
   K_LEN_LOSS,
   K_BRANCH,
   K_TREE_ARGMAX,
-  K_TREE_WALK
+  K_TREE_WALK,
+  K_ROWPAIR_PART,
+  K_ROWPAIR_FIN
 };
 
 // ------------------------------------------------------------------ profiling
@@ -137,6 +140,7 @@ Dims verify_dims(int64_t B, int64_t k_max, int64_t V) {
   d.n_units = d.n_t;
   d.n_slices = sv::n_slices_for(V);
   d.n_chunks = sv::n_chunks_for(V);
+  d.rec_slots = sv::split_slots(2 * B, d.n_t, d.n_slices);  // a call has between 2B and B (k_max + 1) rows
   return d;
 }
 
@@ -150,6 +154,7 @@ Dims rkl_dims(int64_t n_rows, int64_t V, bool with_grad = false) {
   d.n_units = n_rows;
   d.n_slices = sv::n_slices_for(V);
   d.n_chunks = 0;
+  d.rec_slots = sv::split_slots(n_rows, n_rows, d.n_slices);
   return d;
 }
 
@@ -161,6 +166,25 @@ bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
 }  // namespace
 
 namespace {
+
+// The streaming pass over n_units rows (pairs): one launch, or for small launches the split
+// streaming launch and the finalize launch.
+hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace& ws, int64_t rec_slots,
+                       hipStream_t st, int k_whole) {
+  const int P = rec_slots > 0 ? sv::row_split(ra.n_units, ra.n_slices) : 1;
+  if (P < 2 || ra.n_units * P > rec_slots) {
+    ra.phase = 0;
+    ra.split = 1;
+    return timed(k_whole, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
+  }
+  ra.split = P;
+  ra.rec = ws.rec;
+  ra.phase = 1;
+  hipError_t e = timed(K_ROWPAIR_PART, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
+  if (e != hipSuccess) return e;
+  ra.phase = 2;
+  return timed(K_ROWPAIR_FIN, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
+}
 
 // The clipped reverse-KL of n_rows row pairs, and with hard_out the hard-label
 // cross-entropy against each target row's top-1: sv_clipped_rkl and sv_opd_loss.
@@ -203,8 +227,7 @@ sv_status rkl_rows(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t
   ra.stats = with_grad ? ws.stats : nullptr;
   ra.device_status = device_status;
   ra.row_flags = ws.row_flags;
-  if (timed(k_rowpair, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
-    return SV_ERR_HIP;
+  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, k_rowpair) != hipSuccess) return SV_ERR_HIP;
   if (ws_out) {  // the caller folds the row flags into its own final kernel
     *ws_out = ws;
     return SV_OK;
@@ -320,8 +343,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.d_lz = ws.d_lz;
   ra.acc = ws.acc;
   ra.arrive = ws.arrive;
-  if (timed(K_ROWPAIR, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); }) != hipSuccess)
-    return SV_ERR_HIP;
+  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR) != hipSuccess) return SV_ERR_HIP;
 
   sv::SampleArgs sa{};
   sa.target = target_logits;

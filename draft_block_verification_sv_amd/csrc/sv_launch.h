@@ -57,6 +57,13 @@ struct RowPairArgs {
   float* d_lz;
   int32_t* acc;
   int32_t* arrive;  // nullable: per-request draw counters, zeroed here for the draw kernel
+  // Rows split over several workgroups (small launches): phase 0 streams and finalizes each
+  // row (pair) in one workgroup; phase 1 streams part `blockIdx % split` of row (pair)
+  // `blockIdx / split` and stores its lane records in rec; phase 2 folds a row's records and
+  // finalizes it.
+  int32_t phase;
+  int32_t split;
+  void* rec;  // [n_units * split * kRowThreads] lane records (phases 1 and 2)
 };
 
 struct SampleArgs {

@@ -40,6 +40,33 @@ constexpr int kMassChunksPerBlock = 2 * kMassWaves;
 constexpr int kMaxChunks = 1024;
 
 inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
+
+// Small launches split each row (pair) over several streaming workgroups, which store their
+// lane records (at most kLaneRecBytes each) for a finalize launch.  Only launches of at most
+// kSplitMaxUnits rows split (with more, one workgroup per row already covers most of the chip
+// and the finalize launch costs more than it saves); they aim at about SV_SPLIT_TARGET
+// streaming workgroups, with at most 16 parts per row, at least two slices per wave and at
+// most kSplitSlots record sets in all.
+#ifndef SV_SPLIT_TARGET
+#define SV_SPLIT_TARGET 512
+#endif
+constexpr int64_t kSplitMaxUnits = 128;
+constexpr int64_t kSplitSlots = 1024;
+constexpr size_t kLaneRecBytes = 72;
+inline int row_split(int64_t n_units, int64_t n_slices) {
+  if (SV_SPLIT_TARGET < 2 || n_units < 1 || n_units > kSplitMaxUnits) return 1;
+  int64_t P = (SV_SPLIT_TARGET + n_units - 1) / n_units;
+  if (P > 16) P = 16;
+  if (P > n_slices / 8) P = n_slices / 8;
+  if (P > kSplitSlots / n_units) P = kSplitSlots / n_units;
+  return P >= 2 ? static_cast<int>(P) : 1;
+}
+// Record sets to reserve for launches of at least min_units and at most max_units rows.
+inline int64_t split_slots(int64_t min_units, int64_t max_units, int64_t n_slices) {
+  if (SV_SPLIT_TARGET < 2 || min_units > kSplitMaxUnits || n_slices < 16) return 0;
+  const int64_t cap = max_units * 16;
+  return cap < kSplitSlots ? cap : kSplitSlots;
+}
 inline int64_t n_chunks_for(int64_t V) { return (V + kChunk - 1) / kChunk; }
 inline int64_t mass_blocks_for(int64_t n_chunks) {
   return (n_chunks + kMassChunksPerBlock - 1) / kMassChunksPerBlock;
@@ -75,6 +102,7 @@ struct Workspace {
   int32_t* acc;        // [n_d] acceptance flag
   double* chunk_mass;  // [B * n_chunks] draw mass of each chunk of each request's draw row
   int32_t* arrive;     // [B] draw workgroups of each request done (zeroed by the streaming pass)
+  void* rec;           // [rec_slots * kRowThreads] lane records of split rows
   RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
   float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
 };
@@ -82,6 +110,7 @@ struct Workspace {
 struct Dims {
   int64_t B, n_t, n_d, V, n_units, n_slices, n_chunks;
   int64_t n_grad;  // rows of the OPD gradient pass (0 otherwise)
+  int64_t rec_slots;  // record sets for split rows (0: launches of this size never split)
 };
 
 // Lays out the regions (each 256-byte aligned) and returns the total byte count.
@@ -107,6 +136,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.acc = reinterpret_cast<int32_t*>(take(d.n_d * 4));
   w.chunk_mass = reinterpret_cast<double*>(take(d.B * d.n_chunks * sizeof(double)));
   w.arrive = reinterpret_cast<int32_t*>(take(d.B * sizeof(int32_t)));
+  w.rec = take(static_cast<size_t>(d.rec_slots) * kRowThreads * kLaneRecBytes);
   w.stats = reinterpret_cast<RowStats*>(take(d.n_grad * sizeof(RowStats)));
   w.coef = reinterpret_cast<float*>(take(d.n_grad * 2 * sizeof(float)));
   if (ws) *ws = w;

@@ -228,6 +228,35 @@ struct LaneAcc {
   int aidx;                    // ... and its first column
 };
 
+// What a part of a split row hands to the finalize, per lane: the offsets and sums after the
+// top correction, the largest l_q - l_p and the greedy argmax (the running maxima have no use
+// once the sums are corrected).
+struct LaneRec {
+  float kp, kq, ktp, ktq;
+  double sp, sq, stp, stq, w;
+  float dmax, amax;
+  int aidx, pad;
+};
+static_assert(sizeof(LaneRec) <= kLaneRecBytes, "lane records must fit their workspace slots");
+
+__device__ __forceinline__ LaneRec lane_record(const LaneAcc& A) {
+  LaneRec R;
+  R.kp = A.kp;
+  R.kq = A.kq;
+  R.ktp = A.ktp;
+  R.ktq = A.ktq;
+  R.sp = A.sp;
+  R.sq = A.sq;
+  R.stp = A.stp;
+  R.stq = A.stq;
+  R.w = A.w;
+  R.dmax = A.dmax;
+  R.amax = A.amax;
+  R.aidx = A.aidx;
+  R.pad = 0;
+  return R;
+}
+
 __device__ __forceinline__ void lane_clear(LaneAcc& A) {
   A.kp = A.kq = A.ktp = A.ktq = 0.0f;
   A.sp = A.sq = A.stp = A.stq = A.w = 0.0;
@@ -401,20 +430,20 @@ __device__ __forceinline__ void slice_accumulate(const Row& rp, const Row& rq, f
   }
 }
 
-// Streams the wave's slices (s = wave, wave + 4, ...) of the row (pair) into the lane's
-// statistics.  Full bf16 slices of 16-byte-aligned rows: packed, next slice prefetched
+// Streams the wave's slices (s = first, first + step, ...; first = the wave, step = 4 when
+// one workgroup takes the whole row) of the row (pair) into the lane's statistics.  Full bf16 slices of 16-byte-aligned rows: packed, next slice prefetched
 // while the current one is reduced.  The ragged last slice and every other case: fp32,
 // masked.  The lane's first slice sets its offsets from that slice's maxima.
 template <int DT, bool VEC, bool PAIR, int MODE>
 __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, float beta, int V,
-                                           int n_slices, int wave, int lane, LaneAcc& A) {
+                                           int n_slices, int first, int step, int lane, LaneAcc& A) {
   const int n_full = V / kSlice;
-  int s = wave;
+  int s = first;
   bool fresh = true;
   if constexpr (DT == 0 && VEC && !SV_ROWS_PREFETCH) {
     const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
     const uint16_t* Q = static_cast<const uint16_t*>(qrow) + lane * 8;
-    for (; s < n_full; s += kRowWaves) {
+    for (; s < n_full; s += step) {
       PackedRow ap, aq;
       ap.load(P + static_cast<int64_t>(s) * kSlice);
       if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s) * kSlice);
@@ -451,19 +480,19 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
     };
     if (s < n_full) {
       load_pair(ap, aq, s);
-      load_pair(bp, bq, s + kRowWaves);
+      load_pair(bp, bq, s + step);
       lane_init<PAIR, MODE>(ap, aq, beta, A);
       fresh = false;
       while (true) {
-        load_pair(cp, cq, s + 2 * kRowWaves);
+        load_pair(cp, cq, s + 2 * step);
         add(ap, aq, s);
-        if (s + kRowWaves >= n_full) { s += kRowWaves; break; }
-        load_pair(ap, aq, s + 3 * kRowWaves);
-        add(bp, bq, s + kRowWaves);
-        if (s + 2 * kRowWaves >= n_full) { s += 2 * kRowWaves; break; }
-        load_pair(bp, bq, s + 4 * kRowWaves);
-        add(cp, cq, s + 2 * kRowWaves);
-        s += 3 * kRowWaves;
+        if (s + step >= n_full) { s += step; break; }
+        load_pair(ap, aq, s + 3 * step);
+        add(bp, bq, s + step);
+        if (s + 2 * step >= n_full) { s += 2 * step; break; }
+        load_pair(bp, bq, s + 4 * step);
+        add(cp, cq, s + 2 * step);
+        s += 3 * step;
         if (s >= n_full) break;
       }
     }
@@ -473,24 +502,24 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
       lane_init<PAIR, MODE>(ap, aq, beta, A);
       fresh = false;
       while (true) {
-        load_pair(bp, bq, s + kRowWaves);
+        load_pair(bp, bq, s + step);
         slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
                                             static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
-        if (s + kRowWaves >= n_full) {
-          s += kRowWaves;
+        if (s + step >= n_full) {
+          s += step;
           break;
         }
-        load_pair(ap, aq, s + 2 * kRowWaves);
+        load_pair(ap, aq, s + 2 * step);
         slice_accumulate<PAIR, MODE, false>(bp, bq, beta,
-                                            static_cast<int64_t>(s + kRowWaves) * kSlice + lane * 8,
+                                            static_cast<int64_t>(s + step) * kSlice + lane * 8,
                                             V, A);
-        s += 2 * kRowWaves;
+        s += 2 * step;
         if (s >= n_full) break;
       }
     }
 #endif
   }
-  for (; s < n_slices; s += kRowWaves) {  // every slice not handled above
+  for (; s < n_slices; s += step) {  // every slice not handled above
     const int64_t col_lane = static_cast<int64_t>(s) * kSlice + lane * 8;
     FloatRow fp, fq;
     fp.template load<DT, VEC>(prow, col_lane, V);
@@ -500,6 +529,46 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
       fresh = false;
     }
     slice_accumulate<PAIR, MODE, true>(fp, fq, beta, col_lane, V, A);
+  }
+}
+
+// Folds the record R of the same lane position over another part of the row into A.  Sums
+// against whole-number offsets combine exactly up to rounding: both are rescaled to the larger
+// offset of the two that carry mass (a record without mass keeps no offset).  Applied to a
+// lane's parts in part order, so the result does not depend on which part finished first.
+__device__ __forceinline__ void fold_sum(float& kA, double& sA, float kR, double sR) {
+  if (!(sR > 0.0)) return;
+  if (sA > 0.0) {
+    const float K = fmaxf(kA, kR);
+    sA = ldexp(sA, static_cast<int>(kA - K)) + ldexp(sR, static_cast<int>(kR - K));
+    kA = K;
+  } else {
+    kA = kR;
+    sA = sR;
+  }
+}
+
+__device__ __forceinline__ void lane_merge(LaneAcc& A, const LaneRec& R) {
+  fold_sum(A.kp, A.sp, R.kp, R.sp);
+  fold_sum(A.ktp, A.stp, R.ktp, R.stp);
+  fold_sum(A.ktq, A.stq, R.ktq, R.stq);
+  if (R.sq > 0.0) {  // W shares the offset of S_q
+    if (A.sq > 0.0) {
+      const float K = fmaxf(A.kq, R.kq);
+      const int ha = static_cast<int>(A.kq - K), hr = static_cast<int>(R.kq - K);
+      A.sq = ldexp(A.sq, ha) + ldexp(R.sq, hr);
+      A.w = ldexp(A.w, ha) + ldexp(R.w, hr);
+      A.kq = K;
+    } else {
+      A.kq = R.kq;
+      A.sq = R.sq;
+      A.w = R.w;
+    }
+  }
+  A.dmax = fmaxf(A.dmax, R.dmax);
+  if (R.amax > A.amax || (R.amax == A.amax && R.aidx < A.aidx)) {
+    A.amax = R.amax;
+    A.aidx = R.aidx;
   }
 }
 
@@ -656,6 +725,8 @@ __device__ __forceinline__ void draw_offsets(double LZ, float* off, float* lz) {
 
 // ----------------------------------------------------------------------------- kernel
 struct RowCtx {
+  int64_t unit;  // the row (pair) this workgroup works on
+  int part;      // which part of it, when rows are split over several workgroups
   int64_t t, d;  // target row, draft row (-1: bonus row)
   int64_t b;     // request (-1: clipped reverse-KL only)
   int mode;      // 0: T = 1, 1: greedy, 2: other T
@@ -663,7 +734,7 @@ struct RowCtx {
   int row_flags;
 };
 
-template <int DT, bool VEC, bool PAIR, int MODE>
+template <int DT, bool VEC, int PHASE, bool PAIR, int MODE>
 __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
                                              LaneAcc* lacc, double* direct, double* direct_sg,
                                              int* failed, int* s_nfail,
@@ -676,10 +747,12 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   const void* prow = static_cast<const char*>(a.target) + ctx.t * a.ld_t * (DT == 0 ? 2 : 4);
   const void* qrow = static_cast<const char*>(a.draft) + (PAIR ? ctx.d : 0) * a.ld_d * (DT == 0 ? 2 : 4);
 
-  {
+  if constexpr (PHASE != 2) {  // stream the row (pair), or this workgroup's part of it
     LaneAcc L;
     lane_clear(L);
-    stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, wave, lane, L);
+    const int first = (PHASE == 1 ? ctx.part * kRowWaves : 0) + wave;
+    const int step = kRowWaves * (PHASE == 1 ? a.split : 1);
+    stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, first, step, lane, L);
     const float Mp = lane_max(L.mhp, L.mlp);
     correct_top(L.sp, Mp, kL2E, L.kp);
     if constexpr (MODE == 2) correct_top(L.stp, Mp, ctx.beta, L.ktp);
@@ -688,8 +761,13 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       correct_top(L.sq, Mq, kL2E, L.kq);
       if constexpr (MODE == 2) correct_top(L.stq, Mq, ctx.beta, L.ktq);
     }
+    if constexpr (PHASE == 1) {  // a part: its lane records go to the workspace for the finalize
+      static_cast<LaneRec*>(a.rec)[(ctx.unit * a.split + ctx.part) * kRowThreads + tid] = lane_record(L);
+      return;
+    }
     lacc[tid] = L;  // the finalize reads the record back as it needs it
   }
+  // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
 
   // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
@@ -865,7 +943,26 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
   return s_req >= 0;  // false only when the layout is invalid, which the scan reports
 }
 
-template <int DT, bool VEC>
+// The finalize of a split row: the lane's records of every part, folded in part order, eight
+// in flight at a time (a batch past the last part re-reads it and skips it).
+__device__ __forceinline__ void merge_parts(const RowPairArgs& a, int64_t unit, int tid, LaneAcc& L) {
+  lane_clear(L);
+  const LaneRec* mine = static_cast<const LaneRec*>(a.rec) + unit * a.split * kRowThreads + tid;
+  const int last = a.split - 1;
+  for (int j = 0; j <= last; j += 8) {
+    LaneRec R[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) R[u] = mine[min(j + u, last) * kRowThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j + u <= last) lane_merge(L, R[u]);
+  }
+}
+
+// PHASE 0: one workgroup streams and finishes a row (pair).  PHASE 1: workgroup blockIdx
+// streams part blockIdx % split of row (pair) blockIdx / split and stores its lane records.
+// PHASE 2: one workgroup per row (pair) folds the records and finishes it.
+template <int DT, bool VEC, int PHASE>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_ROWS_WAVES_PER_EU)))
 void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ LaneAcc lacc[kRowThreads];
@@ -879,9 +976,17 @@ void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ int s_req, s_off, s_t, s_void, s_x;
   __shared__ float s_lpx, s_lqx;
   const int tid = thread_index();
-  const int64_t unit = block_index();
+  const int64_t blk = block_index();
+  const int64_t unit = PHASE == 1 ? blk / a.split : blk;
+  if constexpr (PHASE == 2) {  // the records depend on nothing else: fetch them first
+    LaneAcc L;
+    merge_parts(a, unit, tid, L);
+    lacc[tid] = L;
+  }
 
   RowCtx ctx;
+  ctx.unit = unit;
+  ctx.part = PHASE == 1 ? static_cast<int>(blk - unit * a.split) : 0;
   if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
     ctx.d = unit;
     ctx.t = a.p_row_index ? a.p_row_index[unit] : unit;
@@ -901,10 +1006,10 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (tid == 0) a.row_flags[unit] = 0;
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
-      rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     } else {
-      rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     }
     return;
@@ -930,8 +1035,8 @@ void sv_rowpair_kernel(RowPairArgs a) {
     ctx.mode = 2;
     ctx.beta = kL2E / T;
   }
-  if (!uniform_ok(a.uniforms[ctx.t])) flags |= 16;
-  if (i == 0 && tid == 0 && !a.desc) {
+  if (PHASE != 1 && !uniform_ok(a.uniforms[ctx.t])) flags |= 16;
+  if (PHASE != 1 && i == 0 && tid == 0 && !a.desc) {
     a.off_t[b] = static_cast<int32_t>(off);
     if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
   }
@@ -940,7 +1045,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
     s_x = -1;
     s_lpx = 0.0f;
     s_lqx = 0.0f;
-    if (ctx.d >= 0) {
+    if (PHASE != 1 && ctx.d >= 0) {  // a part only streams
       const int32_t x = a.tokens[ctx.d];
       if (x < 0 || x >= a.V) {
         flags |= 4;
@@ -956,13 +1061,13 @@ void sv_rowpair_kernel(RowPairArgs a) {
   const int x = s_x;
   const float lpx = s_lpx, lqx = s_lqx;
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
   }
 }
 
@@ -1133,14 +1238,21 @@ hipError_t launch_row_argmax(int dtype, bool vec, const ArgmaxArgs& a, hipStream
 
 // ----------------------------------------------------------------------------- launch
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.n_units));
+  const dim3 grid(static_cast<unsigned>(a.n_units * (a.phase == 1 ? a.split : 1)));
   if (a.n_units == 0) return hipSuccess;
+  if (a.phase < 0 || a.phase > 2 || (a.phase != 0 && (a.split < 2 || !a.rec))) return hipErrorInvalidValue;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, a); };
+  auto by_phase = [&](auto k0, auto k1, auto k2) {
+    if (a.phase == 0) go(k0);
+    else if (a.phase == 1) go(k1);
+    else go(k2);
+  };
   if (dtype == 0) {
-    if (vec) hipLaunchKernelGGL((sv_rowpair_kernel<0, true>), grid, dim3(kRowThreads), 0, st, a);
-    else hipLaunchKernelGGL((sv_rowpair_kernel<0, false>), grid, dim3(kRowThreads), 0, st, a);
+    if (vec) by_phase(sv_rowpair_kernel<0, true, 0>, sv_rowpair_kernel<0, true, 1>, sv_rowpair_kernel<0, true, 2>);
+    else by_phase(sv_rowpair_kernel<0, false, 0>, sv_rowpair_kernel<0, false, 1>, sv_rowpair_kernel<0, false, 2>);
   } else {
-    if (vec) hipLaunchKernelGGL((sv_rowpair_kernel<1, true>), grid, dim3(kRowThreads), 0, st, a);
-    else hipLaunchKernelGGL((sv_rowpair_kernel<1, false>), grid, dim3(kRowThreads), 0, st, a);
+    if (vec) by_phase(sv_rowpair_kernel<1, true, 0>, sv_rowpair_kernel<1, true, 1>, sv_rowpair_kernel<1, true, 2>);
+    else by_phase(sv_rowpair_kernel<1, false, 0>, sv_rowpair_kernel<1, false, 1>, sv_rowpair_kernel<1, false, 2>);
   }
   return hipGetLastError();
 }

@@ -299,3 +299,54 @@ def test_fused_rkl_equals_standalone():
     out, _ = pkg.clipped_rkl(d["target"], d["draft"], w.delta, torch.from_numpy(idx).cuda())
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), got["rkl"])
+
+
+# ----------------------------------------------------------------------------- split rows
+# Launches of a few rows split each row over several workgroups (parts) and fold the parts'
+# lane records in a finalize launch.  V = 70001: 69 slices, so 8 parts per row, the last
+# slice ragged.
+@pytest.mark.parametrize("dtype,ld", [("bf16", 70001), ("f32", 70004)])
+def test_split_rows_parity(dtype, ld):
+    w = make_workload(B=4, k=[3, 1, 5, 2], V=70001, ld=ld, dtype=dtype, s=3.0,
+                      sigma=[0.5, 1.0, 2.0, 0.8], temperature=[1.0, 0.0, 0.7, 1.3], delta=0.05,
+                      outlier_frac=0.05, seed=(13, ld))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report(f"split {dtype} ld={ld}", s)
+    assert s["exact"] >= w.B - 1
+
+
+def test_split_rows_standalone_and_fused():
+    import draft_block_verification_sv_amd as pkg
+    import oracle
+
+    w = make_workload(B=4, k=[3, 1, 5, 2], V=70001, dtype="bf16", sigma=1.2, outlier_frac=0.1,
+                      seed=(14,))
+    d = to_device(w)
+    got = run_gpu(w, d)
+    idx = np.concatenate([np.arange(w.target_offsets[b], w.target_offsets[b] + w.k[b])
+                          for b in range(w.B)]).astype(np.int32)
+    out, st = pkg.clipped_rkl(d["target"], d["draft"], w.delta, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    # the same pairing and the same split give the same bits
+    np.testing.assert_array_equal(out.cpu().numpy(), got["rkl"])
+    tl = oracle.widen_logits(w.target[:, : w.V], "bf16")
+    dl = oracle.widen_logits(w.draft[:, : w.V], "bf16")
+    for delta in (1.0, 0.01):
+        out, st = pkg.clipped_rkl(d["target"], d["draft"], delta, torch.from_numpy(idx[::-1].copy()).cuda())
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().astype(np.float64)
+        for r in range(w.n_draft_rows):
+            ref = oracle.clipped_rkl_row(tl[idx[::-1][r]], dl[r], delta)
+            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21
+            assert abs(o[r] - ref["R"]) <= tol, (delta, r, o[r], ref["R"])
+    # an out-of-range pairing gives NaN for that row only
+    bad = idx.copy()
+    bad[3] = -1
+    out, st = pkg.clipped_rkl(d["target"], d["draft"], 1.0, torch.from_numpy(bad).cuda())
+    torch.cuda.synchronize()
+    assert int(st.item()) & 2
+    o = out.cpu().numpy()
+    assert np.isnan(o[3]) and np.all(np.isfinite(np.delete(o, 3)))
