@@ -562,6 +562,34 @@ def bench_tree(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_read_ceiling(args):
+    """The practical read ceiling: the library's plain read kernel (16-byte loads, four in
+    flight per thread, 1024 workgroups) over the same number of bytes as a streaming launch."""
+    import torch
+
+    import draft_block_verification_sv_amd as pkg
+
+    nbytes = args.read_ceiling // 16 * 16
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    out = torch.empty(pkg.binding.READ_PROBE_WORDS, dtype=torch.int32, device="cuda:0")
+    for _ in range(args.warmup):
+        pkg.read_probe(x, out)
+    torch.cuda.synchronize()
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        pkg.read_probe(x, out)
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    n, ms = kt["sv_read_probe"]
+    us = 1e3 * ms / n
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"read_ceiling": {"bytes": nbytes, "launches": n, "avg_us": round(us, 2),
+                                       "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,8 +603,12 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
+    ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
+                    help="only time the library's plain read kernel over BYTES of device memory")
     args = ap.parse_args()
 
+    if args.read_ceiling:
+        return bench_read_ceiling(args)
     if args.calibrate_copy:
         import torch
 

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     profile_enable,
     profile_read,
     profile_reset,
+    read_probe,
     verify_block,
     verify_block_greedy,
     verify_tree_greedy,

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.sv_status_string.restype = ctypes.c_char_p
     L.sv_version.argtypes = []
     L.sv_version.restype = ctypes.c_char_p
+    L.sv_read_probe.argtypes = [_c_p, _c_i64, _c_p, _c_p]
+    L.sv_read_probe.restype = _c_i32
     L.sv_profile_enable.argtypes = [_c_i32]
     L.sv_profile_enable.restype = _c_i32
     L.sv_profile_reset.argtypes = []
@@ -533,6 +535,22 @@ def clipped_rkl(target: torch.Tensor, draft: torch.Tensor, delta: float = 1.0,
 
 
 # ----------------------------------------------------------------------------- profiling
+READ_PROBE_WORDS = 1024
+
+
+def read_probe(data, out=None, stream=None):
+    """Plain read of the bytes of a contiguous device tensor (diagnostics: the read ceiling).
+    Returns the [READ_PROBE_WORDS] int32 tensor the kernel folds the words into."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("read_probe needs a contiguous device tensor")
+    if out is None:
+        out = torch.empty(READ_PROBE_WORDS, dtype=torch.int32, device=data.device)
+    nbytes = data.numel() * data.element_size()
+    _check(lib().sv_read_probe(data.data_ptr(), nbytes, out.data_ptr(), _stream(stream)),
+           "sv_read_probe")
+    return out
+
+
 def profile_enable(on: bool = True):
     _check(lib().sv_profile_enable(1 if on else 0), "sv_profile_enable")
 

@@ -17,7 +17,7 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 22;
+constexpr int kNumKernels = 23;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
@@ -25,7 +25,7 @@ const char* const kKernelNames[kNumKernels] = {
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
     "sv_head_pool",   "sv_len_loss",
     "sv_branch",      "sv_tree_argmax",  "sv_tree_walk",    "sv_rowpair_part",
-    "sv_rowpair_fin"};
+    "sv_rowpair_fin",  "sv_read_probe"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -48,7 +48,8 @@ enum {
   K_TREE_ARGMAX,
   K_TREE_WALK,
   K_ROWPAIR_PART,
-  K_ROWPAIR_FIN
+  K_ROWPAIR_FIN,
+  K_READ_PROBE
 };
 
 // ------------------------------------------------------------------ profiling
@@ -693,6 +694,17 @@ sv_status sv_clipped_rkl(int32_t dtype, int64_t n_rows, int64_t n_target_rows, i
                   draft_logits, p_row_index, delta, rkl_out, nullptr, nullptr, device_status,
                   workspace, workspace_bytes, static_cast<hipStream_t>(stream), K_RKL_ROWPAIR,
                   K_RKL_STATUS, nullptr);
+}
+
+sv_status sv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream) {
+  if (!data || !out) return SV_ERR_NULL;
+  if (bytes <= 0 || bytes % 16 != 0) return SV_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(data) % 16 != 0) return SV_ERR_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return timed(K_READ_PROBE, st, [&] { return sv::launch_read_probe(data, bytes / 16, out, st); }) ==
+                 hipSuccess
+             ? SV_OK
+             : SV_ERR_HIP;
 }
 
 sv_status sv_profile_enable(int32_t on) {

@@ -221,4 +221,8 @@ struct TreeArgs {
 };
 hipError_t launch_tree_walk(const TreeArgs& a, hipStream_t st);
 
+// Diagnostics: a plain read of n_words 16-byte words; out receives kReadProbeBlocks words.
+constexpr int kReadProbeBlocks = 1024;
+hipError_t launch_read_probe(const void* data, int64_t n_words, uint32_t* out, hipStream_t st);
+
 }  // namespace sv

@@ -374,6 +374,19 @@ int32_t sv_profile_count(void);
 sv_status sv_profile_get(int32_t index, char* name, size_t name_len, int64_t* launches,
                          double* total_ms);
 
+/*
+ * Read ceiling (diagnostics).  A plain read of `bytes` bytes at `data` (device memory, 16-byte
+ * aligned, bytes a positive multiple of 16) on `stream`, folding the words with xor into
+ * out[0 .. SV_READ_PROBE_WORDS) (device memory owned by the caller).  It measures what a
+ * kernel that only streams bytes in reaches on this part: the streaming kernels of this
+ * library read their logits the same way, so their achieved bandwidth is compared with it as
+ * well as with the published HBM peak.  Its duration is reported as "sv_read_probe" by the
+ * kernel timing above.  Errors: SV_ERR_NULL, SV_ERR_SHAPE (size), SV_ERR_VALUE (alignment),
+ * SV_ERR_HIP; nothing is enqueued on an error.
+ */
+#define SV_READ_PROBE_WORDS 1024
+sv_status sv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,3 +215,12 @@ def test_tree_argument_errors(L):
     assert call(ws=None, wsb=1 << 30) == 5
     assert L.sv_tree_workspace_size(2, 10) >= 12 * 4
     assert L.sv_tree_workspace_size(2, 1) == 0
+
+
+def test_read_probe_argument_errors(L):
+    # fake pointers, never dereferenced: every case fails on the host
+    assert L.sv_read_probe(None, 1024, 16, None) == 1
+    assert L.sv_read_probe(16, 1024, None, None) == 1
+    assert L.sv_read_probe(16, 0, 16, None) == 2
+    assert L.sv_read_probe(16, 1000, 16, None) == 2  # not a multiple of 16
+    assert L.sv_read_probe(8, 1024, 16, None) == 4  # not 16-byte aligned
