@@ -647,7 +647,7 @@ __device__ __forceinline__ float logit_at(const void* row, int64_t col) {
 //   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
 // and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
 // ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p.  A lane whose bound may reach
-// delta has its columns re-read by one wave and summed entry by entry.
+// delta has its columns re-read and summed entry by entry.
 // With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
 // OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
 // form plus Q.
@@ -655,12 +655,60 @@ struct RklSums {
   double R, sg;
 };
 
-template <int DT, bool SG>
+// The re-read works on pieces: 8 consecutive columns of one failing lane (the lane's group of
+// 8 in one of its slices).  The pieces of a round are spread over the whole workgroup, four per
+// thread for bf16 rows read 16 bytes at a time and two otherwise (at most kRereadItems), with
+// every load issued before any arithmetic; each piece's sum goes to LDS, and one wave then
+// adds a failing lane's pieces in piece order.
+constexpr int kRereadItems = 1024;
+// A lane has at most ceil(kMaxSlices / 4) * kGroups pieces: one failing lane always fits a round.
+static_assert(((kMaxSlices + kRowWaves - 1) / kRowWaves) * kGroups <= 2 * kRowThreads,
+              "a failing lane's pieces must fit one round");
+
+// The 8 logits of one piece as raw words: a bf16 piece is one 16-byte word, an fp32 piece two.
+// VEC rows are read through a bounds-checked buffer (a piece that is not valid, or the part of
+// one past V, reads zeros); other rows column by column with the column clamped into the row.
+template <int DT, bool VEC>
+struct Piece {
+  u32x4_t w0, w1;
+  __device__ __forceinline__ void load(const void* row, __amdgpu_buffer_rsrc_t rs, int64_t col0,
+                                       bool ok, int V) {
+    constexpr int es = DT == 0 ? 2 : 4;
+    if constexpr (VEC) {
+      const int off = ok ? static_cast<int>(col0) * es : V * es;
+      w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      if constexpr (DT == 1) w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+    } else {
+      int64_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = ok ? (col0 + e < V ? col0 + e : V - 1) : 0;
+      if constexpr (DT == 0) {
+        const uint16_t* r = static_cast<const uint16_t*>(row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w0[e] = static_cast<uint32_t>(r[c[2 * e]]) | (static_cast<uint32_t>(r[c[2 * e + 1]]) << 16);
+      } else {
+        const uint32_t* r = static_cast<const uint32_t*>(row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = r[c[e]];
+          w1[e] = r[c[e + 4]];
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ float at(int e) const {
+    if constexpr (DT == 0) return (e & 1) ? bf16_hi(w0[e >> 1]) : bf16_lo(w0[e >> 1]);
+    else return __uint_as_float(e < 4 ? w0[e] : w1[e - 4]);
+  }
+};
+
+template <int DT, bool VEC, bool SG>
 __device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const void* qrow, int V,
                                                     int n_slices, double LZp, double LZq,
                                                     float delta, const LaneAcc& A, double* direct,
                                                     double* direct_sg, int* failed, int* s_nfail,
-                                                    double* red) {
+                                                    float* ipart, float* igpart, double* red) {
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double c2 = LZp - LZq;
@@ -679,36 +727,73 @@ __device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const voi
   if (fail) failed[atomicAdd(s_nfail, 1)] = tid;
   __syncthreads();
   const int nfail = *s_nfail;
-  const float c2f = static_cast<float>(c2);
-  for (int f = wave; f < nfail; f += kRowWaves) {
-    const int src = failed[f];
-    const int sw = src >> 6, sl = src & 63;  // the failing lane's wave and lane
-    const int n_pieces = ((n_slices - sw + kRowWaves - 1) / kRowWaves) * kGroups;
-    float part = 0.0f, gpart = 0.0f;
-    for (int j = lane; j < n_pieces; j += 64) {
-      const int64_t col0 = static_cast<int64_t>(sw + (j / kGroups) * kRowWaves) * kSlice +
-                           (j % kGroups) * 512 + sl * 8;
+  if (nfail > 0) {
+    const float c2f = static_cast<float>(c2);
+    constexpr int es = DT == 0 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t RQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(qrow), 0, V * es, kBufWord3);
+    const __amdgpu_buffer_rsrc_t RP = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(prow), 0, V * es, kBufWord3);
+    // pieces of a failing lane of wave 0 (the most any lane has); lane src has
+    // ceil((n_slices - src / 64) / 4) * kGroups of them
+    constexpr int PT = (DT == 0 && VEC) ? 4 : 2;  // pieces per thread and round
+    constexpr int items = PT * kRowThreads;
+    static_assert(items <= kRereadItems, "piece sums must fit their LDS arrays");
+    const int npm = ((n_slices + kRowWaves - 1) / kRowWaves) * kGroups;
+    const int per_round = items / npm;  // >= 1: npm <= 2 * kRowThreads <= items
+    for (int f0 = 0; f0 < nfail; f0 += per_round) {
+      const int nf = min(per_round, nfail - f0);
+      const int n_items = nf * npm;
+      int64_t col[PT];
+      bool ok[PT];
+      Piece<DT, VEC> pq[PT], pp[PT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t col = col0 + e;
-        if (col < V) {
-          const float lq = logit_at<DT>(qrow, col);
-          const float lp = logit_at<DT>(prow, col);
+      for (int u = 0; u < PT; ++u) {
+        const int g = tid + u * kRowThreads;
+        const int f = g / npm, j = g - f * npm;
+        const int src = failed[f0 + min(f, nf - 1)];
+        const int sw = src >> 6, sl = src & 63;
+        const int slice = sw + (j / kGroups) * kRowWaves;
+        col[u] = static_cast<int64_t>(slice) * kSlice + (j % kGroups) * 512 + sl * 8;
+        ok[u] = g < n_items && slice < n_slices && col[u] < V;
+        pq[u].load(qrow, RQ, col[u], ok[u], V);
+        pp[u].load(prow, RP, col[u], ok[u], V);
+      }
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int g = tid + u * kRowThreads;
+        float part = 0.0f, gpart = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lq = pq[u].at(e), lp = pp[u].at(e);
           const float q = fast_exp2(static_cast<float>(static_cast<double>(lq) * kL2E - LZq));
           const float term = q * static_cast<float>(kLn2) * __builtin_fmaf(lq - lp, kL2E, c2f);
-          part += fminf(term, delta);
-          if constexpr (SG) gpart += term < delta ? term + q : 0.0f;
+          const bool in = ok[u] && col[u] + e < V;
+          part += in ? fminf(term, delta) : 0.0f;
+          if constexpr (SG) gpart += (in && term < delta) ? term + q : 0.0f;
+        }
+        if (g < n_items) {
+          ipart[g] = part;
+          if constexpr (SG) igpart[g] = gpart;
         }
       }
-    }
-    const double dsum = wave_sum_d(static_cast<double>(part));
-    if (lane == 0) direct[src] = dsum;
-    if constexpr (SG) {
-      const double gsum = wave_sum_d(static_cast<double>(gpart));
-      if (lane == 0) direct_sg[src] = gsum;
+      __syncthreads();
+      for (int f = wave; f < nf; f += kRowWaves) {  // one wave per failing lane, pieces in order
+        const int src = failed[f0 + f];
+        const int n_pieces = ((n_slices - (src >> 6) + kRowWaves - 1) / kRowWaves) * kGroups;
+        double part = 0.0, gpart = 0.0;
+        for (int j = lane; j < n_pieces; j += 64) {
+          part += static_cast<double>(ipart[f * npm + j]);
+          if constexpr (SG) gpart += static_cast<double>(igpart[f * npm + j]);
+        }
+        const double dsum = wave_sum_d(part);
+        if (lane == 0) direct[src] = dsum;
+        if constexpr (SG) {
+          const double gsum = wave_sum_d(gpart);
+          if (lane == 0) direct_sg[src] = gsum;
+        }
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
   RklSums out;
   out.R = block_sum_d(fail ? direct[tid] : closed, red);
   out.sg = SG ? block_sum_d(fail ? direct_sg[tid] : closed + mass, red) : 0.0;
@@ -737,7 +822,7 @@ struct RowCtx {
 template <int DT, bool VEC, int PHASE, bool PAIR, int MODE>
 __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
                                              LaneAcc* lacc, double* direct, double* direct_sg,
-                                             int* failed, int* s_nfail,
+                                             int* failed, int* s_nfail, float* ipart, float* igpart,
                                              double* red_d, float* red_f, int* red_i, int x,
                                              float lpx, float lqx) {
   const int tid = thread_index(), lane = tid & 63;
@@ -793,11 +878,11 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   if (a.rkl_out) {
     RklSums Rk;
     if (MODE == 1 && a.stats)
-      Rk = lanes_clipped_rkl<DT, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
-                                       direct_sg, failed, s_nfail, red_d);
+      Rk = lanes_clipped_rkl<DT, VEC, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
+                                            direct_sg, failed, s_nfail, ipart, igpart, red_d);
     else
-      Rk = lanes_clipped_rkl<DT, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
-                                        direct_sg, failed, s_nfail, red_d);
+      Rk = lanes_clipped_rkl<DT, VEC, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
+                                             direct_sg, failed, s_nfail, ipart, igpart, red_d);
     if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk.R);
     if (MODE == 1 && a.stats && tid == 0) {
       RowStats st;
@@ -969,6 +1054,8 @@ void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ double direct[kRowThreads];
   __shared__ double direct_sg[kRowThreads];
   __shared__ int failed[kRowThreads];
+  __shared__ float ipart[kRereadItems];
+  __shared__ float igpart[kRereadItems];
   __shared__ int s_nfail;
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
@@ -1006,10 +1093,10 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (tid == 0) a.row_flags[unit] = 0;
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
-      rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     } else {
-      rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i,
+      rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
                                      0, 0.0f, 0.0f);
     }
     return;
@@ -1061,13 +1148,13 @@ void sv_rowpair_kernel(RowPairArgs a) {
   const int x = s_x;
   const float lpx = s_lpx, lqx = s_lqx;
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
   }
 }
 

@@ -149,3 +149,23 @@ def test_void_lengths_and_bad_pairing_give_nan():
     assert int(got["device_status"].item()) & 2
     G = got["grad"].cpu().numpy()
     assert np.all(np.isnan(G[3])) and np.all(np.isfinite(np.delete(G, 3, axis=0)))
+
+
+@pytest.mark.parametrize("dtype,ld", [("bf16", 40000), ("f32", 40003)])
+def test_many_clipped_lanes(dtype, ld):
+    # a small delta fails the no-clip bound on most lanes, so the row statistic of the gradient
+    # comes from the entry-by-entry re-read, over several rounds of pieces; the split-row path
+    # (9 rows of 40 slices) is taken as well
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=3, k=[2, 4, 3], V=40000, ld=ld, dtype=dtype, s=3.0, sigma=[0.5, 1.5, 1.0],
+                      outlier_frac=0.05, seed=(34, ld))
+    d = to_device(w)
+    idx = _pairing(w)
+    got = pkg.opd_loss_grad(d["target"], d["draft"], torch.from_numpy(w.k).cuda(), delta=0.004,
+                            alpha=0.8, p_row_index=torch.from_numpy(idx).cuda(),
+                            grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(got["device_status"].item()) == 0
+    worst = _compare(w, got, 0.004, 0.8, idx, range(w.n_draft_rows))
+    print(f"[grad] many clipped lanes {dtype} ld={ld}: max rel err {worst:.2e}", flush=True)

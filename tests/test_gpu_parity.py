@@ -74,6 +74,18 @@ def test_tiny_and_boundary_vocab(V):
     _report(f"V={V}", s)
 
 
+@pytest.mark.parametrize("dtype,ld", [("bf16", 40001), ("f32", 40000), ("f32", 40003)])
+def test_small_delta_every_row_layout(dtype, ld):
+    # nearly every lane fails the no-clip bound: several rounds of re-read pieces, for rows read
+    # 16 bytes at a time and column by column
+    w = make_workload(B=3, k=[5, 3, 4], V=40000, ld=ld, dtype=dtype, s=4.0, sigma=[0.5, 1.0, 2.0],
+                      temperature=[1.0, 0.7, 0.0], delta=1e-3, outlier_frac=0.1, seed=(5, ld))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report(f"delta=1e-3 {dtype} ld={ld}", s)
+
+
 @pytest.mark.parametrize("delta", [1e-3, 1e-2, 0.1])
 def test_small_delta_rereads_clipped_slices(delta):
     # small delta makes many slices fail the no-clip bound and take the direct path
