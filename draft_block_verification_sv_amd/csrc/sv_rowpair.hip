@@ -823,8 +823,7 @@ template <int DT, bool VEC, int PHASE, bool PAIR, int MODE>
 __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
                                              LaneAcc* lacc, double* direct, double* direct_sg,
                                              int* failed, int* s_nfail, float* ipart, float* igpart,
-                                             double* red_d, float* red_f, int* red_i, int x,
-                                             float lpx, float lqx) {
+                                             double* red_d, float* red_f, int* red_i, int xr) {
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = a.V;
@@ -855,6 +854,22 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
 
+  // thread 0, the only user: the draft token's range check and the two logits at it, fetched
+  // here so that their latency overlaps the reductions below instead of delaying the stream
+  int row_flags = ctx.row_flags, x = -1;
+  float lpx = 0.0f, lqx = 0.0f;
+  if constexpr (PAIR) {
+    if (tid == 0 && ctx.b >= 0) {
+      if (xr < 0 || xr >= V) {
+        row_flags |= 4;  // SV_DEV_BAD_TOKEN
+      } else {
+        x = xr;
+        lpx = logit_at<DT>(prow, x);
+        lqx = logit_at<DT>(qrow, x);
+      }
+    }
+  }
+
   // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
   const double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
   const double LZTp = (MODE == 2) ? lanes_lz(A.ktp, A.stp, red_f, red_d) : LZ1p;
@@ -868,7 +883,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     draw_offsets(LZTp, a.t_off + ctx.t, a.t_lz + ctx.t);
     a.t_beta[ctx.t] = scale_T;
     a.t_arg[ctx.t] = argp;
-    a.row_flags[ctx.t] = ctx.row_flags;
+    a.row_flags[ctx.t] = row_flags;
   }
   if constexpr (!PAIR) return;
 
@@ -906,7 +921,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   if (tid == 0 && ctx.b >= 0) {
     draw_offsets(LZTq, a.d_off + ctx.d, a.d_lz + ctx.d);
     int accept = 0;
-    if (ctx.row_flags == 0) {  // the request's own flags are combined by the sampler
+    if (row_flags == 0) {  // the request's own flags are combined by the sampler
       const double Lp = static_cast<double>(lpx) * scale_T - LZTp;  // log2 p_T(x)
       const double Lq = static_cast<double>(lqx) * scale_T - LZTq;  // log2 q_T(x)
       if constexpr (MODE == 1) {
@@ -1060,8 +1075,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
-  __shared__ int s_req, s_off, s_t, s_void, s_x;
-  __shared__ float s_lpx, s_lqx;
+  __shared__ int s_req, s_off, s_t, s_void;
   const int tid = thread_index();
   const int64_t blk = block_index();
   const int64_t unit = PHASE == 1 ? blk / a.split : blk;
@@ -1094,10 +1108,10 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
       rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     0, 0.0f, 0.0f);
+                                     0);
     } else {
       rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     0, 0.0f, 0.0f);
+                                     0);
     }
     return;
   }
@@ -1105,11 +1119,14 @@ void sv_rowpair_kernel(RowPairArgs a) {
   if (!resolve_unit(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
   const int64_t b = s_req;
   const int64_t off = s_off;
-  const int kb = a.k[b];
   ctx.t = s_t;
   const int i = static_cast<int>(ctx.t - off);
   ctx.b = b;
-  ctx.d = (i < kb) ? (off - b + i) : -1;
+  ctx.d = unit < a.n_d ? unit : -1;  // units 0 .. n_d-1 are the draft rows in packed order
+  // thread 0 fetches the draft token with the temperature and the uniform; it is checked, and
+  // the logits at it are fetched, once the row has been streamed
+  int32_t xr = -1;
+  if (PHASE != 1 && tid == 0 && ctx.d >= 0) xr = a.tokens[ctx.d];
   const float T = a.temperature ? a.temperature[b] : 1.0f;
   int flags = 0;
   ctx.mode = 0;
@@ -1127,34 +1144,15 @@ void sv_rowpair_kernel(RowPairArgs a) {
     a.off_t[b] = static_cast<int32_t>(off);
     if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
   }
-  // the draft token and the two logits at it, fetched before the stream starts
-  if (tid == 0) {
-    s_x = -1;
-    s_lpx = 0.0f;
-    s_lqx = 0.0f;
-    if (PHASE != 1 && ctx.d >= 0) {  // a part only streams
-      const int32_t x = a.tokens[ctx.d];
-      if (x < 0 || x >= a.V) {
-        flags |= 4;
-      } else {
-        s_x = x;
-        s_lpx = logit_at<DT>(static_cast<const char*>(a.target) + ctx.t * a.ld_t * (DT == 0 ? 2 : 4), x);
-        s_lqx = logit_at<DT>(static_cast<const char*>(a.draft) + ctx.d * a.ld_d * (DT == 0 ? 2 : 4), x);
-      }
-    }
-  }
-  ctx.row_flags = flags;  // token bit is only known to thread 0; thread 0 writes the flags
-  __syncthreads();
-  const int x = s_x;
-  const float lpx = s_lpx, lqx = s_lqx;
+  ctx.row_flags = flags;  // the token bit is added by thread 0 after the stream
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, x, lpx, lqx);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
   }
 }
 
