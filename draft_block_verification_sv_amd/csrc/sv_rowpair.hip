@@ -2,27 +2,28 @@
 // per-row finalize.
 //
 // One 256-thread workgroup owns one target row t and, when t scores a draft
-// (position i < k_b), the draft row d it pairs with.  Its four wavefronts stream the
-// row (pair) in slices of 64 lanes x kElemsPerLane columns, each wave double-buffering
-// its next slice's 16-byte loads behind the current slice's arithmetic, so every logit
-// is read from HBM exactly once.  Per slice a wave reduces:
-//   m      max (wave butterfly); the exp2 offset is the fp32 product m * L2E;
-//   S      sum 2^(l L2E - fp32(m L2E))                      softmax sum at T = 1;
-//   S_T    sum 2^(l beta - fp32(m beta))                    rows with T_b not in {0, 1};
-//   arg    first column attaining m                         greedy rows (target row);
-//   W, G   sum / max of E_y (l_q - l_p), E_y = 2^(l_q L2E - fp32(m_q L2E)) (draft row),
-// into a record in LDS.  The workgroup then finishes the row from the records:
-//   log2 normalisers LZ = K + log2(sum_s S_s 2^(K_s - K)), fp64, fixed order;
+// (position i < k_b), the draft row d it pairs with.  Its four wavefronts take slices of
+// 64 lanes x kElemsPerLane columns round-robin, each wave loading its next slice (16-byte
+// bounds-checked buffer loads) while it reduces the current one, so every logit is read
+// from HBM exactly once.  Each lane keeps, over its own columns, statistics against
+// whole-number exp2 offsets k (log2 units) set from its first slice:
+//   S   = sum 2^(l L2E - k)                  softmax sums at T = 1 (target and draft);
+//   S_T = sum 2^(l beta - k_T)               rows with T_b not in {0, 1};
+//   W   = sum 2^(l_q L2E - k_q) (l_q - l_p)  and D = max (l_q - l_p)   (row pairs);
+//   the running maxima, and for greedy rows the first argmax of the target row.
+// The workgroup then finishes the row from the 256 lane records, in fixed order:
+//   log2 normalisers LZ = K + log2(sum_l S_l 2^(k_l - K)), fp64;
 //   the clipped reverse-KL R = sum_y min(delta, q log(q/p)) at T = 1 (AdaFlash paper,
-//     Section 3.1 equation; Appendix B.1 for the temperature): per slice,
-//       sum_{y in s} t_y  = ln2 2^(K_s - LZq) (L2E W_s + c2 S_s)     exactly, and
-//       max_{y in s} t_y <= ln2 2^(K_s - LZq) (L2E G_s + max(c2, 0)),   c2 = LZp - LZq;
-//     a slice whose bound stays below delta contributes its exact unclipped sum, any
-//     other slice is re-read (it was just streamed, so it comes from cache) and summed
-//     entry by entry;
+//     Section 3.1 equation; Appendix B.1 for the temperature): per lane, with c2 = LZp - LZq,
+//       sum of t_y over its columns  = ln2 2^(k_q - LZq) (L2E W + c2 S_q)     exactly, and
+//       every t_y <= ln2 2^(k_q - LZq) S_q max(0, L2E D + c2);
+//     a lane whose bound stays below delta contributes its exact unclipped sum, the columns
+//     of any other lane are re-read and summed entry by entry;
 //   the acceptance test u < min(1, p_T(x)/q_T(x)) (paper, Section 2.1), or for T = 0
 //     the argmax match (DFlash notes, Section 5.2, worked example #4);
 //   the offsets the sampler needs to rebuild p_T and q_T of this row.
+// Launches of few rows split each row over several workgroups (phase 1), which hand their
+// lane records to a finalize launch (phase 2).
 //
 // Request layout: for batches up to kInlinePlanMaxB requests every workgroup scans k
 // itself (no separate plan launch); larger batches read per-row descriptors.
@@ -430,10 +431,11 @@ __device__ __forceinline__ void slice_accumulate(const Row& rp, const Row& rq, f
   }
 }
 
-// Streams the wave's slices (s = first, first + step, ...; first = the wave, step = 4 when
-// one workgroup takes the whole row) of the row (pair) into the lane's statistics.  Full bf16 slices of 16-byte-aligned rows: packed, next slice prefetched
-// while the current one is reduced.  The ragged last slice and every other case: fp32,
-// masked.  The lane's first slice sets its offsets from that slice's maxima.
+// Streams the wave's slices s = first, first + step, ... of the row (pair) into the lane's
+// statistics (first = the wave and step = 4 when one workgroup takes the whole row).  Full
+// bf16 slices of 16-byte-aligned rows: packed, next slice prefetched while the current one is
+// reduced.  The ragged last slice and every other case: fp32, masked.  The lane's first slice
+// sets its offsets from that slice's maxima.
 template <int DT, bool VEC, bool PAIR, int MODE>
 __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, float beta, int V,
                                            int n_slices, int first, int step, int lane, LaneAcc& A) {
