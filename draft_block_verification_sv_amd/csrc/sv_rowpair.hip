@@ -856,12 +856,14 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
 
-  // thread 0, the only user: the draft token's range check and the two logits at it, fetched
-  // here so that their latency overlaps the reductions below instead of delaying the stream
+  // thread 0, the only user: the uniform's and the draft token's range checks and the two
+  // logits at the token, fetched here so that their latency overlaps the reductions below
+  // instead of delaying the stream
   int row_flags = ctx.row_flags, x = -1;
   float lpx = 0.0f, lqx = 0.0f;
-  if constexpr (PAIR) {
-    if (tid == 0 && ctx.b >= 0) {
+  if (tid == 0 && ctx.b >= 0) {
+    if (!uniform_ok(a.uniforms[ctx.t])) row_flags |= 16;  // SV_DEV_BAD_UNIFORM
+    if constexpr (PAIR) {
       if (xr < 0 || xr >= V) {
         row_flags |= 4;  // SV_DEV_BAD_TOKEN
       } else {
@@ -947,10 +949,12 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
 // units run last and fill the tail of the grid.  Large batches read the plan's descriptors;
 // otherwise every workgroup scans k itself (8 requests per thread), and unit 0 publishes the
 // call's validity.  Returns false when the workgroup has nothing more to do (a void call,
-// whose outputs it has written).
+// whose outputs it has written).  WITH_T: s_T receives the request's temperature (1 without
+// a temperature array), read in the same round of loads as the lengths.
+template <bool WITH_T>
 __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit, int tid,
                                              int* red_i, int& s_req, int& s_off, int& s_t,
-                                             int& s_void) {
+                                             int& s_void, float* s_T = nullptr) {
   if (a.desc) {  // large batch: descriptors and offsets from sv_plan
     if (a.glob[0]) {
       if (tid == 0 && unit < a.n_d) {
@@ -965,6 +969,7 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
       s_req = rd.b;
       s_off = a.off_t[rd.b];
       s_t = rd.t;
+      if constexpr (WITH_T) *s_T = a.temperature ? a.temperature[rd.b] : 1.0f;
     }
     __syncthreads();
   } else {  // every workgroup scans k itself (B <= kInlinePlanMaxB, 8 requests per thread)
@@ -974,12 +979,15 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
     }
     __syncthreads();
     int kk[kInlinePerThread];
+    float tt[kInlinePerThread];
     int tot = 0, bad = 0;
 #pragma unroll
     for (int e = 0; e < kInlinePerThread; ++e) {
       const int64_t j = static_cast<int64_t>(tid) * kInlinePerThread + e;
       int v = 0;
+      tt[e] = 1.0f;
       if (j < a.B) {
+        if (WITH_T && a.temperature) tt[e] = a.temperature[j];
         v = a.k[j];
         if (v < 1 || v > a.k_max) {
           bad = 1;
@@ -1018,10 +1026,12 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
           s_req = static_cast<int>(j);
           s_off = off;
           s_t = off + (unit - doff);
+          if constexpr (WITH_T) *s_T = tt[e];
         } else if (unit >= a.n_d && unit - a.n_d == j) {
           s_req = static_cast<int>(j);
           s_off = off;
           s_t = off + kk[e] - 1;
+          if constexpr (WITH_T) *s_T = tt[e];
         }
       }
       off += kk[e];
@@ -1046,19 +1056,35 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
 }
 
 // The finalize of a split row: the lane's records of every part, folded in part order, eight
-// in flight at a time (a batch past the last part re-reads it and skips it).
-__device__ __forceinline__ void merge_parts(const RowPairArgs& a, int64_t unit, int tid, LaneAcc& L) {
-  lane_clear(L);
-  const LaneRec* mine = static_cast<const LaneRec*>(a.rec) + unit * a.split * kRowThreads + tid;
-  const int last = a.split - 1;
-  for (int j = 0; j <= last; j += 8) {
-    LaneRec R[8];
+// in flight at a time (a batch past the last part re-reads it and skips it).  The first batch
+// is fetched on entry, before anything else, and folded once the row is resolved.
+struct PartBatch {
+  LaneRec R[8];
+  __device__ __forceinline__ void load(const RowPairArgs& a, int64_t unit, int tid, int j) {
+    const LaneRec* mine = static_cast<const LaneRec*>(a.rec) + unit * a.split * kRowThreads + tid;
+    const int last = a.split - 1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) R[u] = mine[min(j + u, last) * kRowThreads];
+  }
+  __device__ __forceinline__ void fold(LaneAcc& L, int j, int last) const {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (j + u <= last) lane_merge(L, R[u]);
   }
+};
+
+__device__ __forceinline__ void merge_parts(const RowPairArgs& a, int64_t unit, int tid,
+                                            const PartBatch& first, LaneAcc* lacc) {
+  LaneAcc L;
+  lane_clear(L);
+  const int last = a.split - 1;
+  first.fold(L, 0, last);
+  for (int j = 8; j <= last; j += 8) {
+    PartBatch nb;
+    nb.load(a, unit, tid, j);
+    nb.fold(L, j, last);
+  }
+  lacc[tid] = L;
 }
 
 // PHASE 0: one workgroup streams and finishes a row (pair).  PHASE 1: workgroup blockIdx
@@ -1078,14 +1104,12 @@ void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
   __shared__ int s_req, s_off, s_t, s_void;
+  __shared__ float s_T;
   const int tid = thread_index();
   const int64_t blk = block_index();
   const int64_t unit = PHASE == 1 ? blk / a.split : blk;
-  if constexpr (PHASE == 2) {  // the records depend on nothing else: fetch them first
-    LaneAcc L;
-    merge_parts(a, unit, tid, L);
-    lacc[tid] = L;
-  }
+  PartBatch first;  // phase 2: the first records, which depend on nothing else
+  if constexpr (PHASE == 2) first.load(a, unit, tid, 0);
 
   RowCtx ctx;
   ctx.unit = unit;
@@ -1107,6 +1131,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
       return;
     }
     if (tid == 0) a.row_flags[unit] = 0;
+    if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
       rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
@@ -1118,18 +1143,19 @@ void sv_rowpair_kernel(RowPairArgs a) {
     return;
   }
 
-  if (!resolve_unit(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
+  // the draft token (draft units 0 .. n_d-1 are the draft rows in packed order) is fetched by
+  // thread 0 with the lengths and temperatures; it is checked, and the logits at it are
+  // fetched, once the row has been streamed
+  int32_t xr = -1;
+  if (PHASE != 1 && tid == 0 && unit < a.n_d) xr = a.tokens[unit];
+  if (!resolve_unit<true>(a, unit, tid, red_i, s_req, s_off, s_t, s_void, &s_T)) return;
   const int64_t b = s_req;
   const int64_t off = s_off;
   ctx.t = s_t;
   const int i = static_cast<int>(ctx.t - off);
   ctx.b = b;
-  ctx.d = unit < a.n_d ? unit : -1;  // units 0 .. n_d-1 are the draft rows in packed order
-  // thread 0 fetches the draft token with the temperature and the uniform; it is checked, and
-  // the logits at it are fetched, once the row has been streamed
-  int32_t xr = -1;
-  if (PHASE != 1 && tid == 0 && ctx.d >= 0) xr = a.tokens[ctx.d];
-  const float T = a.temperature ? a.temperature[b] : 1.0f;
+  ctx.d = unit < a.n_d ? unit : -1;
+  const float T = s_T;
   int flags = 0;
   ctx.mode = 0;
   ctx.beta = kL2E;
@@ -1141,12 +1167,12 @@ void sv_rowpair_kernel(RowPairArgs a) {
     ctx.mode = 2;
     ctx.beta = kL2E / T;
   }
-  if (PHASE != 1 && !uniform_ok(a.uniforms[ctx.t])) flags |= 16;
   if (PHASE != 1 && i == 0 && tid == 0 && !a.desc) {
     a.off_t[b] = static_cast<int32_t>(off);
     if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
   }
-  ctx.row_flags = flags;  // the token bit is added by thread 0 after the stream
+  ctx.row_flags = flags;  // thread 0 adds the token and uniform bits after the stream
+  if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
   if (ctx.d >= 0) {
     if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
     if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
@@ -1232,7 +1258,7 @@ __global__ __launch_bounds__(kRowThreads) void sv_greedy_kernel(RowPairArgs a) {
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t unit = block_index();
-  if (!resolve_unit(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
+  if (!resolve_unit<false>(a, unit, tid, red_i, s_req, s_off, s_t, s_void)) return;
   const int64_t b = s_req, off = s_off, t = s_t;
   const int kb = a.k[b];
   const int i = static_cast<int>(t - off);

@@ -362,3 +362,37 @@ def test_split_rows_standalone_and_fused():
     assert int(st.item()) & 2
     o = out.cpu().numpy()
     assert np.isnan(o[3]) and np.all(np.isfinite(np.delete(o, 3)))
+
+
+# ----------------------------------------------------------------------------- layouts
+def test_large_batch_uses_the_plan():
+    # more than 2048 requests: per-row descriptors come from the plan kernel
+    B = 2100
+    rng = np.random.default_rng(15)
+    w = make_workload(B=B, k=rng.integers(1, 4, size=B), V=300, dtype="bf16", s=3.0,
+                      sigma=0.8, temperature=rng.choice([0.0, 0.7, 1.0], size=B), delta=0.5,
+                      seed=(15,))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("B=2100 (plan)", s)
+    # a bad length voids the call on this path too
+    dev = to_device(w)
+    bad = w.k.copy()
+    bad[B - 1] = 0
+    dev["k"] = torch.from_numpy(bad).cuda()
+    got = run_gpu(w, dev)
+    assert int(got["device_status"][0]) & 1
+    assert np.all(got["accept_len"] == -1) and np.all(np.isnan(got["rkl"]))
+
+
+def test_invalid_token_in_split_rows():
+    # 7 rows of 40 slices split into parts: the token check happens in the finalize
+    w = make_workload(B=2, k=[3, 2], V=40000, dtype="bf16", temperature=[1.0, 0.7], seed=(16,))
+    w.draft_tokens[1] = -5  # request 0
+    got = run_gpu(w)
+    st = int(got["device_status"][0])
+    assert st & 4 and not (st & 3)
+    assert got["accept_len"][0] == -1 and got["accept_len"][1] >= 0
+    compare(w, got, run_oracle(w, requests=[1]), requests=[1])
+    assert np.all(np.isfinite(got["rkl"]))
