@@ -168,6 +168,16 @@ bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
 
 namespace {
 
+// A workspace that lacks room for the lane records of split rows but holds everything else
+// (one sized for a larger call, say) is used without them: the call then streams each row in
+// one workgroup.
+bool fit_workspace(const void* workspace, size_t bytes, Dims& dm) {
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0) return false;
+  if (bytes >= sv::carve(dm, nullptr, nullptr)) return true;
+  dm.rec_slots = 0;
+  return bytes >= sv::carve(dm, nullptr, nullptr);
+}
+
 // The streaming pass over n_units rows (pairs): one launch, or for small launches the split
 // streaming launch and the finalize launch.
 hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace& ws, int64_t rec_slots,
@@ -199,12 +209,10 @@ sv_status rkl_rows(int32_t dtype, int64_t n_rows, int64_t n_target_rows, int64_t
   if (n_rows < 1 || n_target_rows < 1 || !shape_ok(V, ld_target, ld_draft)) return SV_ERR_SHAPE;
   if (!p_row_index && n_target_rows < n_rows) return SV_ERR_SHAPE;
   if (n_rows >= (int64_t(1) << 31)) return SV_ERR_SHAPE;
-  const Dims dm = rkl_dims(n_rows, V, with_grad);
+  Dims dm = rkl_dims(n_rows, V, with_grad);
   if (!target_logits || !draft_logits || !rkl_out || !device_status) return SV_ERR_NULL;
   if (!(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
-  const size_t need = sv::carve(dm, nullptr, nullptr);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
-    return SV_ERR_WORKSPACE;
+  if (!fit_workspace(workspace, workspace_bytes, dm)) return SV_ERR_WORKSPACE;
 
   Workspace ws{};
   sv::carve(dm, &ws, static_cast<char*>(workspace));
@@ -283,14 +291,12 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   if (B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || !shape_ok(V, ld_target, ld_draft))
     return SV_ERR_SHAPE;
   if (n_draft_rows < B || n_draft_rows > static_cast<int64_t>(B) * k_max) return SV_ERR_SHAPE;
-  const Dims dm = verify_dims(B, k_max, V);
+  Dims dm = verify_dims(B, k_max, V);
   if (!target_logits || !draft_logits || !k || !draft_tokens || !uniforms || !accept_len ||
       !out_tokens || !device_status)
     return SV_ERR_NULL;
   if (rkl_out && !(std::isfinite(delta) && delta > 0.0f)) return SV_ERR_VALUE;
-  const size_t need = sv::carve(dm, nullptr, nullptr);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
-    return SV_ERR_WORKSPACE;
+  if (!fit_workspace(workspace, workspace_bytes, dm)) return SV_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws{};
@@ -468,12 +474,11 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
   if (B < 1 || B > SV_MAX_BATCH || k_max < 1 || k_max > SV_MAX_K || !shape_ok(V, ld_target, V))
     return SV_ERR_SHAPE;
   if (n_draft_rows < B || n_draft_rows > static_cast<int64_t>(B) * k_max) return SV_ERR_SHAPE;
-  const Dims dm = verify_dims(B, k_max, V);
+  Dims dm = verify_dims(B, k_max, V);
   if (!target_logits || !k || !draft_tokens || !accept_len || !out_tokens || !device_status)
     return SV_ERR_NULL;
-  const size_t need = sv::carve(dm, nullptr, nullptr);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % 256) != 0 || workspace_bytes < need)
-    return SV_ERR_WORKSPACE;
+  dm.rec_slots = 0;  // the greedy stream never splits rows
+  if (!fit_workspace(workspace, workspace_bytes, dm)) return SV_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Workspace ws{};

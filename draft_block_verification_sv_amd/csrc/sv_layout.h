@@ -61,11 +61,15 @@ inline int row_split(int64_t n_units, int64_t n_slices) {
   if (P > kSplitSlots / n_units) P = kSplitSlots / n_units;
   return P >= 2 ? static_cast<int>(P) : 1;
 }
-// Record sets to reserve for launches of at least min_units and at most max_units rows.
+// Record sets to reserve for launches of at least min_units and at most max_units rows: the
+// most any such launch splits into.
 inline int64_t split_slots(int64_t min_units, int64_t max_units, int64_t n_slices) {
-  if (SV_SPLIT_TARGET < 2 || min_units > kSplitMaxUnits || n_slices < 16) return 0;
-  const int64_t cap = max_units * 16;
-  return cap < kSplitSlots ? cap : kSplitSlots;
+  int64_t most = 0;
+  for (int64_t n = min_units < 1 ? 1 : min_units; n <= max_units && n <= kSplitMaxUnits; ++n) {
+    const int P = row_split(n, n_slices);
+    if (P > 1 && n * P > most) most = n * P;
+  }
+  return most;
 }
 inline int64_t n_chunks_for(int64_t V) { return (V + kChunk - 1) / kChunk; }
 inline int64_t mass_blocks_for(int64_t n_chunks) {

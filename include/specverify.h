@@ -94,7 +94,10 @@ enum {
 #define SV_MAX_TREE_NODES 1024 /* draft-tree nodes per request */
 
 /* Bytes of workspace sv_verify_block needs for B requests of at most k_max drafts
- * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid. */
+ * over a vocabulary of V entries of the given dtype; 0 if the shape is invalid.  For calls
+ * of at most 128 rows this includes lane records that let several workgroups stream each
+ * row; a workspace without room for them but large enough otherwise (one sized for a larger
+ * batch, say) is accepted, and the call then streams each row in one workgroup. */
 size_t sv_workspace_size(int32_t B, int32_t k_max, int64_t V, int32_t dtype);
 
 /*
@@ -162,7 +165,8 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
                                  int32_t* out_tokens, int32_t* device_status, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace sv_clipped_rkl needs for n_rows row pairs; 0 if invalid. */
+/* Bytes of workspace sv_clipped_rkl needs for n_rows row pairs; 0 if invalid.  As with
+ * sv_workspace_size, the lane records of split rows (n_rows <= 128) are optional. */
 size_t sv_rkl_workspace_size(int64_t n_rows, int64_t V, int32_t dtype);
 
 /*

@@ -224,3 +224,13 @@ def test_read_probe_argument_errors(L):
     assert L.sv_read_probe(16, 0, 16, None) == 2
     assert L.sv_read_probe(16, 1000, 16, None) == 2  # not a multiple of 16
     assert L.sv_read_probe(8, 1024, 16, None) == 4  # not 16-byte aligned
+
+
+def test_split_records_are_optional_in_the_workspace(L):
+    # calls of at most 128 rows reserve lane records for split rows; larger calls do not
+    small = L.sv_workspace_size(1, 15, 151936, 0)
+    big = L.sv_workspace_size(128, 15, 151936, 0)
+    assert small > big > 0
+    assert L.sv_rkl_workspace_size(15, 151936, 0) > L.sv_rkl_workspace_size(129, 151936, 0) > 0
+    # short rows never split
+    assert L.sv_rkl_workspace_size(15, 4096, 0) < 64 * 1024

@@ -396,3 +396,34 @@ def test_invalid_token_in_split_rows():
     assert got["accept_len"][0] == -1 and got["accept_len"][1] >= 0
     compare(w, got, run_oracle(w, requests=[1]), requests=[1])
     assert np.all(np.isfinite(got["rkl"]))
+
+
+def test_workspace_without_split_records():
+    # a workspace sized for B=128 has no room for the lane records of split rows: a one-request
+    # call on it streams each row in one workgroup and still matches the oracle; the same holds
+    # for the standalone reverse-KL on a workspace sized for 129 rows
+    import draft_block_verification_sv_amd as pkg
+    import oracle
+
+    w = workload("single")
+    big = pkg.workspace_size(128, 15, w.V, pkg.SV_BF16)
+    assert big < pkg.workspace_size(1, 15, w.V, pkg.SV_BF16)
+    ws = pkg.alloc_workspace(big, "cuda:0")
+    d = to_device(w)
+    got = run_gpu(w, d, workspace=ws)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("single on a B=128 workspace", s)
+    n = w.n_draft_rows
+    idx = torch.from_numpy(np.arange(n, dtype=np.int32)).cuda()
+    wsr = pkg.alloc_workspace(int(pkg.lib().sv_rkl_workspace_size(129, w.V, pkg.SV_BF16)), "cuda:0")
+    assert wsr.numel() < int(pkg.lib().sv_rkl_workspace_size(n, w.V, pkg.SV_BF16))
+    out, st = pkg.clipped_rkl(d["target"], d["draft"], w.delta, idx, workspace=wsr)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    tl = oracle.widen_logits(w.target[:, : w.V], "bf16")
+    dl = oracle.widen_logits(w.draft[:, : w.V], "bf16")
+    o = out.cpu().numpy().astype(np.float64)
+    for r in range(n):
+        ref = oracle.clipped_rkl_row(tl[r], dl[r], w.delta)
+        assert abs(o[r] - ref["R"]) <= 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21, r
