@@ -178,3 +178,23 @@ def test_bad_lengths_and_pairing_are_flagged():
     h = got["hard_ce"].cpu().numpy()
     assert np.isnan(h[1]) and np.all(np.isfinite(np.delete(h, 1)))
     assert int(got["top1"].cpu().numpy()[1]) == -1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_rows(dtype):
+    # 10 rows of 60 slices: each row is streamed in parts and folded by the finalize launch;
+    # the hard-label cross-entropy needs the first argmax across parts
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=3, k=[4, 1, 5], V=61001, dtype=dtype, s=3.0, sigma=[0.4, 1.2, 2.0],
+                      outlier_frac=0.05, seed=(25, dtype == "f32"))
+    d = to_device(w)
+    idx = _pairing(w)
+    k = torch.from_numpy(w.k.astype(np.int32)).cuda()
+    for delta, alpha in ((1.0, 0.8), (0.01, 0.5)):
+        got = pkg.opd_loss(d["target"], d["draft"], k, delta=delta, alpha=alpha,
+                           p_row_index=torch.from_numpy(idx).cuda())
+        torch.cuda.synchronize()
+        assert int(got["device_status"].item()) == 0
+        worst = _check(w, got, delta, alpha, idx)
+        print(f"[opd] split rows {dtype} delta={delta}: max hard-CE rel err {worst:.2e}", flush=True)
