@@ -115,3 +115,12 @@ def test_bad_token_and_void_calls():
     got = _greedy(w, d)
     assert int(got["device_status"][0]) & 1
     assert np.all(got["accept_len"] == -1) and np.all(got["out_tokens"] == -1)
+
+
+def test_maximum_draft_length():
+    # k_b = k_max = 64: the bonus row of an all-accepted request is row 64
+    w = make_workload(B=3, k=[64, 64, 3], V=2001, dtype="bf16", temperature=0.0, all_accept=(0,),
+                      k_max=64, seed=(45,))
+    got = _greedy(w)
+    assert int(got["device_status"][0]) == 0 and int(got["accept_len"][0]) == 64
+    _exact(w, got, run_oracle(w, with_rkl=False))

@@ -427,3 +427,25 @@ def test_workspace_without_split_records():
     for r in range(n):
         ref = oracle.clipped_rkl_row(tl[r], dl[r], w.delta)
         assert abs(o[r] - ref["R"]) <= 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21, r
+
+
+# ----------------------------------------------------------------------------- maximum length
+def test_maximum_draft_length():
+    # k_b = k_max = 64: 65 target rows per request, one more than a wavefront has lanes.  An
+    # all-accepted sampled request (its bonus row is row 64), an all-accepted greedy request, a
+    # sampled request with rejections, and a short one
+    w = make_workload(B=4, k=[64, 64, 64, 7], V=3001, dtype="bf16",
+                      temperature=[1.0, 0.0, 0.7, 1.0], all_accept=(0, 1), k_max=64, seed=(17,))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    assert got["accept_len"][0] == 64 and got["accept_len"][1] == 64
+    s = compare(w, got, run_oracle(w))
+    _report("k_b = 64", s)
+
+
+def test_maximum_draft_length_split_rows():
+    # one request of 64 drafts at V=40000: 65 rows, streamed in parts
+    w = make_workload(B=1, k=[64], V=40000, dtype="bf16", all_accept=(0,), k_max=64, seed=(18,))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0 and got["accept_len"][0] == 64
+    compare(w, got, run_oracle(w))
