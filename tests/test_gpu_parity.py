@@ -449,3 +449,14 @@ def test_maximum_draft_length_split_rows():
     got = run_gpu(w)
     assert got["device_status"][0] == 0 and got["accept_len"][0] == 64
     compare(w, got, run_oracle(w))
+
+
+def test_maximum_vocabulary():
+    # V = 524288, the largest the library takes: 512 slices per row (split into 16 parts here),
+    # 256 draw chunks, and with a small delta re-read rounds of four failing lanes
+    w = make_workload(B=2, k=[2, 1], V=1 << 19, dtype="bf16", s=4.0, sigma=[0.5, 2.0],
+                      temperature=[1.0, 0.7], delta=0.01, outlier_frac=0.02, seed=(19,))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("V = 524288", s)
