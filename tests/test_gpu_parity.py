@@ -460,3 +460,16 @@ def test_maximum_vocabulary():
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
     _report("V = 524288", s)
+
+
+def test_maximum_batch():
+    # B = 65536 requests (the largest the library takes) of one draft over a tiny vocabulary:
+    # 131072 row pairs and bonus rows laid out by the plan kernel
+    B = 1 << 16
+    rng = np.random.default_rng(20)
+    w = make_workload(B=B, k=1, V=16, dtype="bf16", s=2.0, sigma=0.7,
+                      temperature=rng.choice([0.0, 0.7, 1.0], size=B), delta=0.3, seed=(20,))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report("B = 65536", s)
