@@ -729,6 +729,27 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": stream_name}
 
+    # the practical read ceiling beside it: the library's plain read kernel over the same
+    # number of bytes, timed the same way (after the measured passes)
+    probe = torch.ones(rows_bytes // 4, dtype=torch.int32, device=dev)
+    probe_out = torch.empty(pkg.binding.READ_PROBE_WORDS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pkg.read_probe(probe, probe_out)
+    torch.cuda.synchronize()
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        pkg.read_probe(probe, probe_out)
+    torch.cuda.synchronize()
+    n_probe, ms_probe = pkg.profile_read()["sv_read_probe"]
+    pkg.profile_enable(False)
+    pkg.profile_reset()
+    del probe
+    probe_gbs = (rows_bytes // 4 * 4) / (ms_probe / n_probe * 1e-3) / 1e9
+    roofline["read_ceiling"] = {"kernel": "sv_read_probe", "achieved": round(probe_gbs, 1),
+                                "frac": round(probe_gbs / PEAK_HBM_GBS, 4),
+                                "kernel_over_ceiling": round(achieved / probe_gbs, 4)}
+
     value = n_d / (ms_per_step * 1e-3)
     whole_gbs = (rows_bytes + meta_bytes) / (ms_per_step * 1e-3) / 1e9
     res = {
