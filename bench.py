@@ -64,6 +64,17 @@ def _oracle_request(b):
     return int(w.k[b])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, n_requests: int) -> dict:
     """Runs before anything touches the GPU, so the forked workers inherit no device state."""
     import multiprocessing as mp
@@ -78,6 +89,7 @@ def cpu_baseline(w, n_requests: int) -> dict:
         positions = sum(pool.map(_oracle_request, reqs, chunksize=1))
     dt = time.perf_counter() - t0
     return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions, all "
                       f"outputs incl. the clipped rKL), float64 NumPy, {cores} worker processes, "
                       f"{dt:.2f} s wall"}
@@ -144,6 +156,7 @@ def cpu_baseline_greedy(w, n_requests: int) -> dict:
         positions = sum(pool.map(_oracle_greedy_request, reqs, chunksize=1))
     dt = time.perf_counter() - t0
     return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions at "
                       f"temperature 0, no rKL), float64 NumPy, {cores} worker processes, "
                       f"{dt:.2f} s wall"}
@@ -698,6 +711,55 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
+    # device time of each call: HIP events around every call on the call's stream, in a pass
+    # of its own (median, p10, p90)
+    stream = torch.cuda.current_stream()
+    call_us = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        call_us.append((e0, e1))
+    torch.cuda.synchronize()
+    call_us = np.array([1e3 * a.elapsed_time(b) for a, b in call_us])
+    call_stats = {"median": round(float(np.median(call_us)), 2),
+                  "p10": round(float(np.percentile(call_us, 10)), 2),
+                  "p90": round(float(np.percentile(call_us, 90)), 2)}
+
+    # realised acceptance: mean tokens per request-round and the per-position acceptance rate
+    # (accepted at i among requests that reached i)
+    al = out["accept_len"].cpu().numpy().astype(np.int64)
+    kk = w.k.astype(np.int64)
+    acc_profile = []
+    for i in range(int(w.k_max)):
+        reached = int(np.sum((al >= i) & (kk > i)))
+        acc_profile.append(round(float(np.sum(al > i)) / reached, 4) if reached else None)
+    realised = {"mean_tau": round(float(np.mean(al + 1)), 3), "acc_per_position": acc_profile}
+
+    # inputs that fit the 256 MB last-level cache are also timed from HBM: the call rotates
+    # through enough copies of the logits that each is evicted before it is read again
+    cold = None
+    in_bytes = (w.n_target_rows + w.n_draft_rows) * w.V * (2 if w.dtype == "bf16" else 4)
+    if in_bytes < (512 << 20):
+        n_sets = min(256, max(3, -(-(768 << 20) // in_bytes)))
+        sets = [(target.clone(), draft.clone()) for _ in range(n_sets)]
+        torch.cuda.synchronize()
+        for j in range(args.warmup):
+            tg, dr = sets[j % n_sets]
+            pkg.verify_block(tg, dr, k, toks, uni, temp, w.delta, k_max=w.k_max, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j in range(args.steps):
+            tg, dr = sets[j % n_sets]
+            pkg.verify_block(tg, dr, k, toks, uni, temp, w.delta, k_max=w.k_max, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        ms_cold = 1e3 * (time.perf_counter() - t0) / args.steps
+        cold = {"ms_per_step": round(ms_cold, 5), "value": round(w.n_draft_rows / (ms_cold * 1e-3), 1),
+                "input_sets": n_sets, "bytes_per_set": in_bytes}
+        del sets
+        log(f"[bench] rotating {n_sets} input sets: {ms_cold:.4f} ms/step")
+
     # per-kernel durations: HIP events the library records around each launch on the
     # call's stream, over a second pass of the same number of steps
     pkg.profile_reset()
@@ -772,6 +834,9 @@ def main():
         "step_hbm_gbs": round(whole_gbs, 1),
         "step_frac_of_peak": round(whole_gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {n: round(v["avg_us"], 2) for n, v in kernels.items()},
+        "call_us": call_stats,
+        "inputs_from_hbm": cold,
+        "realised": realised,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }
