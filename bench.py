@@ -54,14 +54,55 @@ _W = None  # the workload, inherited by the forked cpu_baseline workers
 
 
 def _oracle_request(b):
-    # cpu_baseline worker: the oracle, unchanged, on one request
+    # cpu_baseline worker: the oracle, unchanged, on one request; returns that request's outputs
     import oracle
 
     w = _W
-    oracle.verify_block(target=w.target, draft=w.draft, dtype=w.dtype, V=w.V, k=w.k,
-                        draft_tokens=w.draft_tokens, uniforms=w.uniforms,
-                        temperature=w.temperature, delta=w.delta, requests=[b])
-    return int(w.k[b])
+    r = oracle.verify_block(target=w.target, draft=w.draft, dtype=w.dtype, V=w.V, k=w.k,
+                            draft_tokens=w.draft_tokens, uniforms=w.uniforms,
+                            temperature=w.temperature, delta=w.delta, requests=[b])
+    ot, od, kb = int(w.target_offsets[b]), int(w.draft_offsets[b]), int(w.k[b])
+    sl = slice(od, od + kb)
+    return b, {"accept_len": int(r["accept_len"][b]), "tokens": r["out_tokens"][ot: ot + kb + 1],
+               "rkl": r["rkl"][sl], "rkl_l1": r["rkl_l1"][sl], "p_at": r["p_at_draft"][sl],
+               "accept_margin": r["accept_margin"][sl], "token_margin": float(r["token_margin"][b])}
+
+
+def parity_sample(w, out, refs) -> dict:
+    """The GPU outputs of the timed call against the oracle's on the baseline's requests:
+    accept lengths and tokens exact, or a boundary flip when the first differing decision had
+    an oracle margin <= 1e-5; the clipped rKL's error relative to max(|R|, sum |min(delta, t)|)
+    and as a fraction of the parity bar (<= 1 passes); p_T(x_i)'s relative error."""
+    import numpy as np
+
+    al = out["accept_len"].cpu().numpy()
+    ot = out["out_tokens"].cpu().numpy()
+    rkl = out["rkl"].cpu().numpy().astype(np.float64)
+    pat = out["p_at_draft"].cpu().numpy().astype(np.float64)
+    exact = flips = wrong = 0
+    max_rkl = max_bar = max_p = 0.0
+    for b, r in refs:
+        o_t, o_d, kb = int(w.target_offsets[b]), int(w.draft_offsets[b]), int(w.k[b])
+        if int(al[b]) == r["accept_len"] and np.array_equal(ot[o_t: o_t + kb + 1], r["tokens"]):
+            exact += 1
+        else:
+            n = min(int(al[b]), r["accept_len"])  # the first position the two decided apart
+            margin = (r["accept_margin"][n] if int(al[b]) != r["accept_len"] and 0 <= n < kb
+                      else r["token_margin"])
+            if margin <= 1e-5:
+                flips += 1
+            else:
+                wrong += 1
+        g = rkl[o_d: o_d + kb]
+        scale = np.maximum(np.abs(r["rkl"]), r["rkl_l1"])
+        max_rkl = max(max_rkl, float(np.max(np.abs(g - r["rkl"]) / scale)))
+        # against the parity bar: 1e-5 of the scale plus the fp32 accumulation floor 2^-21
+        max_bar = max(max_bar, float(np.max(np.abs(g - r["rkl"]) / (1e-5 * scale + 2.0**-21))))
+        ok = np.isfinite(r["p_at"]) & (r["p_at"] > 0)
+        if np.any(ok):
+            max_p = max(max_p, float(np.max(np.abs(pat[o_d: o_d + kb][ok] - r["p_at"][ok]) / r["p_at"][ok])))
+    return {"requests": len(refs), "exact": exact, "boundary_flips": flips, "mismatches": wrong,
+            "max_rkl_rel": max_rkl, "max_rkl_err_over_bar": max_bar, "max_p_rel": max_p}
 
 
 def cpu_model() -> str:
@@ -86,9 +127,10 @@ def cpu_baseline(w, n_requests: int) -> dict:
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
-        positions = sum(pool.map(_oracle_request, reqs, chunksize=1))
+        refs = pool.map(_oracle_request, reqs, chunksize=1)
     dt = time.perf_counter() - t0
-    return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+    positions = sum(int(w.k[b]) for b, _ in refs)
+    return refs, {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions, all "
                       f"outputs incl. the clipped rKL), float64 NumPy, {cores} worker processes, "
@@ -662,7 +704,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
-        cpu = cpu_baseline(w, args.cpu_requests)
+        refs, cpu = cpu_baseline(w, args.cpu_requests)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} positions/s")
 
     pkg.lib()
@@ -710,6 +752,10 @@ def main():
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    if cpu is not None:  # the timed call's outputs against the oracle's on the sampled requests
+        cpu["parity"] = parity_sample(w, out, refs)
+        log(f"[bench] parity on the baseline's requests: {json.dumps(cpu['parity'])}")
 
     # device time of each call: HIP events around every call on the call's stream, in a pass
     # of its own (median, p10, p90)
