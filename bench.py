@@ -753,6 +753,58 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
+    # per-kernel durations: HIP events the library records around each launch on the
+    # call's stream, over a second pass of the same number of steps
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = pkg.profile_read()
+    pkg.profile_enable(False)
+    pkg.profile_reset()
+    kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in kt.items()}
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    esize = 2 if w.dtype == "bf16" else 4
+    rows_bytes = (w.n_target_rows + n_d) * V * esize  # every logit read once
+    meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
+    # small launches split each row over several workgroups: the streaming launch then reads
+    # every logit and a short finalize launch folds the parts
+    stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_part"
+    rows_us = kernels[stream_name]["avg_us"]
+    achieved = rows_bytes / (rows_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == args.workload:
+            traffic = c.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": stream_name}
+
+    # the practical read ceiling beside it: the library's plain read kernel over the same
+    # number of bytes, timed the same way (after the measured passes)
+    probe = torch.ones(rows_bytes // 4, dtype=torch.int32, device=dev)
+    probe_out = torch.empty(pkg.binding.READ_PROBE_WORDS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pkg.read_probe(probe, probe_out)
+    torch.cuda.synchronize()
+    pkg.profile_reset()
+    pkg.profile_enable(True)
+    for _ in range(args.steps):
+        pkg.read_probe(probe, probe_out)
+    torch.cuda.synchronize()
+    n_probe, ms_probe = pkg.profile_read()["sv_read_probe"]
+    pkg.profile_enable(False)
+    pkg.profile_reset()
+    del probe
+    probe_gbs = (rows_bytes // 4 * 4) / (ms_probe / n_probe * 1e-3) / 1e9
+    roofline["read_ceiling"] = {"kernel": "sv_read_probe", "achieved": round(probe_gbs, 1),
+                                "frac": round(probe_gbs / PEAK_HBM_GBS, 4),
+                                "kernel_over_ceiling": round(achieved / probe_gbs, 4)}
+
     if cpu is not None:  # the timed call's outputs against the oracle's on the sampled requests
         cpu["parity"] = parity_sample(w, out, refs)
         log(f"[bench] parity on the baseline's requests: {json.dumps(cpu['parity'])}")
@@ -805,58 +857,6 @@ def main():
                 "input_sets": n_sets, "bytes_per_set": in_bytes}
         del sets
         log(f"[bench] rotating {n_sets} input sets: {ms_cold:.4f} ms/step")
-
-    # per-kernel durations: HIP events the library records around each launch on the
-    # call's stream, over a second pass of the same number of steps
-    pkg.profile_reset()
-    pkg.profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = pkg.profile_read()
-    pkg.profile_enable(False)
-    pkg.profile_reset()
-    kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in kt.items()}
-    log(f"[bench] kernels: {json.dumps(kernels)}")
-
-    esize = 2 if w.dtype == "bf16" else 4
-    rows_bytes = (w.n_target_rows + n_d) * V * esize  # every logit read once
-    meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
-    # small launches split each row over several workgroups: the streaming launch then reads
-    # every logit and a short finalize launch folds the parts
-    stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_part"
-    rows_us = kernels[stream_name]["avg_us"]
-    achieved = rows_bytes / (rows_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS_FILE):
-        with open(COUNTERS_FILE) as f:
-            c = json.load(f)
-        if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == args.workload:
-            traffic = c.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": stream_name}
-
-    # the practical read ceiling beside it: the library's plain read kernel over the same
-    # number of bytes, timed the same way (after the measured passes)
-    probe = torch.ones(rows_bytes // 4, dtype=torch.int32, device=dev)
-    probe_out = torch.empty(pkg.binding.READ_PROBE_WORDS, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        pkg.read_probe(probe, probe_out)
-    torch.cuda.synchronize()
-    pkg.profile_reset()
-    pkg.profile_enable(True)
-    for _ in range(args.steps):
-        pkg.read_probe(probe, probe_out)
-    torch.cuda.synchronize()
-    n_probe, ms_probe = pkg.profile_read()["sv_read_probe"]
-    pkg.profile_enable(False)
-    pkg.profile_reset()
-    del probe
-    probe_gbs = (rows_bytes // 4 * 4) / (ms_probe / n_probe * 1e-3) / 1e9
-    roofline["read_ceiling"] = {"kernel": "sv_read_probe", "achieved": round(probe_gbs, 1),
-                                "frac": round(probe_gbs / PEAK_HBM_GBS, 4),
-                                "kernel_over_ceiling": round(achieved / probe_gbs, 4)}
 
     value = n_d / (ms_per_step * 1e-3)
     whole_gbs = (rows_bytes + meta_bytes) / (ms_per_step * 1e-3) / 1e9
