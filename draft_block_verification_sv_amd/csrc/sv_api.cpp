@@ -139,6 +139,7 @@ Dims verify_dims(int64_t B, int64_t k_max, int64_t V) {
   d.n_d = B * k_max;
   d.V = V;
   d.n_units = d.n_t;
+  d.kmax1 = k_max + 1;
   d.n_slices = sv::n_slices_for(V);
   d.n_chunks = sv::n_chunks_for(V);
   d.rec_slots = sv::split_slots(2 * B, d.n_t, d.n_slices);  // a call has between 2B and B (k_max + 1) rows
@@ -341,14 +342,8 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.p_at = p_at_draft;
   ra.q_at = q_at_draft;
   ra.device_status = device_status;
-  ra.row_flags = ws.row_flags;
-  ra.t_off = ws.t_off;
-  ra.t_lz = ws.t_lz;
-  ra.t_beta = ws.t_beta;
-  ra.t_arg = ws.t_arg;
-  ra.d_off = ws.d_off;
-  ra.d_lz = ws.d_lz;
-  ra.acc = ws.acc;
+  ra.rowout = ws.rowout;
+  ra.kmax1 = k_max + 1;
   ra.arrive = ws.arrive;
   if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR) != hipSuccess) return SV_ERR_HIP;
 
@@ -367,14 +362,8 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.temperature = temperature;
   sa.tokens = draft_tokens;
   sa.uniforms = uniforms;
-  sa.row_flags = ws.row_flags;
-  sa.t_off = ws.t_off;
-  sa.t_lz = ws.t_lz;
-  sa.t_beta = ws.t_beta;
-  sa.t_arg = ws.t_arg;
-  sa.d_off = ws.d_off;
-  sa.d_lz = ws.d_lz;
-  sa.acc = ws.acc;
+  sa.rowout = ws.rowout;
+  sa.kmax1 = k_max + 1;
   sa.chunk_mass = ws.chunk_mass;
   sa.arrive = ws.arrive;
   sa.mass_blocks = static_cast<int32_t>(sv::mass_blocks_for(n_chunks));
@@ -512,9 +501,8 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
   ra.glob = ws.glob;
   ra.off_t = ws.off_t;
   ra.device_status = device_status;
-  ra.row_flags = ws.row_flags;
-  ra.t_arg = ws.t_arg;
-  ra.acc = ws.acc;
+  ra.rowout = ws.rowout;
+  ra.kmax1 = k_max + 1;
   if (timed(K_GREEDY, st, [&] { return sv::launch_greedy(dtype, vec, ra, st); }) != hipSuccess)
     return SV_ERR_HIP;
 
@@ -529,14 +517,8 @@ sv_status sv_verify_block_greedy(int32_t dtype, int32_t B, int32_t k_max, int64_
   sa.off_t = ws.off_t;
   sa.k = k;
   sa.tokens = draft_tokens;
-  sa.row_flags = ws.row_flags;
-  sa.t_off = ws.t_off;
-  sa.t_lz = ws.t_lz;
-  sa.t_beta = ws.t_beta;
-  sa.t_arg = ws.t_arg;
-  sa.d_off = ws.d_off;
-  sa.d_lz = ws.d_lz;
-  sa.acc = ws.acc;
+  sa.rowout = ws.rowout;
+  sa.kmax1 = k_max + 1;
   sa.chunk_mass = ws.chunk_mass;
   sa.arrive = ws.arrive;
   sa.force_greedy = true;

@@ -379,19 +379,21 @@ __device__ __forceinline__ void column_masses(const SampleArgs& a, int64_t t, in
 }
 
 // A request's state: whether the call is void, T_b, length, first target row, input
-// flags (OR over its k_b + 1 rows), the first rejected position a_b, the final uniform,
-// and what the draw needs of row a_b (its exp2 offsets, its argmax).  Gathered by one
-// wave in two dependent rounds of loads: (call flag, T_b, k_b, first row), then lane i
-// reads everything of row i at once (and its draft token into *tok) and the values of
-// row a_b are taken from lane a_b by a shuffle.
+// flags (OR over its k_b + 1 rows), the first rejected position a_b, and what the draw needs
+// of row a_b (its exp2 offsets, its argmax).  Gathered by one wave in one round of loads: the
+// call flag, T_b, k_b, the first target row, and lane i's slot of position i (the slots sit
+// at a fixed stride per request, so they need nothing from the other loads); the values of
+// row a_b are taken from lane a_b by a shuffle.  Lane i's draft token (into *tok) and uniform
+// (into *u) are fetched after that round and used only by the pick and the emit.
 struct ReqState {
   int void_call, kb, flags, alen, targ;
-  float T, ufin;
+  float T;
   int64_t off;
   RowScale k;
 };
 
-__device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int64_t b, int* tok) {
+__device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int64_t b, int* tok,
+                                                       float* u) {
   const int lane = threadIdx.x & 63;
   ReqState r;
   r.k.beta = r.k.offp = r.k.lzp = r.k.offq = r.k.lzq = 0.f;
@@ -400,31 +402,29 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
   r.T = a.force_greedy ? 0.0f : (a.temperature ? a.temperature[b] : 1.0f);
   r.kb = a.k[b];
   r.off = a.off_t[b];
-  const int64_t t = r.off + lane, d = r.off - b + lane;
+  RowOut ro{};
+  if (lane < a.kmax1) ro = a.rowout[b * a.kmax1 + lane];
   int f = 0, targ = 0;
   bool rej = false;
-  float beta = 0.f, offp = 0.f, lzp = 0.f, offq = 0.f, lzq = 0.f, u = 0.f;
+  float beta = 0.f, offp = 0.f, lzp = 0.f, offq = 0.f, lzq = 0.f;
   *tok = -1;
+  *u = 0.f;
   if (!r.void_call) {
     if (lane <= r.kb) {
-      f = a.row_flags[t];
-      beta = a.t_beta[t];
-      offp = a.t_off[t];
-      lzp = a.t_lz[t];
-      targ = a.t_arg[t];
-      if (a.uniforms) u = a.uniforms[t];
+      f = ro.flags;
+      beta = ro.beta;
+      offp = ro.offp;
+      lzp = ro.lzp;
+      targ = ro.targ;
+      if (a.uniforms) *u = a.uniforms[r.off + lane];
     }
     if (lane < r.kb) {
-      rej = !a.acc[d];
-      offq = a.d_off[d];
-      lzq = a.d_lz[d];
-      *tok = a.tokens[d];
+      rej = !ro.acc;
+      offq = ro.offq;
+      lzq = ro.lzq;
+      *tok = a.tokens[r.off - b + lane];
     }
-  }
-  r.ufin = r.kb < 64 ? __shfl(u, r.kb < 0 ? 0 : r.kb, 64) : 0.f;
-  if (r.kb >= 64 && !r.void_call) {  // k_b = 64: the 65th row
-    if (lane == 0) f |= a.row_flags[r.off + 64];
-    if (a.uniforms) r.ufin = a.uniforms[r.off + 64];
+    if (r.kb >= 64 && lane == 0) f |= a.rowout[b * a.kmax1 + 64].flags;  // k_b = 64: row 64
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) f |= __shfl_xor(f, m, 64);
@@ -439,14 +439,20 @@ __device__ __forceinline__ ReqState wave_request_state(const SampleArgs& a, int6
     r.k.lzq = __shfl(lzq, r.alen, 64);
     r.targ = __shfl(targ, r.alen, 64);
   } else if (!r.void_call) {  // k_b = 64 and every draft accepted: the bonus row is row 64
-    const int64_t tb = r.off + 64;
-    r.k.beta = a.t_beta[tb];
-    r.k.offp = a.t_off[tb];
-    r.k.lzp = a.t_lz[tb];
+    const RowOut rb = a.rowout[b * a.kmax1 + 64];
+    r.k.beta = rb.beta;
+    r.k.offp = rb.offp;
+    r.k.lzp = rb.lzp;
     r.k.offq = r.k.lzq = 0.f;
-    r.targ = a.t_arg[tb];
+    r.targ = rb.targ;
   }
   return r;
+}
+
+// The request's final uniform (slot k_b), from the lanes' uniforms.
+__device__ __forceinline__ float final_uniform(const SampleArgs& a, const ReqState& r, float u) {
+  if (r.kb < 64) return __shfl(u, r.kb < 0 ? 0 : r.kb, 64);
+  return a.uniforms ? a.uniforms[r.off + 64] : 0.f;
 }
 
 
@@ -548,8 +554,9 @@ void sv_draw_kernel(SampleArgs a) {
   const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int my_tok;  // lane i holds draft token i of the request
-  const ReqState rq = wave_request_state(a, b, &my_tok);
+  int my_tok;    // lane i holds draft token i of the request
+  float my_u;    // and the uniform of target row i
+  const ReqState rq = wave_request_state(a, b, &my_tok, &my_u);
 
   if (rq.void_call) {  // void call: the layout is unknown, so -1 everywhere, strided by B
     if (g == 0) {
@@ -639,7 +646,7 @@ void sv_draw_kernel(SampleArgs a) {
   }
   double excl = __shfl_up(incl, 1, 64);
   if (lane == 0) excl = 0.0;
-  const double thr = static_cast<double>(rq.ufin) * Z;
+  const double thr = static_cast<double>(final_uniform(a, rq, my_u)) * Z;
   // chunk c of the lane spans [s_c, s_{c+1}), s_{c_lo} = excl, s_{c+1} = s_c + m_c, and the
   // lane's last chunk ends at incl: the intervals tile [0, Z) exactly
   int sel = -1, last = -1;

@@ -48,14 +48,9 @@ struct RowPairArgs {
   float* p_at;     // nullable
   float* q_at;     // nullable
   int32_t* device_status;
-  int32_t* row_flags;
-  float* t_off;
-  float* t_lz;
-  float* t_beta;
-  int32_t* t_arg;
-  float* d_off;
-  float* d_lz;
-  int32_t* acc;
+  int32_t* row_flags;  // reverse-KL calls: per draft row
+  RowOut* rowout;      // verification: per (request, position), for the draw
+  int32_t kmax1;       // k_max + 1: slots per request in rowout
   int32_t* arrive;  // nullable: per-request draw counters, zeroed here for the draw kernel
   // Rows split over several workgroups (small launches): phase 0 streams and finalizes each
   // row (pair) in one workgroup; phase 1 streams part `blockIdx % split` of row (pair)
@@ -80,14 +75,8 @@ struct SampleArgs {
   const float* temperature;
   const int32_t* tokens;
   const float* uniforms;
-  const int32_t* row_flags;
-  const float* t_off;
-  const float* t_lz;
-  const float* t_beta;
-  const int32_t* t_arg;
-  const float* d_off;
-  const float* d_lz;
-  const int32_t* acc;
+  const RowOut* rowout;  // [B * kmax1] per (request, position)
+  int32_t kmax1;
   double* chunk_mass;   // [B * n_chunks]: each draw workgroup's chunk masses
   int32_t* arrive;      // [B]: draw workgroups of the request done; the last one picks
   bool force_greedy;    // every request greedy (sv_verify_block_greedy): T_b = 0

@@ -83,6 +83,21 @@ struct RowDesc {
   int32_t b;  // request
 };
 
+// What the draw needs of one position i of request b, at slot b (k_max + 1) + i, so that the
+// draw reads a request's positions without first reading where its rows start.  Written by the
+// streaming pass (or the greedy stream) for i = 0 .. k_b.
+struct RowOut {
+  int32_t flags;  // SV_DEV_* bits found on the position's rows
+  int32_t acc;    // draft i accepted (i < k_b)
+  float beta;     // exp2 scale of the target row's temperature (log2(e) / T_b)
+  float offp;     // -round(LZ) of p_T: p_T(y) = 2^(fma(l_y, beta, offp) - lzp)
+  float lzp;
+  float offq;     // likewise for q_T of draft row i (i < k_b)
+  float lzq;
+  int32_t targ;   // first argmax of the target row
+};
+static_assert(sizeof(RowOut) == 32, "two 16-byte loads per slot");
+
 // Per draft row, from the OPD forward pass for the gradient pass: both log2 normalisers,
 // sum_y q_y g_y (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)) and the target's top-1.
 struct RowStats {
@@ -96,14 +111,8 @@ struct Workspace {
   int32_t* glob;       // [4]: [0] call void (bad lengths / row count)
   int32_t* off_t;      // [B + 1] first target row of each request
   RowDesc* desc;       // [n_t] per unit (batches larger than kInlinePlanMaxB)
-  int32_t* row_flags;  // [n_units] SV_DEV_* bits found on each row
-  float* t_off;        // [n_t] -(M * beta) for the sampler's temperature
-  float* t_lz;         // [n_t] log2 normaliser relative to that offset
-  float* t_beta;       // [n_t] exp2 scale of the sampler's temperature (log2(e) / T_b)
-  int32_t* t_arg;      // [n_t] argmax (lowest id)
-  float* d_off;        // [n_d]
-  float* d_lz;         // [n_d]
-  int32_t* acc;        // [n_d] acceptance flag
+  int32_t* row_flags;  // [n_units] SV_DEV_* bits found on each row (reverse-KL calls)
+  RowOut* rowout;      // [B * kmax1] per position, for the draw (verification calls)
   double* chunk_mass;  // [B * n_chunks] draw mass of each chunk of each request's draw row
   int32_t* arrive;     // [B] draw workgroups of each request done (zeroed by the streaming pass)
   void* rec;           // [rec_slots * kRowThreads] lane records of split rows
@@ -113,6 +122,7 @@ struct Workspace {
 
 struct Dims {
   int64_t B, n_t, n_d, V, n_units, n_slices, n_chunks;
+  int64_t kmax1;   // positions per request slot block: k_max + 1 (verification), else 0
   int64_t n_grad;  // rows of the OPD gradient pass (0 otherwise)
   int64_t rec_slots;  // record sets for split rows (0: launches of this size never split)
 };
@@ -131,13 +141,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.off_t = reinterpret_cast<int32_t*>(take((d.B + 1) * sizeof(int32_t)));
   w.desc = reinterpret_cast<RowDesc*>(take(d.n_t * sizeof(RowDesc)));
   w.row_flags = reinterpret_cast<int32_t*>(take(d.n_units * 4));
-  w.t_off = reinterpret_cast<float*>(take(d.n_t * 4));
-  w.t_lz = reinterpret_cast<float*>(take(d.n_t * 4));
-  w.t_beta = reinterpret_cast<float*>(take(d.n_t * 4));
-  w.t_arg = reinterpret_cast<int32_t*>(take(d.n_t * 4));
-  w.d_off = reinterpret_cast<float*>(take(d.n_d * 4));
-  w.d_lz = reinterpret_cast<float*>(take(d.n_d * 4));
-  w.acc = reinterpret_cast<int32_t*>(take(d.n_d * 4));
+  w.rowout = reinterpret_cast<RowOut*>(take(static_cast<size_t>(d.B * d.kmax1) * sizeof(RowOut)));
   w.chunk_mass = reinterpret_cast<double*>(take(d.B * d.n_chunks * sizeof(double)));
   w.arrive = reinterpret_cast<int32_t*>(take(d.B * sizeof(int32_t)));
   w.rec = take(static_cast<size_t>(d.rec_slots) * kRowThreads * kLaneRecBytes);

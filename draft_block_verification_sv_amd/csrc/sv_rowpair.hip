@@ -816,6 +816,7 @@ struct RowCtx {
   int part;      // which part of it, when rows are split over several workgroups
   int64_t t, d;  // target row, draft row (-1: bonus row)
   int64_t b;     // request (-1: clipped reverse-KL only)
+  int pos;       // position of the target row in its request (verification)
   int mode;      // 0: T = 1, 1: greedy, 2: other T
   float beta;
   int row_flags;
@@ -883,11 +884,12 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     argp = block_min_i(A.amax == Mx ? A.aidx : 0x7fffffff, red_i);
   }
   const float scale_T = (MODE == 2) ? ctx.beta : kL2E;
+  RowOut* slot = ctx.b >= 0 ? a.rowout + ctx.b * a.kmax1 + ctx.pos : nullptr;
   if (tid == 0 && ctx.b >= 0) {
-    draw_offsets(LZTp, a.t_off + ctx.t, a.t_lz + ctx.t);
-    a.t_beta[ctx.t] = scale_T;
-    a.t_arg[ctx.t] = argp;
-    a.row_flags[ctx.t] = row_flags;
+    draw_offsets(LZTp, &slot->offp, &slot->lzp);
+    slot->beta = scale_T;
+    slot->targ = argp;
+    slot->flags = row_flags;
   }
   if constexpr (!PAIR) return;
 
@@ -923,7 +925,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     }
   }
   if (tid == 0 && ctx.b >= 0) {
-    draw_offsets(LZTq, a.d_off + ctx.d, a.d_lz + ctx.d);
+    draw_offsets(LZTq, &slot->offq, &slot->lzq);
     int accept = 0;
     if (row_flags == 0) {  // the request's own flags are combined by the sampler
       const double Lp = static_cast<double>(lpx) * scale_T - LZTp;  // log2 p_T(x)
@@ -940,7 +942,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       if (a.p_at) store_nan(a.p_at + ctx.d);
       if (a.q_at) store_nan(a.q_at + ctx.d);
     }
-    a.acc[ctx.d] = accept;
+    slot->acc = accept;
   }
 }
 
@@ -1154,6 +1156,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
   ctx.t = s_t;
   const int i = static_cast<int>(ctx.t - off);
   ctx.b = b;
+  ctx.pos = i;
   ctx.d = unit < a.n_d ? unit : -1;
   const float T = s_T;
   int flags = 0;
@@ -1189,7 +1192,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
 // target rows' first argmax is needed (DFlash notes, Section 5.2, worked example #4), so one
 // workgroup streams one target row and nothing else.  Per lane, the running maximum and the
 // slice where it first appeared; the lanes holding the row maximum then look again at that one
-// slice for the first column.  Writes t_arg, the acceptance flag x_i == argmax (draft-position
+// slice for the first column.  Writes the argmax, the acceptance flag x_i == argmax (draft-position
 // rows) and the row's token flag; the pick kernel then scans and emits.
 template <int DT, bool VEC>
 __device__ __forceinline__ void stream_max(const void* prow, int V, int n_slices, int wave,
@@ -1283,14 +1286,15 @@ __global__ __launch_bounds__(kRowThreads) void sv_greedy_kernel(RowPairArgs a) {
   }
   const int argp = block_min_i(col, red_i);
   if (tid == 0) {
-    a.t_arg[t] = argp;
+    RowOut* slot = a.rowout + b * a.kmax1 + i;
+    slot->targ = argp;
     int flags = 0;
     if (d >= 0) {
       const int32_t x = a.tokens[d];
       if (x < 0 || x >= a.V) flags |= 4;  // SV_DEV_BAD_TOKEN
-      a.acc[d] = (flags == 0 && x == argp) ? 1 : 0;
+      slot->acc = (flags == 0 && x == argp) ? 1 : 0;
     }
-    a.row_flags[t] = flags;
+    slot->flags = flags;
   }
 }
 
