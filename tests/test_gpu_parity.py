@@ -99,10 +99,15 @@ def test_small_delta_rereads_clipped_slices(delta):
 # ----------------------------------------------------------------------------- full-size workloads
 def test_single_request_full_vocab():
     w = workload("single")
-    got = run_gpu(w)
+    dev = to_device(w)
+    got = run_gpu(w, dev)
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
     _report("single", s)
+    # split rows fold their parts in a fixed order: bitwise deterministic too
+    again = run_gpu(w, dev)
+    for key in ("accept_len", "out_tokens", "rkl", "p_at_draft", "q_at_draft"):
+        np.testing.assert_array_equal(got[key], again[key])
 
 
 def test_ragged_batch_mixed_temperatures():
