@@ -224,19 +224,21 @@ struct LaneAcc {
   float kp, kq, ktp, ktq;      // offsets: T = 1 for p and q; T_b (rows with T_b not in {0, 1})
   double sp, sq, stp, stq, w;  // sums of 2^(l L2E - k), of 2^(l beta - kt), of E_q (l_q - l_p)
   float dmax;                  // max of l_q - l_p
+  float xmax;                  // max of E_q (l_q - l_p), E_q = 2^(l_q L2E - kq) as in w
   float mhp, mlp, mhq, mlq;    // running maxima of l_p and l_q (see fold_max)
   float amax;                  // greedy rows: the lane's largest target logit ...
   int aidx;                    // ... and its first column
 };
 
 // What a part of a split row hands to the finalize, per lane: the offsets and sums after the
-// top correction, the largest l_q - l_p and the greedy argmax (the running maxima have no use
-// once the sums are corrected).
+// top correction, the largest l_q - l_p and E_q (l_q - l_p), and the greedy argmax (the running
+// maxima have no use once the sums are corrected).
 struct LaneRec {
   float kp, kq, ktp, ktq;
   double sp, sq, stp, stq, w;
   float dmax, amax;
-  int aidx, pad;
+  int aidx;
+  float xmax;
 };
 static_assert(sizeof(LaneRec) <= kLaneRecBytes, "lane records must fit their workspace slots");
 
@@ -254,14 +256,14 @@ __device__ __forceinline__ LaneRec lane_record(const LaneAcc& A) {
   R.dmax = A.dmax;
   R.amax = A.amax;
   R.aidx = A.aidx;
-  R.pad = 0;
+  R.xmax = A.xmax;
   return R;
 }
 
 __device__ __forceinline__ void lane_clear(LaneAcc& A) {
   A.kp = A.kq = A.ktp = A.ktq = 0.0f;
   A.sp = A.sq = A.stp = A.stq = A.w = 0.0;
-  A.dmax = -INFINITY;
+  A.dmax = A.xmax = -INFINITY;
   A.mhp = A.mlp = A.mhq = A.mlq = -INFINITY;
   A.amax = -INFINITY;
   A.aidx = 0x7fffffff;
@@ -318,6 +320,7 @@ __device__ __forceinline__ void lane_rebase(const Row& rp_in, const Row& rq_in, 
     const int sh = static_cast<int>(A.kq - kn);
     A.sq = ldexp(A.sq, sh);
     A.w = ldexp(A.w, sh);
+    A.xmax = ldexpf(A.xmax, sh);
     A.kq = kn;
     if constexpr (MODE == 2) raise_offset(A.ktq, A.stq, mq, beta);
   }
@@ -325,7 +328,7 @@ __device__ __forceinline__ void lane_rebase(const Row& rp_in, const Row& rq_in, 
 
 // One slice's partial sums against the lane's current offsets.
 struct SlicePart {
-  float sp, sq, stp, stq, w, dm;
+  float sp, sq, stp, stq, w, dm, xm;
   bool ok;  // every partial sum below 2^64
 };
 
@@ -334,13 +337,13 @@ __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq
                                                     int64_t col_lane, int V, const LaneAcc& A) {
   const float op = -A.kp, oq = -A.kq, otp = -A.ktp, otq = -A.ktq;
   // Two chains per sum, each started from its first term (no add of zero); the maxima of
-  // l_q - l_p as chains of three-input maxima.
-  float sp0, sp1, sq0, sq1, w0, w1, stp0, stp1, stq0, stq1, dm0, dm1;
+  // l_q - l_p and of E_q (l_q - l_p) as chains of three-input maxima.
+  float sp0, sp1, sq0, sq1, w0, w1, stp0, stp1, stq0, stq1, dm0, dm1, xm0, xm1;
   auto acc = [](float& s, float v, bool first) { s = first ? v : s + v; };
 #pragma unroll
   for (int e = 0; e < kElemsPerLane; e += 2) {
     const bool first = (e == 0);
-    float t[2];
+    float t[2], x[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float xp = rp.at(e + h);
@@ -363,6 +366,7 @@ __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq
         acc(sq, eq, first);
         w = first ? eq * diff : __builtin_fmaf(eq, diff, w);
         t[h] = diff;
+        x[h] = eq * diff;
         if constexpr (MODE == 2) {
           const float etq = fast_exp2(__builtin_fmaf(xq, beta, otq));
           acc(h ? stq1 : stq0, etq, first);
@@ -372,13 +376,15 @@ __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq
     if constexpr (PAIR) {
       float& dm = (e & 2) ? dm1 : dm0;
       dm = (e < 4) ? fmaxf(t[0], t[1]) : fmaxf(fmaxf(dm, t[0]), t[1]);
+      float& xm = (e & 2) ? xm1 : xm0;
+      xm = (e < 4) ? fmaxf(x[0], x[1]) : fmaxf(fmaxf(xm, x[0]), x[1]);
     }
   }
   SlicePart P;
   P.sp = sp0 + sp1;
   P.ok = P.sp < kOverflow;
   P.stp = P.sq = P.stq = P.w = 0.f;
-  P.dm = -INFINITY;
+  P.dm = P.xm = -INFINITY;
   if constexpr (MODE == 2) {
     P.stp = stp0 + stp1;
     P.ok = P.ok && P.stp < kOverflow;
@@ -387,6 +393,7 @@ __device__ __forceinline__ SlicePart slice_partials(const Row& rp, const Row& rq
     P.sq = sq0 + sq1;
     P.w = w0 + w1;
     P.dm = fmaxf(dm0, dm1);
+    P.xm = fmaxf(xm0, xm1);
     P.ok = P.ok && P.sq < kOverflow;
     if constexpr (MODE == 2) {
       P.stq = stq0 + stq1;
@@ -427,6 +434,7 @@ __device__ __forceinline__ void slice_accumulate(const Row& rp, const Row& rq, f
     A.sq += static_cast<double>(P.sq);
     A.w += static_cast<double>(P.w);
     A.dmax = fmaxf(A.dmax, P.dm);
+    A.xmax = fmaxf(A.xmax, P.xm);
     if constexpr (MODE == 2) A.stq += static_cast<double>(P.stq);
   }
 }
@@ -560,11 +568,13 @@ __device__ __forceinline__ void lane_merge(LaneAcc& A, const LaneRec& R) {
       const int ha = static_cast<int>(A.kq - K), hr = static_cast<int>(R.kq - K);
       A.sq = ldexp(A.sq, ha) + ldexp(R.sq, hr);
       A.w = ldexp(A.w, ha) + ldexp(R.w, hr);
+      A.xmax = fmaxf(ldexpf(A.xmax, ha), ldexpf(R.xmax, hr));
       A.kq = K;
     } else {
       A.kq = R.kq;
       A.sq = R.sq;
       A.w = R.w;
+      A.xmax = R.xmax;
     }
   }
   A.dmax = fmaxf(A.dmax, R.dmax);
@@ -720,8 +730,16 @@ __device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const voi
     const double scale = kLn2 * exp2_d(static_cast<double>(A.kq) - LZq);
     closed = scale * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
     mass = scale * A.sq / kLn2;
+    // Two bounds on the lane's largest term t_y = scale E_y (L2E d_y + c2), d_y = l_q - l_p,
+    // both from max over y of a sum <= the sum of the maxima: its q-mass times the largest
+    // slope, and L2E max_y E_y d_y + max(c2, 0) S_q (every E_y >= 0, so no E_y exceeds S_q;
+    // the lane's offset need not cover its later slices).  The lane's sum is closed-form when
+    // the smaller one stays below delta.
     const double slope = static_cast<double>(kL2E) * A.dmax + c2;
-    const double bound = scale * A.sq * (slope > 0.0 ? slope : 0.0);
+    const double by_mass = scale * A.sq * (slope > 0.0 ? slope : 0.0);
+    const double by_peak = scale * (static_cast<double>(kL2E) * fmax(static_cast<double>(A.xmax), 0.0) +
+                                    (c2 > 0.0 ? c2 : 0.0) * A.sq);
+    const double bound = fmin(by_mass, by_peak);
     fail = !(bound * 1.0001 < static_cast<double>(delta));
   }
   if (tid == 0) *s_nfail = 0;
