@@ -618,8 +618,9 @@ def bench_tree(args):
 
 
 def bench_read_ceiling(args):
-    """The practical read ceiling: the library's plain read kernel (16-byte loads, four in
-    flight per thread, 1024 workgroups) over the same number of bytes as a streaming launch."""
+    """The practical read ceiling: the library's plain read kernel (1024 workgroups, each
+    reading its contiguous share front to back with two 16-byte nontemporal loads per thread in
+    flight) over the same number of bytes as a streaming launch."""
     import torch
 
     import draft_block_verification_sv_amd as pkg

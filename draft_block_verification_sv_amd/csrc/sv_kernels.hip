@@ -548,7 +548,7 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(SV_MASS_WAVES_PER_EU)))
 void sv_draw_kernel(SampleArgs a) {
-  __shared__ double s_pm[kMaxChunks];  // p_T chunk masses of a zero-mass residual row
+  __shared__ double s_pm[kMaxChunks];  // the picking wave's chunk masses (p_T's after a fallback)
   __shared__ int s_last;
   const int64_t b = blockIdx.x / a.mass_blocks;
   const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
@@ -619,22 +619,25 @@ void sv_draw_kernel(SampleArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  // ---- 1. chunk level (every wave computes the same total, so they agree on the fallback)
+  // ---- 1. chunk level (every wave computes the same total, so they agree on the fallback).
+  // The masses are read back once; wave 0, which draws, keeps its lanes' masses in s_pm.
   const int cpl = (nc + 63) / 64;  // chunks per lane
   const int c_lo = min(nc, lane * cpl), c_hi = min(nc, c_lo + cpl);
-  auto mass_at = [&](int c, bool from_lds) -> double {
-    return from_lds ? s_pm[c] : __hip_atomic_load(cm + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
   bool usep = false;
   double lsum = 0.0;
-  for (int c = c_lo; c < c_hi; ++c) lsum += mass_at(c, false);
+  for (int c = c_lo; c < c_hi; ++c) {
+    const double m = __hip_atomic_load(cm + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0) s_pm[c] = m;
+    lsum += m;
+  }
   double Z = wave_sum_d(lsum);
   if (!(Z > 0.0)) {  // zero residual mass (rounding only): draw from p_T of the same row
     usep = true;
+    __syncthreads();  // wave 0's copies are written before s_pm is refilled
     chunk_masses<DT, VEC, kMassWaves, 2, false>(a, t, d, false, rq.k, 0, nc, wave, lane, s_pm);
     __syncthreads();
     lsum = 0.0;
-    for (int c = c_lo; c < c_hi; ++c) lsum += mass_at(c, true);
+    for (int c = c_lo; c < c_hi; ++c) lsum += s_pm[c];
     Z = wave_sum_d(lsum);
   }
   if (wave != 0) return;  // one wave draws
@@ -653,7 +656,7 @@ void sv_draw_kernel(SampleArgs a) {
   double sel_start = 0.0;
   double s_c = excl;
   for (int c = c_lo; c < c_hi; ++c) {
-    const double m_c = mass_at(c, usep);
+    const double m_c = s_pm[c];  // the residual's masses, or p_T's after the fallback
     const double e_c = (c == c_hi - 1) ? incl : s_c + m_c;
     if (m_c > 0.0) {
       last = c;

@@ -382,9 +382,10 @@ sv_status sv_profile_get(int32_t index, char* name, size_t name_len, int64_t* la
  * Read ceiling (diagnostics).  A plain read of `bytes` bytes at `data` (device memory, 16-byte
  * aligned, bytes a positive multiple of 16) on `stream`, folding the words with xor into
  * out[0 .. SV_READ_PROBE_WORDS) (device memory owned by the caller).  It measures what a
- * kernel that only streams bytes in reaches on this part: the streaming kernels of this
- * library read their logits the same way, so their achieved bandwidth is compared with it as
- * well as with the published HBM peak.  Its duration is reported as "sv_read_probe" by the
+ * kernel that only streams bytes in reaches on this part: each of 1024 workgroups reads its
+ * contiguous share front to back with 16-byte nontemporal loads, the fastest of the read
+ * patterns measured.  The streaming kernels' achieved bandwidth is compared with it as well as
+ * with the published HBM peak.  Its duration is reported as "sv_read_probe" by the
  * kernel timing above.  Errors: SV_ERR_NULL, SV_ERR_SHAPE (size), SV_ERR_VALUE (alignment),
  * SV_ERR_HIP; nothing is enqueued on an error.
  */
