@@ -96,6 +96,35 @@ def test_small_delta_rereads_clipped_slices(delta):
     _report(f"delta={delta}", s)
 
 
+@pytest.mark.parametrize("B", [1, 65])  # one request: split rows; 65 (130 rows): one WG per row
+def test_clip_bound_when_lane_offset_trails_later_slices(B):
+    # Regression for the no-clip bound.  Every logit is -30 except one token y that both rows
+    # favour (l_q = l_p = 10, in a slice that is no lane's first) and a larger target token z
+    # (l_p = 14).  Then c2 = LZ_p - LZ_q > 0 and t_y = ln2 q_y (L2E d_y + c2) with d_y = 0 is
+    # about 4, clipped to delta = 1.  The lane's sum offset comes from its first slice (-30), so
+    # E_y = 2^(l_q L2E - k_q) is about 2^57 against it: a bound that took max E_y <= 1 let this
+    # lane through as unclipped and returned R near 4.
+    from synth import bf16_bits_from_f64
+
+    V = 151936
+    w = make_workload(B=B, k=[1] * B, V=V, dtype="bf16", delta=1.0, temperature=1.0, seed=(11, B))
+    lq = np.full(V, -30.0)
+    lp = np.full(V, -30.0)
+    y, z = 100 * 1024, 100
+    lq[y] = lp[y] = 10.0
+    lp[z] = 14.0
+    to = w.target_offsets
+    for b in range(B):
+        w.target[to[b], :V] = bf16_bits_from_f64(lp)
+        w.draft[b, :V] = bf16_bits_from_f64(lq)
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    ref = run_oracle(w)
+    assert np.all(np.abs(ref["rkl"] - 1.0) < 1e-3)  # the clipped term dominates
+    s = compare(w, got, ref)
+    _report(f"lane offset below a later slice, B={B}", s)
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 def test_single_request_full_vocab():
     w = workload("single")
