@@ -654,6 +654,13 @@ __device__ __forceinline__ float logit_at(const void* row, int64_t col) {
   else return static_cast<const float*>(row)[col];
 }
 
+// A value the whole workgroup shares, moved to scalar registers (a buffer resource needs one).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Clipped reverse-KL of the row pair.  With Q = 2^(k_q - LZq) S_q, the q-mass of a lane's
 // columns, and c2 = LZp - LZq, those columns contribute exactly
 //   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
@@ -875,23 +882,44 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
 
-  // thread 0, the only user: the uniform's and the draft token's range checks and the two
-  // logits at the token, fetched here so that their latency overlaps the reductions below
-  // instead of delaying the stream
-  int row_flags = ctx.row_flags, x = -1;
-  float lpx = 0.0f, lqx = 0.0f;
-  if (tid == 0 && ctx.b >= 0) {
-    if (!uniform_ok(a.uniforms[ctx.t])) row_flags |= 16;  // SV_DEV_BAD_UNIFORM
-    if constexpr (PAIR) {
-      if (xr < 0 || xr >= V) {
-        row_flags |= 4;  // SV_DEV_BAD_TOKEN
-      } else {
-        x = xr;
-        lpx = logit_at<DT>(prow, x);
-        lqx = logit_at<DT>(qrow, x);
-      }
+  // The uniform and the two logits at the draft token, for thread 0's acceptance test at the
+  // end.  Every thread issues the same three buffer loads, at offsets kept in bounds and with
+  // no branch around them: a load under a branch is waited for where the branch closes, which
+  // held the other waves at the first barrier below for two round trips behind the streaming
+  // traffic.  Loaded this way they are waited for only where they are used.  Buffers of zero
+  // length (no uniforms, an invalid token, a bonus row) read as 0 and touch no memory.
+  const bool x_ok = PAIR && xr >= 0 && xr < V;
+  uint32_t u_bits, lp_bits, lq_bits;
+  {
+    // a zero the compiler cannot see through: with it the loaded values are per-lane to the
+    // compiler, which then leaves them in vector registers instead of waiting for them at once
+    // to move them to scalar ones
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    constexpr int es = DT == 0 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t RU = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.uniforms), 0, a.uniforms ? static_cast<int>(a.n_units * 4) : 0, kBufWord3);
+    u_bits = __builtin_amdgcn_raw_buffer_load_b32(RU, static_cast<int>(ctx.t * 4) + vzero, 0, 0);
+    const int xoff = (x_ok ? xr : 0) * es + vzero;
+    const __amdgpu_buffer_rsrc_t RPX = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(prow))), 0, x_ok ? V * es : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t RQX = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(qrow))), 0, x_ok ? V * es : 0, kBufWord3);
+    if constexpr (DT == 0) {
+      lp_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RPX, xoff, 0, 0)) << 16;
+      lq_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RQX, xoff, 0, 0)) << 16;
+    } else {
+      lp_bits = __builtin_amdgcn_raw_buffer_load_b32(RPX, xoff, 0, 0);
+      lq_bits = __builtin_amdgcn_raw_buffer_load_b32(RQX, xoff, 0, 0);
     }
   }
+  // thread 0: the uniform's and the draft token's range checks
+  auto input_flags = [&]() {
+    int f = ctx.row_flags;
+    if (!uniform_ok(__uint_as_float(u_bits))) f |= 16;  // SV_DEV_BAD_UNIFORM
+    if (PAIR && !x_ok) f |= 4;                          // SV_DEV_BAD_TOKEN
+    return f;
+  };
 
   // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
   const double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
@@ -907,7 +935,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     draw_offsets(LZTp, &slot->offp, &slot->lzp);
     slot->beta = scale_T;
     slot->targ = argp;
-    slot->flags = row_flags;
+    if constexpr (!PAIR) slot->flags = input_flags();  // a pair row's flags come at the end
   }
   if constexpr (!PAIR) return;
 
@@ -944,15 +972,17 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   }
   if (tid == 0 && ctx.b >= 0) {
     draw_offsets(LZTq, &slot->offq, &slot->lzq);
+    const int row_flags = input_flags();
+    slot->flags = row_flags;
     int accept = 0;
     if (row_flags == 0) {  // the request's own flags are combined by the sampler
-      const double Lp = static_cast<double>(lpx) * scale_T - LZTp;  // log2 p_T(x)
-      const double Lq = static_cast<double>(lqx) * scale_T - LZTq;  // log2 q_T(x)
+      const double Lp = static_cast<double>(__uint_as_float(lp_bits)) * scale_T - LZTp;  // log2 p_T(x)
+      const double Lq = static_cast<double>(__uint_as_float(lq_bits)) * scale_T - LZTq;  // log2 q_T(x)
       if constexpr (MODE == 1) {
-        accept = (x == argp) ? 1 : 0;
+        accept = (xr == argp) ? 1 : 0;
       } else {
         const double ratio = fmin(1.0, exp2_d(Lp - Lq));
-        accept = (static_cast<double>(a.uniforms[ctx.t]) < ratio) ? 1 : 0;
+        accept = (static_cast<double>(__uint_as_float(u_bits)) < ratio) ? 1 : 0;
       }
       if (a.p_at) a.p_at[ctx.d] = static_cast<float>(exp2_d(Lp));
       if (a.q_at) a.q_at[ctx.d] = static_cast<float>(exp2_d(Lq));
@@ -1155,19 +1185,19 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
       rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     0);
+                                     -1);
     } else {
       rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     0);
+                                     -1);
     }
     return;
   }
 
-  // the draft token (draft units 0 .. n_d-1 are the draft rows in packed order) is fetched by
-  // thread 0 with the lengths and temperatures; it is checked, and the logits at it are
-  // fetched, once the row has been streamed
+  // the draft token (draft units 0 .. n_d-1 are the draft rows in packed order), the same for
+  // every thread, is fetched with the lengths and temperatures; it is checked, and the logits
+  // at it are fetched, once the row has been streamed
   int32_t xr = -1;
-  if (PHASE != 1 && tid == 0 && unit < a.n_d) xr = a.tokens[unit];
+  if (PHASE != 1 && unit < a.n_d) xr = a.tokens[unit];
   if (!resolve_unit<true>(a, unit, tid, red_i, s_req, s_off, s_t, s_void, &s_T)) return;
   const int64_t b = s_req;
   const int64_t off = s_off;
