@@ -665,8 +665,10 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
 // columns, and c2 = LZp - LZq, those columns contribute exactly
 //   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
 // and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
-// ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p.  A lane whose bound may reach
-// delta has its columns re-read and summed entry by entry.
+// ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p, nor
+// ln2 2^(k_q - LZq) (L2E max(0, X) + max(0, c2) S_q), X the lane's largest E_q (l_q - l_p).
+// A lane whose smaller bound may reach delta has its columns re-read and summed entry by
+// entry.
 // With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
 // OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
 // form plus Q.
