@@ -96,8 +96,8 @@ def parity_sample(w, out, refs) -> dict:
         g = rkl[o_d: o_d + kb]
         scale = np.maximum(np.abs(r["rkl"]), r["rkl_l1"])
         max_rkl = max(max_rkl, float(np.max(np.abs(g - r["rkl"]) / scale)))
-        # against the parity bar: 1e-5 of the scale plus the fp32 accumulation floor 2^-21
-        max_bar = max(max_bar, float(np.max(np.abs(g - r["rkl"]) / (1e-5 * scale + 2.0**-21))))
+        # against the parity bar: 1e-5 of the scale plus the fp64 rounding floor of the finalize
+        max_bar = max(max_bar, float(np.max(np.abs(g - r["rkl"]) / (1e-5 * scale + 1e-12))))
         ok = np.isfinite(r["p_at"]) & (r["p_at"] > 0)
         if np.any(ok):
             max_p = max(max_p, float(np.max(np.abs(pat[o_d: o_d + kb][ok] - r["p_at"][ok]) / r["p_at"][ok])))
@@ -122,6 +122,7 @@ def cpu_baseline(w, n_requests: int) -> dict:
 
     global _W
     _W = w
+    # the GPU machine gives one GPU's jobs a 16-core share, whatever os.cpu_count() reports there
     cores = max(1, min(16, os.cpu_count() or 1))
     reqs = list(range(min(n_requests, w.B)))
     ctx = mp.get_context("fork")
@@ -131,7 +132,8 @@ def cpu_baseline(w, n_requests: int) -> dict:
     dt = time.perf_counter() - t0
     positions = sum(int(w.k[b]) for b, _ in refs)
     return refs, {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count(),
+            "cores_note": "worker processes capped at the 16-core share one GPU's jobs get",
             "sample": f"{len(reqs)} of {w.B} requests ({positions} verified positions, all "
                       f"outputs incl. the clipped rKL), float64 NumPy, {cores} worker processes, "
                       f"{dt:.2f} s wall"}
@@ -160,6 +162,7 @@ def cpu_baseline_opd(w, idx, n_requests: int, grad: bool = False) -> dict:
     tl = oracle.widen_logits(w.target[:, : w.V], w.dtype)
     dl = oracle.widen_logits(w.draft[:, : w.V], w.dtype)
     _OPD = (tl, dl, idx, w.draft_offsets, w.k, w.delta, grad)
+    # the GPU machine gives one GPU's jobs a 16-core share, whatever os.cpu_count() reports there
     cores = max(1, min(16, os.cpu_count() or 1))
     reqs = list(range(min(n_requests, w.B)))
     t0 = time.perf_counter()
@@ -191,6 +194,7 @@ def cpu_baseline_greedy(w, n_requests: int) -> dict:
 
     global _W
     _W = w
+    # the GPU machine gives one GPU's jobs a 16-core share, whatever os.cpu_count() reports there
     cores = max(1, min(16, os.cpu_count() or 1))
     reqs = list(range(min(n_requests, w.B)))
     t0 = time.perf_counter()
@@ -656,7 +660,7 @@ def main():
                                          "tree"),
                     default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=64)
+    ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
@@ -774,16 +778,18 @@ def main():
     # every logit and a short finalize launch folds the parts
     stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_part"
     rows_us = kernels[stream_name]["avg_us"]
-    achieved = rows_bytes / (rows_us * 1e-6) / 1e9
+    kernel_gbs = rows_bytes / (rows_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
         if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == args.workload:
-            traffic = c.get("hbm_bytes_per_launch")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": stream_name}
+            traffic = c.get("hbm_bytes_per_call")
+    roofline = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s", "traffic": traffic,
+                "kernel": "sv_verify_block (every kernel of the call)",
+                "kernels": sorted(kernels),
+                "kernel_frac": {"kernel": stream_name, "achieved": round(kernel_gbs, 1),
+                                "frac": round(kernel_gbs / PEAK_HBM_GBS, 4)}}
 
     # the practical read ceiling beside it: the library's plain read kernel over the same
     # number of bytes, timed the same way (after the measured passes)
@@ -804,7 +810,7 @@ def main():
     probe_gbs = (rows_bytes // 4 * 4) / (ms_probe / n_probe * 1e-3) / 1e9
     roofline["read_ceiling"] = {"kernel": "sv_read_probe", "achieved": round(probe_gbs, 1),
                                 "frac": round(probe_gbs / PEAK_HBM_GBS, 4),
-                                "kernel_over_ceiling": round(achieved / probe_gbs, 4)}
+                                "kernel_over_ceiling": round(kernel_gbs / probe_gbs, 4)}
 
     if cpu is not None:  # the timed call's outputs against the oracle's on the sampled requests
         cpu["parity"] = parity_sample(w, out, refs)
@@ -825,6 +831,10 @@ def main():
     call_stats = {"median": round(float(np.median(call_us)), 2),
                   "p10": round(float(np.percentile(call_us, 10)), 2),
                   "p90": round(float(np.percentile(call_us, 90)), 2)}
+    # the call's rate: algorithmic bytes over the median device time of a whole call
+    achieved = (rows_bytes + meta_bytes) / (float(np.median(call_us)) * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), **roofline}
 
     # realised acceptance: mean tokens per request-round and the per-position acceptance rate
     # (accepted at i among requests that reached i)

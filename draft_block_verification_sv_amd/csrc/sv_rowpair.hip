@@ -38,19 +38,6 @@
 #include "sv_layout.h"
 #include "sv_launch.h"
 
-#ifndef SV_ROWS_NT
-#define SV_ROWS_NT 1
-#endif
-#ifndef SV_ROWS_PREFETCH
-#define SV_ROWS_PREFETCH 1
-#endif
-#ifndef SV_ROWS_WAVES_PER_EU
-#define SV_ROWS_WAVES_PER_EU 1
-#endif
-#ifndef SV_ROWS_DEPTH
-#define SV_ROWS_DEPTH 1  // slices prefetched ahead of the one being reduced (1 or 2)
-#endif
-
 namespace sv {
 
 // Work-item and workgroup ids straight from the hardware registers: this translation unit
@@ -70,7 +57,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // bounds-checked loads of the streaming loop; the loads stream (nontemporal) like the
 // plain ones.
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kBufAux = SV_ROWS_NT ? 2 : 0;
+constexpr int kBufAux = 2;
 
 __device__ __forceinline__ void store_nan(float* p) { *reinterpret_cast<uint32_t*>(p) = kNaNBits; }
 
@@ -89,11 +76,7 @@ __device__ __forceinline__ bool temperature_ok(float T) {
 template <class T>
 __device__ __forceinline__ T stream_load(const T* p) {
   static_assert(sizeof(T) == 16, "16-byte loads");
-#if SV_ROWS_NT
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-#else
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-#endif
   T r;
   __builtin_memcpy(&r, &v, 16);
   return r;
@@ -450,22 +433,7 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
   const int n_full = V / kSlice;
   int s = first;
   bool fresh = true;
-  if constexpr (DT == 0 && VEC && !SV_ROWS_PREFETCH) {
-    const uint16_t* P = static_cast<const uint16_t*>(prow) + lane * 8;
-    const uint16_t* Q = static_cast<const uint16_t*>(qrow) + lane * 8;
-    for (; s < n_full; s += step) {
-      PackedRow ap, aq;
-      ap.load(P + static_cast<int64_t>(s) * kSlice);
-      if constexpr (PAIR) aq.load(Q + static_cast<int64_t>(s) * kSlice);
-      if (fresh) {
-        lane_init<PAIR, MODE>(ap, aq, beta, A);
-        fresh = false;
-      }
-      slice_accumulate<PAIR, MODE, false>(ap, aq, beta,
-                                          static_cast<int64_t>(s) * kSlice + lane * 8, V, A);
-    }
-  }
-  if constexpr (DT == 0 && VEC && SV_ROWS_PREFETCH) {
+  if constexpr (DT == 0 && VEC) {
     // The row's full slices as bounds-checked buffers: the prefetch of a slice past the
     // last one reads zeros without touching memory, so every prefetch is issued without a
     // branch and the wait before a slice's arithmetic covers that slice's loads alone (a
@@ -481,32 +449,6 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
       rp.load(RP, lane_off + sl * (kSlice * 2));
       if constexpr (PAIR) rq.load(RQ, lane_off + sl * (kSlice * 2));
     };
-#if SV_ROWS_DEPTH == 2
-    // two slices in flight ahead of the one being reduced
-    PackedRow cp, cq;
-    auto add = [&](const PackedRow& rp, const PackedRow& rq, int sl) {
-      slice_accumulate<PAIR, MODE, false>(rp, rq, beta, static_cast<int64_t>(sl) * kSlice + lane * 8,
-                                          V, A);
-    };
-    if (s < n_full) {
-      load_pair(ap, aq, s);
-      load_pair(bp, bq, s + step);
-      lane_init<PAIR, MODE>(ap, aq, beta, A);
-      fresh = false;
-      while (true) {
-        load_pair(cp, cq, s + 2 * step);
-        add(ap, aq, s);
-        if (s + step >= n_full) { s += step; break; }
-        load_pair(ap, aq, s + 3 * step);
-        add(bp, bq, s + step);
-        if (s + 2 * step >= n_full) { s += 2 * step; break; }
-        load_pair(bp, bq, s + 4 * step);
-        add(cp, cq, s + 2 * step);
-        s += 3 * step;
-        if (s >= n_full) break;
-      }
-    }
-#else
     if (s < n_full) {
       load_pair(ap, aq, s);
       lane_init<PAIR, MODE>(ap, aq, beta, A);
@@ -527,7 +469,6 @@ __device__ __forceinline__ void stream_row(const void* prow, const void* qrow, f
         if (s >= n_full) break;
       }
     }
-#endif
   }
   for (; s < n_slices; s += step) {  // every slice not handled above
     const int64_t col_lane = static_cast<int64_t>(s) * kSlice + lane * 8;
@@ -661,31 +602,13 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Clipped reverse-KL of the row pair.  With Q = 2^(k_q - LZq) S_q, the q-mass of a lane's
-// columns, and c2 = LZp - LZq, those columns contribute exactly
-//   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
-// and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
-// ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p, nor
-// ln2 2^(k_q - LZq) (L2E max(0, X) + max(0, c2) S_q), X the lane's largest E_q (l_q - l_p).
-// A lane whose smaller bound may reach delta has its columns re-read and summed entry by
-// entry.
-// With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
-// OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
-// form plus Q.
-struct RklSums {
-  double R, sg;
-};
-
-// The re-read works on pieces: 8 consecutive columns of one failing lane (the lane's group of
-// 8 in one of its slices).  The pieces of a round are spread over the whole workgroup, four per
-// thread for bf16 rows read 16 bytes at a time and two otherwise (at most kRereadItems), with
-// every load issued before any arithmetic; each piece's sum goes to LDS, and one wave then
-// adds a failing lane's pieces in piece order.
-constexpr int kRereadItems = 1024;
-// A lane has at most ceil(kMaxSlices / 4) * kGroups pieces: one failing lane always fits a round.
-static_assert(((kMaxSlices + kRowWaves - 1) / kRowWaves) * kGroups <= 2 * kRowThreads,
-              "a failing lane's pieces must fit one round");
-
+// ----------------------------------------------------------------------------- lane re-reads
+// Some lanes have their columns read again after the stream, one wave per lane: piece j of
+// lane src (8 consecutive columns: the lane's group j % kGroups of its slice
+// src / 64 + (j / kGroups) * kRowWaves) goes to thread j % 64 of the wave, two pieces in flight
+// per thread, every load issued before any arithmetic.  f(l_p, l_q) is applied to every
+// column of the lane inside [0, V), in a fixed order per thread; the wave's sums then combine
+// in a fixed tree, so the results do not depend on which lanes were listed or in what order.
 // The 8 logits of one piece as raw words: a bf16 piece is one 16-byte word, an fp32 piece two.
 // VEC rows are read through a bounds-checked buffer (a piece that is not valid, or the part of
 // one past V, reads zeros); other rows column by column with the column clamped into the row.
@@ -724,12 +647,127 @@ struct Piece {
   }
 };
 
+template <int DT, bool VEC, class F>
+__device__ __forceinline__ void for_lane_columns(const void* prow, const void* qrow, int V,
+                                                 int n_slices, int src, int lane, F&& f) {
+  constexpr int es = DT == 0 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t RQ =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(qrow), 0, V * es, kBufWord3);
+  const __amdgpu_buffer_rsrc_t RP =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(prow), 0, V * es, kBufWord3);
+  const int sw = src >> 6, sl = src & 63;
+  // the lane's slices are sw, sw + 4, ... < n_slices: kGroups pieces each
+  const int n_pieces = ((n_slices - sw + kRowWaves - 1) / kRowWaves) * kGroups;
+  for (int j0 = 0; j0 < n_pieces; j0 += 2 * 64) {
+    Piece<DT, VEC> pq[2], pp[2];
+    int64_t col[2];
+    bool ok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + u * 64 + lane;
+      const int slice = sw + (j / kGroups) * kRowWaves;  // < n_slices whenever j < n_pieces
+      col[u] = static_cast<int64_t>(slice) * kSlice + (j % kGroups) * 512 + sl * 8;
+      ok[u] = j < n_pieces && col[u] < V;
+      pq[u].load(qrow, RQ, col[u], ok[u], V);
+      pp[u].load(prow, RP, col[u], ok[u], V);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ok[u] && col[u] + e < V) f(pp[u].at(e), pq[u].at(e));
+  }
+}
+
+// Lists the lanes whose flag is set (order of arrival; users combine per lane, so the order
+// does not matter) and returns how many there are.
+__device__ __forceinline__ int list_lanes(bool flag, int* list, int* s_n) {
+  if (thread_index() == 0) *s_n = 0;
+  __syncthreads();
+  if (flag) list[atomicAdd(s_n, 1)] = thread_index();
+  __syncthreads();
+  return *s_n;
+}
+
+// Exact sums of the lanes that carry the row's mass.  The stream's lane sums come from fp32
+// exponentials (one unit in the last place each) and fp32 partial sums of 16 elements, a
+// relative error of ~1e-7 of the lane's mass.  On a lane that holds most of a row's mass this
+// is an absolute error of ~1e-7 in the normaliser and, through the closed form below, in the
+// clipped reverse-KL, where L2E W and c2 S_q are two large terms that cancel to a small one
+// (one token dominating both rows).  Such rows have a small sum_y |min(delta, t_y)|, so the
+// error would be large against it.  A lane holding more than half of either row's mass, or
+// more than 1/32 of it with a closed form that cancels by a factor above 64, is therefore
+// summed again from the logits in fp64 (exponentials exact to ~1e-15), against the same
+// offsets; its S_p, S_q and W are replaced.  Returns whether any lane was replaced (the
+// normalisers must then be formed again).
+template <int DT, bool VEC>
+__device__ __forceinline__ bool exact_heavy_lanes(const void* prow, const void* qrow, int V,
+                                                  int n_slices, double LZp, double LZq,
+                                                  LaneAcc* lacc, int* list, int* s_n) {
+  const int tid = thread_index(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  bool heavy;
+  {
+    const LaneAcc& A = lacc[tid];
+    const double P = A.sp > 0.0 ? exp2_d(static_cast<double>(A.kp) - LZp) * A.sp : 0.0;
+    if (A.sq > 0.0) {
+      const double s = exp2_d(static_cast<double>(A.kq) - LZq);
+      const double c2 = LZp - LZq;
+      const double Q = s * A.sq;
+      const double closed = s * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
+      const double mag = s * (static_cast<double>(kL2E) * fabs(A.w) + fabs(c2) * A.sq);
+      const double big = fmax(P, Q);
+      heavy = big > 0.5 || (big > 1.0 / 32.0 && mag > 64.0 * fabs(closed));
+    } else {
+      heavy = P > 0.5;
+    }
+  }
+  const int n = list_lanes(heavy, list, s_n);
+  if (n == 0) return false;
+  for (int f = wave; f < n; f += kRowWaves) {
+    const int src = list[f];
+    const double kp = static_cast<double>(lacc[src].kp), kq = static_cast<double>(lacc[src].kq);
+    double sp = 0.0, sq = 0.0, w = 0.0;
+    for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src, lane, [&](float lp, float lq) {
+      const double eq = exp2_d(static_cast<double>(lq) * static_cast<double>(kL2E) - kq);
+      sp += exp2_d(static_cast<double>(lp) * static_cast<double>(kL2E) - kp);
+      sq += eq;
+      w += eq * (static_cast<double>(lq) - static_cast<double>(lp));
+    });
+    sp = wave_sum_d(sp);
+    sq = wave_sum_d(sq);
+    w = wave_sum_d(w);
+    if (lane == 0) {
+      lacc[src].sp = sp;
+      lacc[src].sq = sq;
+      lacc[src].w = w;
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+// Clipped reverse-KL of the row pair.  With Q = 2^(k_q - LZq) S_q, the q-mass of a lane's
+// columns, and c2 = LZp - LZq, those columns contribute exactly
+//   sum t_y = ln2 2^(k_q - LZq) (L2E W + c2 S_q),
+// and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
+// ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p, nor
+// ln2 2^(k_q - LZq) (L2E max(0, X) + max(0, c2) S_q), X the lane's largest E_q (l_q - l_p).
+// A lane whose smaller bound may reach delta has its columns re-read and summed entry by
+// entry: q_y from an fp32 exponential, the log ratio L2E (l_q - l_p) + c2 and the sums in fp64.
+// With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
+// OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
+// form plus Q.
+struct RklSums {
+  double R, sg;
+};
+
 template <int DT, bool VEC, bool SG>
 __device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const void* qrow, int V,
                                                     int n_slices, double LZp, double LZq,
                                                     float delta, const LaneAcc& A, double* direct,
                                                     double* direct_sg, int* failed, int* s_nfail,
-                                                    float* ipart, float* igpart, double* red) {
+                                                    double* red) {
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double c2 = LZp - LZq;
@@ -751,77 +789,28 @@ __device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const voi
     const double bound = fmin(by_mass, by_peak);
     fail = !(bound * 1.0001 < static_cast<double>(delta));
   }
-  if (tid == 0) *s_nfail = 0;
-  __syncthreads();
-  if (fail) failed[atomicAdd(s_nfail, 1)] = tid;
-  __syncthreads();
-  const int nfail = *s_nfail;
+  const int nfail = list_lanes(fail, failed, s_nfail);
   if (nfail > 0) {
-    const float c2f = static_cast<float>(c2);
-    constexpr int es = DT == 0 ? 2 : 4;
-    const __amdgpu_buffer_rsrc_t RQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(qrow), 0, V * es, kBufWord3);
-    const __amdgpu_buffer_rsrc_t RP = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(prow), 0, V * es, kBufWord3);
-    // pieces of a failing lane of wave 0 (the most any lane has); lane src has
-    // ceil((n_slices - src / 64) / 4) * kGroups of them
-    constexpr int PT = (DT == 0 && VEC) ? 4 : 2;  // pieces per thread and round
-    constexpr int items = PT * kRowThreads;
-    static_assert(items <= kRereadItems, "piece sums must fit their LDS arrays");
-    const int npm = ((n_slices + kRowWaves - 1) / kRowWaves) * kGroups;
-    const int per_round = items / npm;  // >= 1: npm <= 2 * kRowThreads <= items
-    for (int f0 = 0; f0 < nfail; f0 += per_round) {
-      const int nf = min(per_round, nfail - f0);
-      const int n_items = nf * npm;
-      int64_t col[PT];
-      bool ok[PT];
-      Piece<DT, VEC> pq[PT], pp[PT];
-#pragma unroll
-      for (int u = 0; u < PT; ++u) {
-        const int g = tid + u * kRowThreads;
-        const int f = g / npm, j = g - f * npm;
-        const int src = failed[f0 + min(f, nf - 1)];
-        const int sw = src >> 6, sl = src & 63;
-        const int slice = sw + (j / kGroups) * kRowWaves;
-        col[u] = static_cast<int64_t>(slice) * kSlice + (j % kGroups) * 512 + sl * 8;
-        ok[u] = g < n_items && slice < n_slices && col[u] < V;
-        pq[u].load(qrow, RQ, col[u], ok[u], V);
-        pp[u].load(prow, RP, col[u], ok[u], V);
+    const double dd = static_cast<double>(delta);
+    for (int f = wave; f < nfail; f += kRowWaves) {
+      const int src = failed[f];
+      double part = 0.0, gpart = 0.0;
+      for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src, lane, [&](float lp, float lq) {
+        const double a = static_cast<double>(lq) * static_cast<double>(kL2E);
+        const double q = static_cast<double>(fast_exp2(static_cast<float>(a - LZq)));
+        const double term =
+            q * kLn2 * ((static_cast<double>(lq) - static_cast<double>(lp)) * static_cast<double>(kL2E) + c2);
+        part += fmin(term, dd);
+        if constexpr (SG) gpart += term < dd ? term + q : 0.0;
+      });
+      part = wave_sum_d(part);
+      if (lane == 0) direct[src] = part;
+      if constexpr (SG) {
+        gpart = wave_sum_d(gpart);
+        if (lane == 0) direct_sg[src] = gpart;
       }
-#pragma unroll
-      for (int u = 0; u < PT; ++u) {
-        const int g = tid + u * kRowThreads;
-        float part = 0.0f, gpart = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lq = pq[u].at(e), lp = pp[u].at(e);
-          const float q = fast_exp2(static_cast<float>(static_cast<double>(lq) * kL2E - LZq));
-          const float term = q * static_cast<float>(kLn2) * __builtin_fmaf(lq - lp, kL2E, c2f);
-          const bool in = ok[u] && col[u] + e < V;
-          part += in ? fminf(term, delta) : 0.0f;
-          if constexpr (SG) gpart += (in && term < delta) ? term + q : 0.0f;
-        }
-        if (g < n_items) {
-          ipart[g] = part;
-          if constexpr (SG) igpart[g] = gpart;
-        }
-      }
-      __syncthreads();
-      for (int f = wave; f < nf; f += kRowWaves) {  // one wave per failing lane, pieces in order
-        const int src = failed[f0 + f];
-        const int n_pieces = ((n_slices - (src >> 6) + kRowWaves - 1) / kRowWaves) * kGroups;
-        double part = 0.0, gpart = 0.0;
-        for (int j = lane; j < n_pieces; j += 64) {
-          part += static_cast<double>(ipart[f * npm + j]);
-          if constexpr (SG) gpart += static_cast<double>(igpart[f * npm + j]);
-        }
-        const double dsum = wave_sum_d(part);
-        if (lane == 0) direct[src] = dsum;
-        if constexpr (SG) {
-          const double gsum = wave_sum_d(gpart);
-          if (lane == 0) direct_sg[src] = gsum;
-        }
-      }
-      __syncthreads();
     }
+    __syncthreads();
   }
   RklSums out;
   out.R = block_sum_d(fail ? direct[tid] : closed, red);
@@ -838,6 +827,19 @@ __device__ __forceinline__ void draw_offsets(double LZ, float* off, float* lz) {
 }
 
 // ----------------------------------------------------------------------------- kernel
+// The workgroup's LDS: the lane records, per-lane re-read results, the list of re-read
+// lanes and the block reductions' slots.
+struct Scratch {
+  LaneAcc* lacc;
+  double* direct;
+  double* direct_sg;
+  int* failed;
+  int* s_nfail;
+  double* red_d;
+  float* red_f;
+  int* red_i;
+};
+
 struct RowCtx {
   int64_t unit;  // the row (pair) this workgroup works on
   int part;      // which part of it, when rows are split over several workgroups
@@ -851,9 +853,10 @@ struct RowCtx {
 
 template <int DT, bool VEC, int PHASE, bool PAIR, int MODE>
 __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx& ctx,
-                                             LaneAcc* lacc, double* direct, double* direct_sg,
-                                             int* failed, int* s_nfail, float* ipart, float* igpart,
-                                             double* red_d, float* red_f, int* red_i, int xr) {
+                                             const Scratch& sc, int xr) {
+  LaneAcc* lacc = sc.lacc;
+  double* red_d = sc.red_d;
+  float* red_f = sc.red_f;
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = a.V;
@@ -924,34 +927,47 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   };
 
   // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
-  const double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
-  const double LZTp = (MODE == 2) ? lanes_lz(A.ktp, A.stp, red_f, red_d) : LZ1p;
+  double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
+  const double LZTp0 = (MODE == 2) ? lanes_lz(A.ktp, A.stp, red_f, red_d) : LZ1p;
   int argp = 0;
   if constexpr (MODE == 1) {
     const float Mx = block_max_f(A.amax, red_f);
-    argp = block_min_i(A.amax == Mx ? A.aidx : 0x7fffffff, red_i);
+    argp = block_min_i(A.amax == Mx ? A.aidx : 0x7fffffff, sc.red_i);
   }
   const float scale_T = (MODE == 2) ? ctx.beta : kL2E;
   RowOut* slot = ctx.b >= 0 ? a.rowout + ctx.b * a.kmax1 + ctx.pos : nullptr;
+  if constexpr (!PAIR) {  // a bonus row: its offsets and flags for the draw
+    if (tid == 0 && ctx.b >= 0) {
+      draw_offsets(LZTp0, &slot->offp, &slot->lzp);
+      slot->beta = scale_T;
+      slot->targ = argp;
+      slot->flags = input_flags();
+    }
+    return;
+  }
+
+  // draft row
+  double LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
+  if (a.rkl_out &&
+      exact_heavy_lanes<DT, VEC>(prow, qrow, V, n_slices, LZ1p, LZ1q, lacc, sc.failed, sc.s_nfail)) {
+    LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);  // A reads the replaced sums back
+    LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
+  }
+  const double LZTp = (MODE == 2) ? LZTp0 : LZ1p;
+  const double LZTq = (MODE == 2) ? lanes_lz(A.ktq, A.stq, red_f, red_d) : LZ1q;
   if (tid == 0 && ctx.b >= 0) {
     draw_offsets(LZTp, &slot->offp, &slot->lzp);
     slot->beta = scale_T;
     slot->targ = argp;
-    if constexpr (!PAIR) slot->flags = input_flags();  // a pair row's flags come at the end
   }
-  if constexpr (!PAIR) return;
-
-  // draft row
-  const double LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
-  const double LZTq = (MODE == 2) ? lanes_lz(A.ktq, A.stq, red_f, red_d) : LZ1q;
   if (a.rkl_out) {
     RklSums Rk;
     if (MODE == 1 && a.stats)
-      Rk = lanes_clipped_rkl<DT, VEC, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
-                                            direct_sg, failed, s_nfail, ipart, igpart, red_d);
+      Rk = lanes_clipped_rkl<DT, VEC, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, sc.direct,
+                                            sc.direct_sg, sc.failed, sc.s_nfail, red_d);
     else
-      Rk = lanes_clipped_rkl<DT, VEC, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, direct,
-                                             direct_sg, failed, s_nfail, ipart, igpart, red_d);
+      Rk = lanes_clipped_rkl<DT, VEC, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, sc.direct,
+                                             sc.direct_sg, sc.failed, sc.s_nfail, red_d);
     if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk.R);
     if (MODE == 1 && a.stats && tid == 0) {
       RowStats st;
@@ -1143,20 +1159,19 @@ __device__ __forceinline__ void merge_parts(const RowPairArgs& a, int64_t unit, 
 // streams part blockIdx % split of row (pair) blockIdx / split and stores its lane records.
 // PHASE 2: one workgroup per row (pair) folds the records and finishes it.
 template <int DT, bool VEC, int PHASE>
-__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(SV_ROWS_WAVES_PER_EU)))
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ LaneAcc lacc[kRowThreads];
   __shared__ double direct[kRowThreads];
   __shared__ double direct_sg[kRowThreads];
   __shared__ int failed[kRowThreads];
-  __shared__ float ipart[kRereadItems];
-  __shared__ float igpart[kRereadItems];
   __shared__ int s_nfail;
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
   __shared__ int s_req, s_off, s_t, s_void;
   __shared__ float s_T;
+  const Scratch sc{lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i};
   const int tid = thread_index();
   const int64_t blk = block_index();
   const int64_t unit = PHASE == 1 ? blk / a.split : blk;
@@ -1186,11 +1201,9 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
-      rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     -1);
+      rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, -1);
     } else {
-      rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i,
-                                     -1);
+      rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, sc, -1);
     }
     return;
   }
@@ -1227,13 +1240,13 @@ void sv_rowpair_kernel(RowPairArgs a) {
   ctx.row_flags = flags;  // thread 0 adds the token and uniform bits after the stream
   if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
   if (ctx.d >= 0) {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, sc, xr);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, xr);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, true, 2>(a, ctx, sc, xr);
   } else {
-    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
-    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
-    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, lacc, direct, direct_sg, failed, &s_nfail, ipart, igpart, red_d, red_f, red_i, xr);
+    if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, false, 0>(a, ctx, sc, xr);
+    if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, false, 1>(a, ctx, sc, xr);
+    if (ctx.mode == 2) rowpair_body<DT, VEC, PHASE, false, 2>(a, ctx, sc, xr);
   }
 }
 

@@ -9,13 +9,12 @@ Comparison rules (fp32 GPU against the float64 oracle):
   reported, and the rest of that request is not compared.  Greedy decisions have
   infinite margin and must always match.
 * p_T(x_i), q_T(x_i): |got - ref| <= 1e-5 |ref|.
-* clipped reverse-KL: |got - ref| <= 1e-5 max(|ref|, sum_y |min(delta, t_y)|) + 2^-21.
-  The absolute floor is the resolution of fp32 accumulation itself: each row's
-  log-normaliser comes from fp32 exponentials and fp32 slice sums (relative error
-  ~1e-7 of the sum), and an error eps in LZ_p - LZ_q moves R by ln2 * eps because
-  R = E_q[ln q - ln p] contains that difference with weight sum_y q_y = 1.  Rows whose
-  divergence is below ~1e-2 (nearly identical q and p, or V = 1) would otherwise be held
-  to an absolute accuracy fp32 cannot express.
+* clipped reverse-KL: |got - ref| <= 1e-5 max(|ref|, sum_y |min(delta, t_y)|) + 1e-12.
+  The relative bar is the one the verification path is built to (fp32 accumulation,
+  lanes that hold most of a row's mass summed again in fp64).  The absolute floor covers
+  only the fp64 rounding of the finalize, which forms R from per-lane terms of up to
+  ~100 (log2 units times mass) that cancel: ~1e-14.  It matters only where the scale is
+  0 or nearly so (q equal to p up to a constant, V = 1).
 """
 
 from __future__ import annotations
@@ -27,7 +26,7 @@ import oracle
 
 MARGIN = 1e-5
 RTOL = 1e-5
-RKL_ABS = 2.0**-21
+RKL_ABS = 1e-12
 
 
 def to_device(w, dev="cuda:0"):

@@ -13,7 +13,8 @@ from synth import make_workload, workload
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from gpu_util import compare, run_gpu, run_oracle, to_device  # noqa: E402
+from gpu_util import RKL_ABS, compare, run_gpu, run_oracle, to_device  # noqa: E402
+from oracle_pool import oracle_refs  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -158,25 +159,23 @@ def large_vocab():
     return workload("large_vocab")
 
 
-def test_high_concurrency_full_size_sampled(high_concurrency):
+def test_high_concurrency_full_size_all_requests(high_concurrency):
     w = high_concurrency
     dev = to_device(w)
     got = run_gpu(w, dev)
     assert got["device_status"][0] == 0
-    # every request: structural properties
     assert np.all((got["accept_len"] >= 0) & (got["accept_len"] <= 15))
-    assert np.all(np.isfinite(got["rkl"])) and np.all(got["rkl"] <= w.delta * w.V)
-    # a sample of requests against the oracle, one by one
-    sample = [0, 1, 17, 63, 64, 100, 126, 127]
-    s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
-    _report("high concurrency sampled", s)
+    # every request against the oracle (run in parallel worker processes)
+    s = compare(w, got, oracle_refs(w))
+    _report("high concurrency, all 128 requests", s)
+    assert s["exact"] + len(s["flips"]) == w.B
     # bitwise determinism at full size
     again = run_gpu(w, dev)
     for key in ("accept_len", "out_tokens", "rkl", "p_at_draft", "q_at_draft"):
         np.testing.assert_array_equal(got[key], again[key])
 
 
-def test_large_vocab_full_size_edge_cases(large_vocab):
+def test_large_vocab_full_size_all_requests(large_vocab):
     w = large_vocab
     got = run_gpu(w)
     assert got["device_status"][0] == 0
@@ -187,9 +186,9 @@ def test_large_vocab_full_size_edge_cases(large_vocab):
         assert np.all(got["rkl"][d0: d0 + 15] == 0.0)
     for b in fr:
         assert got["accept_len"][b] == 0
-    sample = sorted(set(aa[:2]) | set(fr[:2]) | {5, 77})
-    s = compare(w, got, run_oracle(w, requests=sample), requests=sample)
-    _report("large vocab sampled", s)
+    s = compare(w, got, oracle_refs(w))
+    _report("large vocab, all 128 requests", s)
+    assert s["exact"] + len(s["flips"]) == w.B
 
 
 # ----------------------------------------------------------------------------- edge cases
@@ -321,7 +320,7 @@ def test_clipped_rkl_standalone(dtype):
         dl = oracle.widen_logits(w.draft[:, : w.V], dtype)
         for r in range(w.n_draft_rows):
             ref = oracle.clipped_rkl_row(tl[idx[r]], dl[r], delta)
-            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21
+            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + RKL_ABS
             assert abs(got[r] - ref["R"]) <= tol, (r, got[r], ref["R"])
     # out-of-range pairing is flagged and gives NaN for that row only
     idx[0] = w.n_target_rows
@@ -386,7 +385,7 @@ def test_split_rows_standalone_and_fused():
         o = out.cpu().numpy().astype(np.float64)
         for r in range(w.n_draft_rows):
             ref = oracle.clipped_rkl_row(tl[idx[::-1][r]], dl[r], delta)
-            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21
+            tol = 1e-5 * max(abs(ref["R"]), ref["L1"]) + RKL_ABS
             assert abs(o[r] - ref["R"]) <= tol, (delta, r, o[r], ref["R"])
     # an out-of-range pairing gives NaN for that row only
     bad = idx.copy()
@@ -460,7 +459,7 @@ def test_workspace_without_split_records():
     o = out.cpu().numpy().astype(np.float64)
     for r in range(n):
         ref = oracle.clipped_rkl_row(tl[r], dl[r], w.delta)
-        assert abs(o[r] - ref["R"]) <= 1e-5 * max(abs(ref["R"]), ref["L1"]) + 2.0**-21, r
+        assert abs(o[r] - ref["R"]) <= 1e-5 * max(abs(ref["R"]), ref["L1"]) + RKL_ABS, r
 
 
 # ----------------------------------------------------------------------------- maximum length
