@@ -55,15 +55,14 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build_library(verbose: bool = False, defines=(), out: str = LIB) -> str:
+def build_library(verbose: bool = False, out: str = LIB) -> str:
     """Compiles each source to an object (own flags), links the shared library."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    extra_defs = [f"-D{d}" for d in defines]
     for src, extra in SOURCES:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        _run([hipcc(), *FLAGS, *extra, *extra_defs, "-I", os.path.join(ROOT, "include"), "-c", src,
+        _run([hipcc(), *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src,
               "-o", obj], verbose)
         objs.append(obj)
     tmp = out + ".tmp"

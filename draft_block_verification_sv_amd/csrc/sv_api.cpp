@@ -3,6 +3,7 @@
 // invalid call returns its status without touching the device or the runtime.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -53,13 +54,17 @@ enum {
 };
 
 // ------------------------------------------------------------------ profiling
+// An opt-in diagnostic: while it is on, every launch is bracketed by a pair of HIP events on
+// the call's stream, and the pairs are folded into per-kernel totals when they are read.  While
+// it is off (the default) a launch reads one atomic flag and touches nothing else, so calls on
+// different streams never contend on the host.
 struct ProfRec {
   int kernel;
   hipEvent_t start, stop;
 };
 struct Profiler {
-  std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
+  std::mutex mu;  // guards everything below; taken only while profiling is on or being read
   std::vector<ProfRec> pending;
   std::vector<hipEvent_t> pool;
   int64_t launches[kNumKernels] = {};
@@ -70,6 +75,7 @@ Profiler& prof() {
   return p;
 }
 
+// Callers hold p.mu.
 hipEvent_t take_event() {
   Profiler& p = prof();
   if (!p.pool.empty()) {
@@ -81,8 +87,11 @@ hipEvent_t take_event() {
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
+void give_event(hipEvent_t e) {
+  if (e) prof().pool.push_back(e);
+}
 
-// Waits for pending event pairs and folds them into the per-kernel totals.
+// Waits for pending event pairs and folds them into the per-kernel totals (callers hold p.mu).
 hipError_t drain_pending() {
   Profiler& p = prof();
   hipError_t first = hipSuccess;
@@ -106,19 +115,17 @@ hipError_t drain_pending() {
 template <class F>
 hipError_t timed(int kernel, hipStream_t st, F&& launch) {
   Profiler& p = prof();
-  std::unique_lock<std::mutex> lock(p.mu);
-  if (!p.on) {
-    lock.unlock();
-    return launch();
-  }
+  if (!p.on.load(std::memory_order_relaxed)) return launch();
+  std::lock_guard<std::mutex> lock(p.mu);
   hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, st);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, st);
-  if (e != hipSuccess) return e;
+  hipError_t e = (a && b) ? hipEventRecord(a, st) : hipErrorOutOfMemory;
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, st);
+  if (e != hipSuccess) {  // the events go back to the pool; the launch error is the result
+    give_event(a);
+    give_event(b);
+    return e;
+  }
   p.pending.push_back({kernel, a, b});
   return hipSuccess;
 }
@@ -695,9 +702,7 @@ sv_status sv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* st
 }
 
 sv_status sv_profile_enable(int32_t on) {
-  Profiler& p = prof();
-  std::lock_guard<std::mutex> lock(p.mu);
-  p.on = on != 0;
+  prof().on.store(on != 0, std::memory_order_relaxed);
   return SV_OK;
 }
 

@@ -130,15 +130,13 @@ struct HeadArgs {
   int32_t* k_hat;   // [B]
   int32_t* off_t;   // [B + 1] or null
 };
-#ifndef SV_HEAD_SPLIT_TARGET
-#define SV_HEAD_SPLIT_TARGET 512  // workgroups the projection's K split aims for
-#endif
+constexpr int64_t kHeadSplitTarget = 512;  // workgroups the projection's K split aims for
 // Blocks per workgroup and features per workgroup of the projection.
 constexpr int kHeadBlocks = 4;
 constexpr int kHeadTileN = 64;
 constexpr int kHeadMaxSplit = 8;  // K-chunks at most
 // The split of the projection for a head call: K-chunks so that the grid has about
-// SV_HEAD_SPLIT_TARGET workgroups (at most kHeadMaxSplit chunks, at least one K step of 32
+// kHeadSplitTarget workgroups (at most kHeadMaxSplit chunks, at least one K step of 32
 // each).
 inline HeadArgs head_split(int64_t B, int32_t k, int32_t H, int32_t Hf) {
   HeadArgs a{};
@@ -149,7 +147,7 @@ inline HeadArgs head_split(int64_t B, int32_t k, int32_t H, int32_t Hf) {
   a.R = (k + 15) / 16;
   a.NB = B * a.R;
   const int64_t tiles = ((a.NB + kHeadBlocks - 1) / kHeadBlocks) * ((Hf + kHeadTileN - 1) / kHeadTileN);
-  int64_t S = (SV_HEAD_SPLIT_TARGET + tiles - 1) / tiles;
+  int64_t S = (kHeadSplitTarget + tiles - 1) / tiles;
   S = S < 1 ? 1 : (S > kHeadMaxSplit ? kHeadMaxSplit : S);
   if (S > H / 32) S = H / 32;
   a.S = static_cast<int32_t>(S);

@@ -11,10 +11,7 @@ namespace sv {
 // kElemsPerLane elements, in groups of 8 consecutive columns 512 columns apart.  At
 // 32 elements a bf16 slice of a row pair is 8 KiB, read with eight 16-byte loads per
 // lane, all issued before any arithmetic.
-#ifndef SV_ELEMS_PER_LANE
-#define SV_ELEMS_PER_LANE 16
-#endif
-constexpr int kElemsPerLane = SV_ELEMS_PER_LANE;
+constexpr int kElemsPerLane = 16;
 static_assert(kElemsPerLane % 8 == 0 && kElemsPerLane >= 8, "groups of 8 columns per lane");
 constexpr int kGroups = kElemsPerLane / 8;
 constexpr int kSlice = 64 * kElemsPerLane;
@@ -44,18 +41,16 @@ inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 // Small launches split each row (pair) over several streaming workgroups, which store their
 // lane records (at most kLaneRecBytes each) for a finalize launch.  Only launches of at most
 // kSplitMaxUnits rows split (with more, one workgroup per row already covers most of the chip
-// and the finalize launch costs more than it saves); they aim at about SV_SPLIT_TARGET
+// and the finalize launch costs more than it saves); they aim at about kSplitTarget
 // streaming workgroups, with at most 16 parts per row, at least two slices per wave and at
 // most kSplitSlots record sets in all.
-#ifndef SV_SPLIT_TARGET
-#define SV_SPLIT_TARGET 512
-#endif
+constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMaxUnits = 128;
 constexpr int64_t kSplitSlots = 1024;
 constexpr size_t kLaneRecBytes = 72;
 inline int row_split(int64_t n_units, int64_t n_slices) {
-  if (SV_SPLIT_TARGET < 2 || n_units < 1 || n_units > kSplitMaxUnits) return 1;
-  int64_t P = (SV_SPLIT_TARGET + n_units - 1) / n_units;
+  if (n_units < 1 || n_units > kSplitMaxUnits) return 1;
+  int64_t P = (kSplitTarget + n_units - 1) / n_units;
   if (P > 16) P = 16;
   if (P > n_slices / 8) P = n_slices / 8;
   if (P > kSplitSlots / n_units) P = kSplitSlots / n_units;

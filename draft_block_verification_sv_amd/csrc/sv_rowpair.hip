@@ -66,10 +66,14 @@ __device__ __forceinline__ bool uniform_ok(float u) {
   const uint32_t b = __float_as_uint(u);
   return b < 0x3f800000u || b == 0x80000000u;
 }
-// Temperature valid iff +-0 or a positive normal finite number.
+// Temperature valid iff +-0 (greedy) or finite and at least kMinTemperature = 2^-10.  The
+// stream forms exponents as fma(l, log2(e) / T, -k) with whole-number fp32 offsets k, and the
+// draw rebuilds p_T from the fp32 offset -round(LZ_T); both are exact only while
+// |l| log2(e) / T stays below 2^24, i.e. |l| < 11360 at the minimum temperature.  Below it,
+// greedy decoding (T = 0) is the limit the caller wants.
 __device__ __forceinline__ bool temperature_ok(float T) {
   const uint32_t b = __float_as_uint(T);
-  return (b & 0x7fffffffu) == 0u || (b >= 0x00800000u && b < 0x7f800000u);
+  return (b & 0x7fffffffu) == 0u || (b >= 0x3a800000u && b < 0x7f800000u);
 }
 
 // One 16-byte streaming load (nontemporal: every byte is read once).

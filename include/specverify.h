@@ -80,7 +80,7 @@ enum {
   SV_DEV_BAD_LENGTH = 1,       /* some k_b outside [1, k_max]: the whole call is void     */
   SV_DEV_ROWS_MISMATCH = 2,    /* sum_b k_b != n_draft_rows: the whole call is void       */
   SV_DEV_BAD_TOKEN = 4,        /* a draft token outside [0, V)                            */
-  SV_DEV_BAD_TEMPERATURE = 8,  /* a T_b negative, not finite, or positive below FLT_MIN   */
+  SV_DEV_BAD_TEMPERATURE = 8,  /* a T_b negative, not finite, or in (0, 2^-10)           */
   SV_DEV_BAD_UNIFORM = 16,     /* a uniform outside [0, 1) or NaN                         */
   SV_DEV_BAD_PARENT = 32       /* a tree node whose parent is not an earlier node or -1   */
 };
@@ -115,7 +115,9 @@ size_t sv_workspace_size(int32_t B, int32_t k_max, int64_t V, int32_t dtype);
  *   draft_tokens    int32[n_draft_rows], ids in [0, V)
  *   uniforms        float[n_draft_rows + B] in [0, 1): slot i < k_b of a request is the
  *                   acceptance uniform of draft i, slot k_b drives the final token.
- *   temperature     float[B], T_b >= 0 (0 = greedy), or NULL for all 1.0.
+ *   temperature     float[B], T_b = 0 (greedy) or 2^-10 <= T_b < inf, or NULL for all 1.0.
+ *                   Positive temperatures below 2^-10 are flagged SV_DEV_BAD_TEMPERATURE:
+ *                   the fp32 exponent offsets are exact only while |l| log2(e) / T_b < 2^24.
  *   delta           clip threshold of the reverse-KL (finite, > 0 when rkl_out != NULL).
  * Outputs (device):
  *   accept_len      int32[B]: a_b, the accepted drafts (0..k_b); -1 for an invalid request.

@@ -268,6 +268,21 @@ def test_invalid_requests_are_flagged_not_fatal():
     assert np.all(np.isfinite(got["rkl"]))  # the divergence does not depend on tokens
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_temperature_limits(dtype):
+    # T_b = 2^-10, the smallest accepted temperature, against the oracle; positive
+    # temperatures below it (1e-9, a subnormal) are flagged and only their request is void
+    w = make_workload(B=4, k=[3, 4, 2, 5], V=3001, dtype=dtype, s=3.0, sigma=0.05,
+                      temperature=[2.0**-10, 1e-9, 1.0, 1e-40], seed=(21, dtype == "bf16"))
+    got = run_gpu(w)
+    st = int(got["device_status"][0])
+    assert st == 8, st
+    assert got["accept_len"][1] == -1 and got["accept_len"][3] == -1
+    s = compare(w, got, run_oracle(w, requests=[0, 2]), requests=[0, 2])
+    _report(f"temperature limits {dtype}", s)
+    assert s["exact"] + len(s["flips"]) == 2
+
+
 def test_void_calls():
     w = make_workload(B=3, k=[2, 2, 2], V=300, dtype="bf16", seed=(8,))
     bad = w.k.copy()
