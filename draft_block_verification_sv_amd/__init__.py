@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     read_probe,
     verify_block,
     verify_block_greedy,
+    verify_block_noalloc,
     verify_tree_greedy,
     version,
     workspace_size,

@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
                                   _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f32,
                                   _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_verify_block.restype = _c_i32
+    L.sv_verify_block_noalloc.argtypes = [_c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f32,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]
+    L.sv_verify_block_noalloc.restype = _c_i32
     L.sv_clipped_rkl.argtypes = [_c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
                                  _c_p, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.sv_clipped_rkl.restype = _c_i32
@@ -571,3 +575,47 @@ def profile_read() -> dict:
         if n.value:
             res[buf.value.decode()] = (int(n.value), float(ms.value))
     return res
+
+
+def verify_block_noalloc(target: torch.Tensor, draft: torch.Tensor, k: torch.Tensor,
+                         draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                         temperature: Optional[torch.Tensor], delta: float, out: dict, *,
+                         k_max: Optional[int] = None, stream=None) -> dict:
+    """sv_verify_block_noalloc: sv_verify_block on the library's own fixed scratch buffer.
+    Allocates nothing: the caller passes every output in ``out`` (accept_len, out_tokens,
+    device_status, and rkl / p_at_draft / q_at_draft or None)."""
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    code = _dtype_code(target)
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft must share a dtype")
+    if target.dim() != 2 or draft.dim() != 2 or target.stride(1) != 1 or draft.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit column stride")
+    B = int(k.numel())
+    n_d = int(draft.shape[0])
+    V = int(target.shape[1])
+    if int(draft.shape[1]) != V or int(target.shape[0]) != n_d + B:
+        raise ValueError(f"shapes: target {tuple(target.shape)} must be [n_draft_rows + B, V], "
+                         f"draft {tuple(draft.shape)} [n_draft_rows, V], B = {B}")
+    if k_max is None:
+        k_max = max(1, min(SV_MAX_K, n_d - B + 1))
+    _need(k, "k", torch.int32, B, dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, n_d, dev)
+    _need(uniforms, "uniforms", torch.float32, n_d + B, dev)
+    if temperature is not None:
+        _need(temperature, "temperature", torch.float32, B, dev)
+    _need(out["accept_len"], "accept_len", torch.int32, B, dev)
+    _need(out["out_tokens"], "out_tokens", torch.int32, n_d + B, dev)
+    for name in ("rkl", "p_at_draft", "q_at_draft"):
+        if out.get(name) is not None:
+            _need(out[name], name, torch.float32, n_d, dev)
+    _need(out["device_status"], "device_status", torch.int32, 1, dev)
+    st = lib().sv_verify_block_noalloc(
+        code, B, k_max, V, target.stride(0), draft.stride(0), n_d, _ptr(target), _ptr(draft),
+        _ptr(k), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), float(delta),
+        _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("rkl")),
+        _ptr(out.get("p_at_draft")), _ptr(out.get("q_at_draft")), _ptr(out["device_status"]),
+        _stream(stream))
+    _check(st, "sv_verify_block_noalloc")
+    return out

@@ -18,6 +18,7 @@ SOURCES = [
     (os.path.join(CSRC, "sv_kernels.hip"), []),
     (os.path.join(CSRC, "sv_head.hip"), []),
     (os.path.join(CSRC, "sv_diag.hip"), []),
+    (os.path.join(CSRC, "sv_noalloc.hip"), []),
     (os.path.join(CSRC, "sv_api.cpp"), []),
 ]
 HEADERS = [os.path.join(CSRC, f) for f in ("sv_device.h", "sv_layout.h", "sv_launch.h")] + [

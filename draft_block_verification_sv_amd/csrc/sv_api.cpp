@@ -271,6 +271,7 @@ const char* sv_status_string(sv_status s) {
     case SV_ERR_VALUE: return "delta must be finite and > 0 when the reverse-KL is requested";
     case SV_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or too small";
     case SV_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case SV_ERR_SCRATCH: return "the call needs more scratch than the library's fixed 16 MiB buffer holds";
     default: return "unknown status";
   }
 }

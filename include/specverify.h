@@ -69,7 +69,9 @@ enum {
   SV_ERR_DTYPE = 3,     /* dtype is not SV_BF16 / SV_F32                               */
   SV_ERR_VALUE = 4,     /* delta not finite or <= 0 while the rKL is requested         */
   SV_ERR_WORKSPACE = 5, /* workspace NULL, misaligned (256 B) or smaller than required */
-  SV_ERR_HIP = 6        /* a HIP runtime call or kernel launch failed                  */
+  SV_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed                  */
+  SV_ERR_SCRATCH = 7    /* sv_verify_block_noalloc: the call needs more scratch than the
+                           library's fixed buffer (SV_NOALLOC_SCRATCH_BYTES) holds       */
 };
 
 /* Logit element types. */
@@ -144,6 +146,32 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
                           int32_t* accept_len, int32_t* out_tokens, float* rkl_out,
                           float* p_at_draft, float* q_at_draft, int32_t* device_status,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sv_verify_block_noalloc: sv_verify_block for callers that cannot allocate device memory
+ * around the call (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  The same arguments and outputs as sv_verify_block, without the workspace: the
+ * call uses the library's own scratch, a fixed device array of SV_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * that each GPU the library runs on holds until the process ends.  Nothing is allocated per
+ * call (the array's address on a device is looked up once, on the first call there).
+ *
+ * Limit: calls whose workspace (sv_workspace_size) exceeds the buffer run like a caller
+ * workspace sized for a larger batch (each row streamed by one workgroup); calls that need
+ * more than the buffer even then return SV_ERR_SCRATCH and enqueue nothing.  At V = 151936
+ * and k_max = 15 that is beyond about 12000 requests (B = 128 needs 0.2 MiB).
+ * Concurrency: every call on one GPU shares that GPU's buffer, and each call overwrites it;
+ * calls that overlap on one GPU (several streams or host threads) race and must be serialised
+ * by the caller.  Errors otherwise as sv_verify_block.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+sv_status sv_verify_block_noalloc(int32_t dtype, int32_t B, int32_t k_max, int64_t V,
+                                  int64_t ld_target, int64_t ld_draft, int64_t n_draft_rows,
+                                  const void* target_logits, const void* draft_logits,
+                                  const int32_t* k, const int32_t* draft_tokens,
+                                  const float* uniforms, const float* temperature, float delta,
+                                  int32_t* accept_len, int32_t* out_tokens, float* rkl_out,
+                                  float* p_at_draft, float* q_at_draft, int32_t* device_status,
+                                  void* stream);
 
 /*
  * sv_verify_block_greedy: sv_verify_block for a batch whose every request decodes greedily

@@ -86,6 +86,24 @@ def test_verify_argument_errors(L):
     assert _verify(L, ws=256 * 4, ws_bytes=16) == 5  # too small
 
 
+def test_noalloc_argument_errors(L):
+    # every host-checkable problem is reported before the fixed scratch is looked up (no GPU
+    # here: any HIP call would fail with SV_ERR_HIP instead)
+    def call(dtype=0, B=1, k_max=4, V=100, n_d=1, ptrs=None, outs=None, delta=1.0):
+        ptrs = ptrs if ptrs is not None else [8] * 5 + [None]
+        outs = outs if outs is not None else [8, 8, None, None, None, 8]
+        return L.sv_verify_block_noalloc(dtype, B, k_max, V, V, V, n_d, *ptrs, delta, *outs, None)
+
+    assert call(dtype=3) == 3
+    assert call(B=0) == 2
+    assert call(k_max=65) == 2
+    assert call(n_d=5) == 2
+    assert call(ptrs=[None, 8, 8, 8, 8, None]) == 1
+    assert call(outs=[8, 8, None, None, None, None]) == 1
+    assert call(outs=[8, 8, 8, None, None, 8], delta=float("nan")) == 4
+    assert L.sv_status_string(7).decode().startswith("the call needs more scratch")
+
+
 def test_rkl_argument_errors(L):
     def call(dtype=1, n=2, nt=2, V=10, ldt=10, ldd=10, tp=8, dp=8, idx=None, delta=1.0, out=8,
              st=8, ws=None, wsb=0):
