@@ -35,7 +35,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "sv_rowpair_b128_k15_v151936_coun
 STREAM_KERNEL = "sv_rowpair"  # the kernel that streams the logits: the roofline kernel
 # the sources the streaming kernel is compiled from (its counters are void once they change)
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_verification_sv_amd", "csrc", f)
-                  for f in ("sv_rowpair.hip", "sv_device.h", "sv_layout.h", "sv_launch.h")]
+                  for f in ("sv_rowpair.hip", "sv_kernels.hip", "sv_device.h", "sv_lanes.h", "sv_layout.h", "sv_launch.h")]
 
 
 def log(*a):

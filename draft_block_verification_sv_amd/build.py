@@ -21,7 +21,7 @@ SOURCES = [
     (os.path.join(CSRC, "sv_noalloc.hip"), []),
     (os.path.join(CSRC, "sv_api.cpp"), []),
 ]
-HEADERS = [os.path.join(CSRC, f) for f in ("sv_device.h", "sv_layout.h", "sv_launch.h")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("sv_device.h", "sv_lanes.h", "sv_layout.h", "sv_launch.h")] + [
     os.path.join(ROOT, "include", "specverify.h")
 ]
 

@@ -353,6 +353,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.rowout = ws.rowout;
   ra.kmax1 = k_max + 1;
   ra.arrive = ws.arrive;
+  if (rkl_out) ra.fix = ws.fix;  // heavy lanes of the reverse-KL rows are summed by the draw launch
   if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR) != hipSuccess) return SV_ERR_HIP;
 
   sv::SampleArgs sa{};
@@ -380,6 +381,9 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.p_at = p_at_draft;
   sa.q_at = q_at_draft;
   sa.device_status = device_status;
+  sa.rkl_out = rkl_out;
+  sa.fix = ws.fix;
+  sa.n_slices = n_slices;
   if (timed(K_DRAW, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

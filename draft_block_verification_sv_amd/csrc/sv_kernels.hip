@@ -15,9 +15,10 @@
 // sv_clipped_rkl runs sv_rowpair alone and then sv_status.
 #include <float.h>
 #include <math.h>
+#include <stddef.h>
 
 #include "sv_device.h"
-
+#include "sv_lanes.h"
 #include "sv_layout.h"
 #include "sv_launch.h"
 
@@ -495,45 +496,115 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int
     chunk_masses_t<DT, VEC, WAVES, BATCH, false, DEVICE_OUT>(a, t, d, k, c_begin, c_end, wave, lane, out);
 }
 
-// sv_draw: workgroup g of request b computes the draw masses of chunks
-// [g * kMassChunksPerBlock, (g + 1) * kMassChunksPerBlock) of the request's draw row into
-// chunk_mass[b * n_chunks + c]; the last of the request's workgroups to finish (a ticket
-// from its arrival counter, after a device-wide fence) then draws the token from them:
-//   1. the chunk where the prefix of the masses first exceeds u * Z (u the request's last
-//      uniform, Z the total): one wave, lane l owning a run of consecutive chunks, fp64
-//      sums in chunk order and a fixed-order scan across the lanes;
-//   2. the column inside that chunk: one wave, 32 consecutive columns per lane, the fp64
-//      prefix again in column order; the row is read once more only there;
-//   3. emit: a_b accepted drafts, the final token, -1 after.
-// A residual whose masses sum to zero (rounding only) is redrawn from p_T of the same row,
-// whose chunk masses the picking workgroup then computes itself.  Greedy requests (and
-// every request of sv_verify_block_greedy) emit the target's argmax from workgroup 0; void
-// calls and invalid requests are written by workgroup 0, with their input-check bits.
-// Each wave derives the request state itself (a few cached loads), so only the pick needs
-// the workgroup's barrier.  Register use is capped so that all the workgroups of a B = 128
-// call are resident at once.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
-void sv_draw_kernel(SampleArgs a) {
-  __shared__ double s_pm[kMaxChunks];  // the picking wave's chunk masses (p_T's after a fallback)
-  __shared__ int s_last;
-  const int64_t b = blockIdx.x / a.mass_blocks;
-  const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int my_tok;    // lane i holds draft token i of the request
-  float my_u;    // and the uniform of target row i
-  const ReqState rq = wave_request_state(a, b, &my_tok, &my_u);
+// The clipped reverse-KL of draft row d (target row t), which the streaming pass left
+// provisional with a record of its heavy lanes (RklFix), finished by one wave: each heavy lane
+// is summed again from the logits in fp64 (exp2 in fp64, against the lane's own offsets), the
+// normalisers are formed with the new sums, and R moves to them.  With LZp, LZq the streaming
+// pass's normalisers and LZp', LZq' the new ones, c2 = LZp - LZq, c2' = LZp' - LZq' and
+// s = 2^-(LZq' - LZq), every term the pass kept, t_y = ln2 q_y (L2E (l_q - l_p)_y + c2) with
+// q_y = 2^(l_q L2E - LZq), becomes s t_y + s ln2 (c2' - c2) q_y unless it was clipped at delta
+// (the clip set is taken as the pass found it, its bound being 1e-4 away from delta).  Over
+// the lanes other than the heavy closed-form ones that is
+//   r_rest + (s - 1) u1 + s ln2 (c2' - c2) u0,
+// u1 the sum of their unclipped terms and u0 their q-mass; each heavy closed-form lane adds
+// ln2 2^(k_q - LZq') (L2E W + c2' S_q) with its new W and S_q.
+// A row's record as one 32-bit word per lane (lanes past the record hold 0); a wave reads it
+// with one vector load, early, and takes the fields out with readlane.  The load goes through a
+// bounds-checked buffer over the records (empty without them) and is issued with no branch
+// around it, so nothing waits for it before its first use; want = false reads 0.
+__device__ __forceinline__ uint32_t load_fix_words(const SampleArgs& a, int64_t d, bool want,
+                                                   int lane) {
+  const int bytes = (a.rkl_out && a.fix)
+                        ? static_cast<int>(a.B * (a.kmax1 - 1) * static_cast<int64_t>(sizeof(RklFix)))
+                        : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<RklFix*>(a.fix), 0, bytes, kBufWord3);
+  const int off = (want && lane < kFixDwords)
+                      ? static_cast<int>(d * static_cast<int64_t>(sizeof(RklFix))) + lane * 4
+                      : bytes;
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+}
+__device__ __forceinline__ int fix_word(uint32_t w, int i) { return __builtin_amdgcn_readlane(w, i); }
+__device__ __forceinline__ double fix_double(uint32_t w, int i) {
+  return __hiloint2double(fix_word(w, i + 1), fix_word(w, i));
+}
 
-  if (rq.void_call) {  // void call: the layout is unknown, so -1 everywhere, strided by B
-    if (g == 0) {
-      if (tid == 0) a.accept_len[b] = -1;
-      for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
-           t += static_cast<int64_t>(kMassThreads) * a.B)
-        a.out_tokens[t] = -1;
+template <int DT, bool VEC>
+__device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, int64_t t,
+                                               uint32_t rec, int lane) {
+  const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
+  if (n <= 0) return;
+  constexpr int es = DT == 0 ? 2 : 4;
+  const void* prow = static_cast<const char*>(a.target) + t * a.ld_t * es;
+  const void* qrow = static_cast<const char*>(a.draft) + d * a.ld_d * es;
+  const float Kp = __int_as_float(fix_word(rec, offsetof(RklFix, kp_ref) / 4));
+  const float Kq = __int_as_float(fix_word(rec, offsetof(RklFix, kq_ref) / 4));
+  double Sp = fix_double(rec, offsetof(RklFix, sp_rest) / 4);
+  double Sq = fix_double(rec, offsetof(RklFix, sq_rest) / 4);
+  double HW = 0.0, HS = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const int h0 = offsetof(RklFix, h) / 4 + j * 4;
+    const int src = fix_word(rec, h0);
+    const bool direct = fix_word(rec, h0 + 1) != 0;
+    const float hkp = __int_as_float(fix_word(rec, h0 + 2));
+    const float hkq = __int_as_float(fix_word(rec, h0 + 3));
+    const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, a.V, static_cast<int>(a.n_slices), src,
+                                                lane, static_cast<double>(hkp),
+                                                static_cast<double>(hkq));
+    const double sp = e.sp, sq = e.sq, w = e.w;
+    if (sp > 0.0) Sp += ldexp(sp, static_cast<int>(hkp - Kp));
+    if (sq > 0.0) {
+      const int e = static_cast<int>(hkq - Kq);
+      Sq += ldexp(sq, e);
+      if (!direct) {
+        HW += ldexp(w, e);
+        HS += ldexp(sq, e);
+      }
     }
-    return;
   }
+  const double LZp = static_cast<double>(Kp) + log2_d(Sp);
+  const double LZq = static_cast<double>(Kq) + log2_d(Sq);
+  const double dp = LZp - fix_double(rec, offsetof(RklFix, lzp) / 4);
+  const double dq = LZq - fix_double(rec, offsetof(RklFix, lzq) / 4);
+  const double s = exp2_d(-dq);
+  const double R = fix_double(rec, offsetof(RklFix, r_rest) / 4) +
+                   (s - 1.0) * fix_double(rec, offsetof(RklFix, u1) / 4) +
+                   s * kLn2 * (dp - dq) * fix_double(rec, offsetof(RklFix, u0) / 4) +
+                   kLn2 * exp2_d(static_cast<double>(Kq) - LZq) *
+                       (static_cast<double>(kL2E) * HW + (LZp - LZq) * HS);
+  if (lane == 0) a.rkl_out[d] = static_cast<float>(R);
+}
+
+// The rows of request b (draft rows off - b + i, target rows off + i, i < k_b) left to this
+// launch: row i goes to workgroup i % mass_blocks of the request, and there to wave
+// 3 - (i / mass_blocks) % 4, so that wave 0, which draws in the picking workgroup, comes last.
+// A wave's first row has its record loaded when the wave starts (first_fix_row /
+// load_fix_words), so that only the heavy lanes' columns are read after the draw; each wave
+// finishes its rows where it has nothing else left to do.
+__device__ __forceinline__ int first_fix_row(const SampleArgs& a, int g, int kb, int wave) {
+  const int i = g + (kMassWaves - 1 - wave) * a.mass_blocks;
+  return i < kb ? i : -1;
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void finish_rkl_rows(const SampleArgs& a, int64_t b, int g, int64_t off,
+                                                int kb, int wave, int lane, uint32_t first_rec) {
+  if (!a.rkl_out || !a.fix) return;
+  int j = 0;
+  for (int i = g; i < kb; i += a.mass_blocks, ++j) {
+    if (kMassWaves - 1 - (j % kMassWaves) != wave) continue;
+    const int64_t d = off - b + i;
+    const uint32_t rec = j < kMassWaves ? first_rec : load_fix_words(a, d, true, lane);
+    finish_rkl_row<DT, VEC>(a, d, off + i, rec, lane);
+  }
+}
+
+// One request's part of sv_draw for workgroup g (see the kernel below); returns once the
+// calling wave has nothing more to do for the draw.
+template <int DT, bool VEC>
+__device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int g, int tid, int lane,
+                                             int wave, int my_tok, float my_u, const ReqState& rq,
+                                             double* s_pm, int* s_last) {
   const int kb = rq.kb;
   const int64_t off = rq.off;
   if (rq.flags & kReqInvalid) {
@@ -581,10 +652,10 @@ void sv_draw_kernel(SampleArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (tid == 0)
-    s_last = (__hip_atomic_fetch_add(a.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    *s_last = (__hip_atomic_fetch_add(a.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               a.mass_blocks - 1) ? 1 : 0;
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_last) return;
 
   // ---- 1. chunk level (every wave computes the same total, so they agree on the fallback).
   // The masses are read back once; wave 0, which draws, keeps its lanes' masses in s_pm.
@@ -700,6 +771,54 @@ void sv_draw_kernel(SampleArgs a) {
     tok = __shfl(static_cast<int>(colL) + (lastc < 0 ? 0 : lastc), src, 64);
   }
   emit(tok);
+}
+
+// sv_draw: workgroup g of request b computes the draw masses of chunks
+// [g * kMassChunksPerBlock, (g + 1) * kMassChunksPerBlock) of the request's draw row into
+// chunk_mass[b * n_chunks + c]; the last of the request's workgroups to finish (a ticket
+// from its arrival counter, after a device-wide fence) then draws the token from them:
+//   1. the chunk where the prefix of the masses first exceeds u * Z (u the request's last
+//      uniform, Z the total): one wave, lane l owning a run of consecutive chunks, fp64
+//      sums in chunk order and a fixed-order scan across the lanes;
+//   2. the column inside that chunk: one wave, 32 consecutive columns per lane, the fp64
+//      prefix again in column order; the row is read once more only there;
+//   3. emit: a_b accepted drafts, the final token, -1 after.
+// A residual whose masses sum to zero (rounding only) is redrawn from p_T of the same row,
+// whose chunk masses the picking workgroup then computes itself.  Greedy requests (and
+// every request of sv_verify_block_greedy) emit the target's argmax from workgroup 0; void
+// calls and invalid requests are written by workgroup 0, with their input-check bits.
+// Each wave derives the request state itself (a few cached loads), so only the pick needs
+// the workgroup's barrier.  A wave done with the draw then finishes the request's reverse-KL
+// rows that the streaming pass left to this launch (finish_rkl_rows).  Register use is capped so that all the workgroups of a B = 128
+// call are resident at once.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void sv_draw_kernel(SampleArgs a) {
+  __shared__ double s_pm[kMaxChunks];  // the picking wave's chunk masses (p_T's after a fallback)
+  __shared__ int s_last;
+  const int64_t b = blockIdx.x / a.mass_blocks;
+  const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int my_tok;    // lane i holds draft token i of the request
+  float my_u;    // and the uniform of target row i
+  const ReqState rq = wave_request_state(a, b, &my_tok, &my_u);
+
+  if (rq.void_call) {  // void call: the layout is unknown, so -1 everywhere, strided by B
+    if (g == 0) {
+      if (tid == 0) a.accept_len[b] = -1;
+      for (int64_t t = b + static_cast<int64_t>(tid) * a.B; t < a.n_t;
+           t += static_cast<int64_t>(kMassThreads) * a.B)
+        a.out_tokens[t] = -1;
+    }
+    return;
+  }
+  // the record of this wave's first reverse-KL row left to this launch, read while it draws
+  const int i_fix = first_fix_row(a, g, rq.kb, wave);
+  const uint32_t fix_rec = load_fix_words(a, rq.off - b + (i_fix >= 0 ? i_fix : 0), i_fix >= 0, lane);
+  draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_last);
+  // each wave, once its part of the draw is done: the reverse-KL rows left to this launch
+  finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
 }
 
 // =========================================================================== branch lookup

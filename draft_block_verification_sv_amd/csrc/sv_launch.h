@@ -59,6 +59,8 @@ struct RowPairArgs {
   int32_t phase;
   int32_t split;
   void* rec;  // [n_units * split * kRowThreads] lane records (phases 1 and 2)
+  // verification with the reverse-KL, nullable: rows whose heavy lanes the draw launch sums
+  RklFix* fix;  // [n_d]
 };
 
 struct SampleArgs {
@@ -86,6 +88,10 @@ struct SampleArgs {
   float* p_at;
   float* q_at;
   int32_t* device_status;
+  // the reverse-KL rows the streaming pass left to this launch (nullable)
+  float* rkl_out;
+  const RklFix* fix;
+  int64_t n_slices;  // the streaming pass's slices per row (lane geometry of the records)
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);

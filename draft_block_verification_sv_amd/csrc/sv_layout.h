@@ -101,6 +101,32 @@ struct RowStats {
   int32_t pad;
 };
 
+// Verification with the clipped reverse-KL: a draft row whose heavy lanes (lanes holding much
+// of a row's mass, whose fp32 sums the streaming pass does not trust for the reverse-KL) number
+// at most kFixLanes is finished by the draw launch.  The streaming pass writes its provisional
+// reverse-KL and this record (n = 0 for every other row); the draw launch sums the heavy lanes
+// again in fp64, forms the normalisers with them and moves R to them.  Sums are in log2 units
+// as in the streaming pass.  The draw reads a record as kFixDwords 32-bit words, one per lane.
+constexpr int kFixLanes = 8;
+struct RklFixLane {
+  int32_t lane;    // thread of the streaming workgroup that owned the lane
+  int32_t direct;  // 1: the lane was summed term by term (near the clip); only its sums move
+  float kp, kq;    // the lane's exp2 offsets
+};
+struct RklFix {
+  double r_rest;            // R over every lane but the heavy closed-form ones
+  double u1, u0;            // over those lanes: unclipped terms, and their q-mass
+  double lzp, lzq;          // the normalisers the streaming pass used
+  double sp_rest, sq_rest;  // the other lanes' sums scaled to 2^kp_ref and 2^kq_ref
+  float kp_ref, kq_ref;     // the normalisers' reference offsets (largest lane offsets)
+  int32_t n, pad;  // n: heavy lanes recorded (0: R is final)
+  RklFixLane h[kFixLanes];
+};
+constexpr int kFixDwords = static_cast<int>(sizeof(RklFix) / 4);
+static_assert(sizeof(RklFix) % 8 == 0 && kFixDwords <= 64, "one word per lane of a wave");
+static_assert(offsetof(RklFix, kp_ref) == 56 && offsetof(RklFix, n) == 64 &&
+              offsetof(RklFix, h) == 72 && sizeof(RklFixLane) == 16, "word offsets the draw reads");
+
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
   int32_t* glob;       // [4]: [0] call void (bad lengths / row count)
@@ -113,6 +139,7 @@ struct Workspace {
   void* rec;           // [rec_slots * kRowThreads] lane records of split rows
   RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
   float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
+  RklFix* fix;         // [n_d] verification: heavy lanes left to the draw launch per draft row
 };
 
 struct Dims {
@@ -142,6 +169,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.rec = take(static_cast<size_t>(d.rec_slots) * kRowThreads * kLaneRecBytes);
   w.stats = reinterpret_cast<RowStats*>(take(d.n_grad * sizeof(RowStats)));
   w.coef = reinterpret_cast<float*>(take(d.n_grad * 2 * sizeof(float)));
+  w.fix = reinterpret_cast<RklFix*>(take(d.n_d * sizeof(RklFix)));
   if (ws) *ws = w;
   return off;
 }

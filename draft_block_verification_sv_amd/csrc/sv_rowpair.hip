@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include "sv_device.h"
+#include "sv_lanes.h"
 #include "sv_layout.h"
 #include "sv_launch.h"
 
@@ -51,12 +52,7 @@ __device__ __forceinline__ int64_t block_index() {
 }
 
 constexpr uint32_t kNaNBits = 0x7fc00000u;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer resources (stride 0, byte-addressed, 32-bit data format word) for the
-// bounds-checked loads of the streaming loop; the loads stream (nontemporal) like the
-// plain ones.
-constexpr int kBufWord3 = 0x00020000;
+// The bounds-checked loads of the streaming loop stream (nontemporal) like the plain ones.
 constexpr int kBufAux = 2;
 
 __device__ __forceinline__ void store_nan(float* p) { *reinterpret_cast<uint32_t*>(p) = kNaNBits; }
@@ -585,13 +581,57 @@ __device__ __forceinline__ void correct_top(double& S, float M, float scale, flo
   }
 }
 
-// log2 normaliser from every lane's (offset k, sum S): K + log2(sum_l S_l 2^(k_l - K)),
-// K the largest offset of a lane with mass; the scaling by 2^(k_l - K) is exact.
-__device__ __forceinline__ double lanes_lz(float k, double S, float* red_f, double* red_d) {
-  const float K = block_max_f(S > 0.0 ? k : -INFINITY, red_f);  // lanes with mass only
-  const double v = S > 0.0 ? ldexp(S, static_cast<int>(k - K)) : 0.0;
-  return static_cast<double>(K) + log2_d(block_sum_d(v, red_d));
+// Fixed-order reductions of N values per thread over the workgroup with one pair of barriers:
+// value j is summed, or with bit j of MAX set, maximised.  red: N * kRowWaves doubles.
+template <int N, unsigned MAX>
+__device__ __forceinline__ void block_reduce(double (&v)[N], double* red) {
+  const int lane = thread_index() & 63, wave = thread_index() >> 6;
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = ((MAX >> j) & 1u) ? wave_max_d(v[j]) : wave_sum_d(v[j]);
+  if (lane == 0)
+#pragma unroll
+    for (int j = 0; j < N; ++j) red[j * kRowWaves + wave] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    double r = red[j * kRowWaves];
+#pragma unroll
+    for (int w = 1; w < kRowWaves; ++w)
+      r = ((MAX >> j) & 1u) ? fmax(r, red[j * kRowWaves + w]) : r + red[j * kRowWaves + w];
+    v[j] = r;
+  }
+  __syncthreads();
 }
+
+// The log2 normalisers of N (offset, sum) pairs of every lane at once:
+// LZ_j = K_j + log2(sum_l S_jl 2^(k_jl - K_j)), K_j the largest offset of a lane with mass (the
+// scaling by 2^(k_jl - K_j) is exact).
+// With ARG, also the row's first argmax from every lane's (largest value, its column): the
+// largest value in the first round, the lowest column holding it in the second.
+template <int N, bool ARG>
+__device__ __forceinline__ void lanes_lz_n(const float (&k)[N], const double (&S)[N], double (&LZ)[N],
+                                           float (&K)[N], float amax, int aidx, int* argmax,
+                                           double* red) {
+  constexpr int NA = N + (ARG ? 1 : 0);
+  double m[NA];
+#pragma unroll
+  for (int j = 0; j < N; ++j) m[j] = S[j] > 0.0 ? static_cast<double>(k[j]) : -INFINITY;
+  if constexpr (ARG) m[N] = static_cast<double>(amax);
+  block_reduce<NA, (1u << NA) - 1u>(m, red);
+  double v[NA];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    K[j] = static_cast<float>(m[j]);
+    v[j] = S[j] > 0.0 ? ldexp(S[j], static_cast<int>(k[j] - K[j])) : 0.0;
+  }
+  // lowest column among the maxima, as the largest of -column
+  if constexpr (ARG) v[N] = (static_cast<double>(amax) == m[N]) ? -static_cast<double>(aidx) : -2147483647.0;
+  block_reduce<NA, ARG ? (1u << N) : 0u>(v, red);
+#pragma unroll
+  for (int j = 0; j < N; ++j) LZ[j] = static_cast<double>(K[j]) + log2_d(v[j]);
+  if constexpr (ARG) *argmax = static_cast<int>(-v[N]);
+}
+
 
 template <int DT>
 __device__ __forceinline__ float logit_at(const void* row, int64_t col) {
@@ -606,83 +646,6 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// ----------------------------------------------------------------------------- lane re-reads
-// Some lanes have their columns read again after the stream, one wave per lane: piece j of
-// lane src (8 consecutive columns: the lane's group j % kGroups of its slice
-// src / 64 + (j / kGroups) * kRowWaves) goes to thread j % 64 of the wave, two pieces in flight
-// per thread, every load issued before any arithmetic.  f(l_p, l_q) is applied to every
-// column of the lane inside [0, V), in a fixed order per thread; the wave's sums then combine
-// in a fixed tree, so the results do not depend on which lanes were listed or in what order.
-// The 8 logits of one piece as raw words: a bf16 piece is one 16-byte word, an fp32 piece two.
-// VEC rows are read through a bounds-checked buffer (a piece that is not valid, or the part of
-// one past V, reads zeros); other rows column by column with the column clamped into the row.
-template <int DT, bool VEC>
-struct Piece {
-  u32x4_t w0, w1;
-  __device__ __forceinline__ void load(const void* row, __amdgpu_buffer_rsrc_t rs, int64_t col0,
-                                       bool ok, int V) {
-    constexpr int es = DT == 0 ? 2 : 4;
-    if constexpr (VEC) {
-      const int off = ok ? static_cast<int>(col0) * es : V * es;
-      w0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-      if constexpr (DT == 1) w1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
-    } else {
-      int64_t c[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = ok ? (col0 + e < V ? col0 + e : V - 1) : 0;
-      if constexpr (DT == 0) {
-        const uint16_t* r = static_cast<const uint16_t*>(row);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w0[e] = static_cast<uint32_t>(r[c[2 * e]]) | (static_cast<uint32_t>(r[c[2 * e + 1]]) << 16);
-      } else {
-        const uint32_t* r = static_cast<const uint32_t*>(row);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[e] = r[c[e]];
-          w1[e] = r[c[e + 4]];
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ float at(int e) const {
-    if constexpr (DT == 0) return (e & 1) ? bf16_hi(w0[e >> 1]) : bf16_lo(w0[e >> 1]);
-    else return __uint_as_float(e < 4 ? w0[e] : w1[e - 4]);
-  }
-};
-
-template <int DT, bool VEC, class F>
-__device__ __forceinline__ void for_lane_columns(const void* prow, const void* qrow, int V,
-                                                 int n_slices, int src, int lane, F&& f) {
-  constexpr int es = DT == 0 ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t RQ =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(qrow), 0, V * es, kBufWord3);
-  const __amdgpu_buffer_rsrc_t RP =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(prow), 0, V * es, kBufWord3);
-  const int sw = src >> 6, sl = src & 63;
-  // the lane's slices are sw, sw + 4, ... < n_slices: kGroups pieces each
-  const int n_pieces = ((n_slices - sw + kRowWaves - 1) / kRowWaves) * kGroups;
-  for (int j0 = 0; j0 < n_pieces; j0 += 2 * 64) {
-    Piece<DT, VEC> pq[2], pp[2];
-    int64_t col[2];
-    bool ok[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = j0 + u * 64 + lane;
-      const int slice = sw + (j / kGroups) * kRowWaves;  // < n_slices whenever j < n_pieces
-      col[u] = static_cast<int64_t>(slice) * kSlice + (j % kGroups) * 512 + sl * 8;
-      ok[u] = j < n_pieces && col[u] < V;
-      pq[u].load(qrow, RQ, col[u], ok[u], V);
-      pp[u].load(prow, RP, col[u], ok[u], V);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (ok[u] && col[u] + e < V) f(pp[u].at(e), pq[u].at(e));
-  }
-}
-
 // Lists the lanes whose flag is set (order of arrival; users combine per lane, so the order
 // does not matter) and returns how many there are.
 __device__ __forceinline__ int list_lanes(bool flag, int* list, int* s_n) {
@@ -693,63 +656,22 @@ __device__ __forceinline__ int list_lanes(bool flag, int* list, int* s_n) {
   return *s_n;
 }
 
-// Exact sums of the lanes that carry the row's mass.  The stream's lane sums come from fp32
-// exponentials (one unit in the last place each) and fp32 partial sums of 16 elements, a
-// relative error of ~1e-7 of the lane's mass.  On a lane that holds most of a row's mass this
-// is an absolute error of ~1e-7 in the normaliser and, through the closed form below, in the
-// clipped reverse-KL, where L2E W and c2 S_q are two large terms that cancel to a small one
-// (one token dominating both rows).  Such rows have a small sum_y |min(delta, t_y)|, so the
-// error would be large against it.  A lane holding more than half of either row's mass, or
-// more than 1/32 of it with a closed form that cancels by a factor above 64, is therefore
-// summed again from the logits in fp64 (exponentials exact to ~1e-15), against the same
-// offsets; its S_p, S_q and W are replaced.  Returns whether any lane was replaced (the
-// normalisers must then be formed again).
-template <int DT, bool VEC>
-__device__ __forceinline__ bool exact_heavy_lanes(const void* prow, const void* qrow, int V,
-                                                  int n_slices, double LZp, double LZq,
-                                                  LaneAcc* lacc, int* list, int* s_n) {
-  const int tid = thread_index(), lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  bool heavy;
-  {
-    const LaneAcc& A = lacc[tid];
-    const double P = A.sp > 0.0 ? exp2_d(static_cast<double>(A.kp) - LZp) * A.sp : 0.0;
-    if (A.sq > 0.0) {
-      const double s = exp2_d(static_cast<double>(A.kq) - LZq);
-      const double c2 = LZp - LZq;
-      const double Q = s * A.sq;
-      const double closed = s * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
-      const double mag = s * (static_cast<double>(kL2E) * fabs(A.w) + fabs(c2) * A.sq);
-      const double big = fmax(P, Q);
-      heavy = big > 0.5 || (big > 1.0 / 32.0 && mag > 64.0 * fabs(closed));
-    } else {
-      heavy = P > 0.5;
-    }
-  }
-  const int n = list_lanes(heavy, list, s_n);
-  if (n == 0) return false;
-  for (int f = wave; f < n; f += kRowWaves) {
-    const int src = list[f];
-    const double kp = static_cast<double>(lacc[src].kp), kq = static_cast<double>(lacc[src].kq);
-    double sp = 0.0, sq = 0.0, w = 0.0;
-    for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src, lane, [&](float lp, float lq) {
-      const double eq = exp2_d(static_cast<double>(lq) * static_cast<double>(kL2E) - kq);
-      sp += exp2_d(static_cast<double>(lp) * static_cast<double>(kL2E) - kp);
-      sq += eq;
-      w += eq * (static_cast<double>(lq) - static_cast<double>(lp));
-    });
-    sp = wave_sum_d(sp);
-    sq = wave_sum_d(sq);
-    w = wave_sum_d(w);
-    if (lane == 0) {
-      lacc[src].sp = sp;
-      lacc[src].sq = sq;
-      lacc[src].w = w;
-    }
-  }
-  __syncthreads();
-  return true;
-}
+// The workgroup's LDS: the lane records, per-lane re-read results, the list of re-read
+// lanes and the block reductions' slots.
+struct Scratch {
+  LaneAcc* lacc;
+  double* direct;
+  double* direct_x;
+  double* direct_u0;
+  int* failed;
+  int* s_nfail;
+  int* s_nheavy;  // a counter of its own: the heavy list is read while the next one starts
+  double* red_d;
+  float* red_f;
+  int* red_i;
+  double* red_v;  // kRowWaves * kRowSums
+};
+constexpr int kRowSums = 6;  // values of the widest block reduction (lanes_lz_n: 5)
 
 // Clipped reverse-KL of the row pair.  With Q = 2^(k_q - LZq) S_q, the q-mass of a lane's
 // columns, and c2 = LZp - LZq, those columns contribute exactly
@@ -757,68 +679,153 @@ __device__ __forceinline__ bool exact_heavy_lanes(const void* prow, const void* 
 // and since t_y = ln2 q_y (L2E (l_q - l_p)_y + c2), none of them exceeds
 // ln2 Q max(0, L2E D + c2), D the lane's largest l_q - l_p, nor
 // ln2 2^(k_q - LZq) (L2E max(0, X) + max(0, c2) S_q), X the lane's largest E_q (l_q - l_p).
-// A lane whose smaller bound may reach delta has its columns re-read and summed entry by
-// entry: q_y from an fp32 exponential, the log ratio L2E (l_q - l_p) + c2 and the sums in fp64.
-// With SG, also sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the
-// OPD gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)): a passing lane adds its closed
-// form plus Q.
-struct RklSums {
-  double R, sg;
+// A lane whose smaller bound may reach delta (fail) has its columns re-read and summed entry
+// by entry; the others take the closed form.
+struct LaneClosed {
+  double closed, mass;  // ln2-scaled closed form, q-mass
+  bool fail;
 };
+__device__ __forceinline__ LaneClosed lane_closed(const LaneAcc& A, double LZp, double LZq,
+                                                  float delta) {
+  LaneClosed out{0.0, 0.0, false};
+  if (!(A.sq > 0.0)) return out;
+  const double c2 = LZp - LZq;
+  const double scale = kLn2 * exp2_d(static_cast<double>(A.kq) - LZq);
+  out.closed = scale * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
+  out.mass = scale * A.sq / kLn2;
+  // Two bounds on the lane's largest term t_y = scale E_y (L2E d_y + c2), d_y = l_q - l_p,
+  // both from max over y of a sum <= the sum of the maxima: its q-mass times the largest
+  // slope, and L2E max_y E_y d_y + max(c2, 0) S_q (every E_y >= 0, so no E_y exceeds S_q;
+  // the lane's offset need not cover its later slices).  The lane's sum is closed-form when
+  // the smaller one stays below delta.
+  const double slope = static_cast<double>(kL2E) * A.dmax + c2;
+  const double by_mass = scale * A.sq * (slope > 0.0 ? slope : 0.0);
+  const double by_peak = scale * (static_cast<double>(kL2E) * fmax(static_cast<double>(A.xmax), 0.0) +
+                                  (c2 > 0.0 ? c2 : 0.0) * A.sq);
+  const double bound = fmin(by_mass, by_peak);
+  out.fail = !(bound * 1.0001 < static_cast<double>(delta));
+  return out;
+}
 
-template <int DT, bool VEC, bool SG>
-__device__ __forceinline__ RklSums lanes_clipped_rkl(const void* prow, const void* qrow, int V,
-                                                    int n_slices, double LZp, double LZq,
-                                                    float delta, const LaneAcc& A, double* direct,
-                                                    double* direct_sg, int* failed, int* s_nfail,
-                                                    double* red) {
+// A lower bound on the row's sum_y |min(delta, t_y)| from one lane: |sum t_y| for a closed-form
+// lane, and for a lane near the clip the sum of its negative terms, at least -sum t_y.
+__device__ __forceinline__ double lane_l1_lower(const LaneClosed& L) {
+  return L.fail ? fmax(0.0, -L.closed) : fabs(L.closed);
+}
+
+// Exact sums of the lanes that carry the row's mass.  The stream's lane sums come from fp32
+// exponentials (one unit in the last place each) and fp32 partial sums of 16 elements, a
+// relative error of up to ~2.4e-7 of the lane's mass.  Through the normalisers that moves the
+// clipped reverse-KL by up to ~2.4e-7 (P + Q) (P, Q the lane's shares of the two rows), and
+// through its closed form, where L2E W and c2 S_q may be two large terms that cancel to a small
+// one, by up to ~2.4e-7 ln2 mag, mag = 2^(k_q - LZq) (L2E |W| + |c2| S_q).  Against the
+// accuracy the path is built to, 1e-5 max(|R|, L1) with L1 = sum_y |min(delta, t_y)|, a lane is
+// heavy when its share of that error exceeds an eighth of 1e-5 times a lower bound on L1 (the
+// sum of lane_l1_lower over the row), or when it holds more than half of either row's mass, or
+// more than 1/32 of it with a closed form that cancels by a factor above 64.  A lane whose two
+// rows are equal bit for bit (W = 0, same sums and offsets) rounds the same way in both, and
+// moves R only through c2: its share is 2 * 2.4e-7 ln2 mag.  Heavy lanes are summed again from
+// the logits in fp64 (exponentials exact to ~1e-15), against the same offsets, and their S_p,
+// S_q and W replaced.  In verification the draw launch does this for rows with at most
+// kFixLanes heavy lanes (RklFix); otherwise the finalize does it here.
+constexpr double kLaneSumErr = 2.4e-7;
+struct HeavyParts {
+  bool by_mass;  // the mass and cancellation rules
+  double err;    // the lane's share of the error, against 1e-5 L1 / 8
+};
+__device__ __forceinline__ HeavyParts heavy_parts(const LaneAcc& A, double LZp, double LZq) {
+  const double P = A.sp > 0.0 ? exp2_d(static_cast<double>(A.kp) - LZp) * A.sp : 0.0;
+  double Q = 0.0, closed = 0.0, mag = 0.0;
+  if (A.sq > 0.0) {
+    const double s = exp2_d(static_cast<double>(A.kq) - LZq);
+    const double c2 = LZp - LZq;
+    Q = s * A.sq;
+    closed = s * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
+    mag = s * (static_cast<double>(kL2E) * fabs(A.w) + fabs(c2) * A.sq);
+  }
+  const double big = fmax(P, Q);
+  const bool same = A.w == 0.0 && A.sp == A.sq && A.kp == A.kq;
+  HeavyParts h;
+  h.by_mass = big > 0.5 || (big > 1.0 / 32.0 && mag > 64.0 * fabs(closed));
+  h.err = kLaneSumErr * (same ? 2.0 * kLn2 * mag : P + Q + kLn2 * mag);  // 0 without mass
+  return h;
+}
+__device__ __forceinline__ double heavy_threshold(double L1lo) { return 1e-5 * L1lo * 0.125; }
+__device__ __forceinline__ bool is_heavy(const HeavyParts& h, double thr) {
+  return h.by_mass || h.err > thr;
+}
+
+// The n listed heavy lanes, one wave each, summed again; their records in lacc are replaced.
+template <int DT, bool VEC>
+__device__ __forceinline__ void exact_heavy_sums(const void* prow, const void* qrow, int V,
+                                                 int n_slices, LaneAcc* lacc, const int* list,
+                                                 int n) {
+  const int lane = thread_index() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(thread_index() >> 6);
+  for (int f = wave; f < n; f += kRowWaves) {
+    const int src = list[f];
+    const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, V, n_slices, src, lane,
+                                                static_cast<double>(lacc[src].kp),
+                                                static_cast<double>(lacc[src].kq));
+    if (lane == 0) {
+      lacc[src].sp = e.sp;
+      lacc[src].sq = e.sq;
+      lacc[src].w = e.w;
+    }
+  }
+  __syncthreads();
+}
+
+// The row's clipped reverse-KL, lane by lane (lane_closed): closed form, or for a lane near the
+// clip its columns re-read and summed entry by entry, q_y from an fp32 exponential, the log
+// ratio L2E (l_q - l_p) + c2 and the sums in fp64.
+// Per thread: its lane's closed form and q-mass, and whether it was re-read; the re-read lanes'
+// sums are in LDS on return: direct = sum_y min(t_y, delta).  With SG, also
+// direct_x = sum_y 1[t_y < delta] (t_y + q_y) = sum_y q_y g_y, the row statistic of the OPD
+// gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)), whose closed form on a passing lane is
+// the lane's closed form plus Q.  With FIX instead, direct_x = sum over the unclipped terms and
+// direct_u0 = their q-mass, from which the draw launch moves the lane's sum to new normalisers.
+template <int DT, bool VEC, bool SG, bool FIX>
+__device__ __forceinline__ LaneClosed lanes_clipped_rkl(const void* prow, const void* qrow, int V,
+                                                       int n_slices, double LZp, double LZq,
+                                                       float delta, const LaneAcc& A,
+                                                       const Scratch& sc) {
+  static_assert(!(SG && FIX), "one use of the extra per-lane sums at a time");
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double c2 = LZp - LZq;
-  double closed = 0.0, mass = 0.0;
-  bool fail = false;
-  if (A.sq > 0.0) {
-    const double scale = kLn2 * exp2_d(static_cast<double>(A.kq) - LZq);
-    closed = scale * (static_cast<double>(kL2E) * A.w + c2 * A.sq);
-    mass = scale * A.sq / kLn2;
-    // Two bounds on the lane's largest term t_y = scale E_y (L2E d_y + c2), d_y = l_q - l_p,
-    // both from max over y of a sum <= the sum of the maxima: its q-mass times the largest
-    // slope, and L2E max_y E_y d_y + max(c2, 0) S_q (every E_y >= 0, so no E_y exceeds S_q;
-    // the lane's offset need not cover its later slices).  The lane's sum is closed-form when
-    // the smaller one stays below delta.
-    const double slope = static_cast<double>(kL2E) * A.dmax + c2;
-    const double by_mass = scale * A.sq * (slope > 0.0 ? slope : 0.0);
-    const double by_peak = scale * (static_cast<double>(kL2E) * fmax(static_cast<double>(A.xmax), 0.0) +
-                                    (c2 > 0.0 ? c2 : 0.0) * A.sq);
-    const double bound = fmin(by_mass, by_peak);
-    fail = !(bound * 1.0001 < static_cast<double>(delta));
-  }
-  const int nfail = list_lanes(fail, failed, s_nfail);
+  const LaneClosed out = lane_closed(A, LZp, LZq, delta);
+  const int nfail = list_lanes(out.fail, sc.failed, sc.s_nfail);
   if (nfail > 0) {
     const double dd = static_cast<double>(delta);
     for (int f = wave; f < nfail; f += kRowWaves) {
-      const int src = failed[f];
-      double part = 0.0, gpart = 0.0;
+      const int src = sc.failed[f];
+      double part = 0.0, xpart = 0.0, u0 = 0.0;
       for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src, lane, [&](float lp, float lq) {
         const double a = static_cast<double>(lq) * static_cast<double>(kL2E);
         const double q = static_cast<double>(fast_exp2(static_cast<float>(a - LZq)));
         const double term =
             q * kLn2 * ((static_cast<double>(lq) - static_cast<double>(lp)) * static_cast<double>(kL2E) + c2);
         part += fmin(term, dd);
-        if constexpr (SG) gpart += term < dd ? term + q : 0.0;
+        if constexpr (SG) xpart += term < dd ? term + q : 0.0;
+        if constexpr (FIX) {
+          xpart += term < dd ? term : 0.0;
+          u0 += term < dd ? q : 0.0;
+        }
       });
       part = wave_sum_d(part);
-      if (lane == 0) direct[src] = part;
-      if constexpr (SG) {
-        gpart = wave_sum_d(gpart);
-        if (lane == 0) direct_sg[src] = gpart;
+      if (lane == 0) sc.direct[src] = part;
+      if constexpr (SG || FIX) {
+        xpart = wave_sum_d(xpart);
+        if (lane == 0) sc.direct_x[src] = xpart;
+      }
+      if constexpr (FIX) {
+        u0 = wave_sum_d(u0);
+        if (lane == 0) sc.direct_u0[src] = u0;
       }
     }
     __syncthreads();
   }
-  RklSums out;
-  out.R = block_sum_d(fail ? direct[tid] : closed, red);
-  out.sg = SG ? block_sum_d(fail ? direct_sg[tid] : closed + mass, red) : 0.0;
   return out;
 }
 
@@ -831,19 +838,6 @@ __device__ __forceinline__ void draw_offsets(double LZ, float* off, float* lz) {
 }
 
 // ----------------------------------------------------------------------------- kernel
-// The workgroup's LDS: the lane records, per-lane re-read results, the list of re-read
-// lanes and the block reductions' slots.
-struct Scratch {
-  LaneAcc* lacc;
-  double* direct;
-  double* direct_sg;
-  int* failed;
-  int* s_nfail;
-  double* red_d;
-  float* red_f;
-  int* red_i;
-};
-
 struct RowCtx {
   int64_t unit;  // the row (pair) this workgroup works on
   int part;      // which part of it, when rows are split over several workgroups
@@ -868,6 +862,39 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   const void* prow = static_cast<const char*>(a.target) + ctx.t * a.ld_t * (DT == 0 ? 2 : 4);
   const void* qrow = static_cast<const char*>(a.draft) + (PAIR ? ctx.d : 0) * a.ld_d * (DT == 0 ? 2 : 4);
 
+  // The uniform and the two logits at the draft token, for thread 0's acceptance test at the
+  // end, are loaded before the row is streamed: issued at the finalize they waited behind the
+  // streaming traffic of the other workgroups, at the end of every row.  Every thread issues the
+  // same three buffer loads, at offsets kept in bounds and with no branch around them (a load
+  // under a branch is waited for where the branch closes), so nothing waits for them before
+  // their use.  Buffers of zero length (no uniforms, an invalid token, a bonus row) read as 0
+  // and touch no memory.
+  const bool x_ok = PAIR && xr >= 0 && xr < V;
+  uint32_t u_bits = 0, lp_bits = 0, lq_bits = 0;
+  if constexpr (PHASE != 1) {
+    // a zero the compiler cannot see through: with it the loaded values are per-lane to the
+    // compiler, which then leaves them in vector registers instead of waiting for them at once
+    // to move them to scalar ones
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    constexpr int es = DT == 0 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t RU = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.uniforms), 0, a.uniforms ? static_cast<int>(a.n_units * 4) : 0, kBufWord3);
+    u_bits = __builtin_amdgcn_raw_buffer_load_b32(RU, static_cast<int>(ctx.t * 4) + vzero, 0, 0);
+    const int xoff = (x_ok ? xr : 0) * es + vzero;
+    const __amdgpu_buffer_rsrc_t RPX = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(prow))), 0, x_ok ? V * es : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t RQX = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(qrow))), 0, x_ok ? V * es : 0, kBufWord3);
+    if constexpr (DT == 0) {
+      lp_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RPX, xoff, 0, 0)) << 16;
+      lq_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RQX, xoff, 0, 0)) << 16;
+    } else {
+      lp_bits = __builtin_amdgcn_raw_buffer_load_b32(RPX, xoff, 0, 0);
+      lq_bits = __builtin_amdgcn_raw_buffer_load_b32(RQX, xoff, 0, 0);
+    }
+  }
+
   if constexpr (PHASE != 2) {  // stream the row (pair), or this workgroup's part of it
     LaneAcc L;
     lane_clear(L);
@@ -891,37 +918,6 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
 
-  // The uniform and the two logits at the draft token, for thread 0's acceptance test at the
-  // end.  Every thread issues the same three buffer loads, at offsets kept in bounds and with
-  // no branch around them: a load under a branch is waited for where the branch closes, which
-  // held the other waves at the first barrier below for two round trips behind the streaming
-  // traffic.  Loaded this way they are waited for only where they are used.  Buffers of zero
-  // length (no uniforms, an invalid token, a bonus row) read as 0 and touch no memory.
-  const bool x_ok = PAIR && xr >= 0 && xr < V;
-  uint32_t u_bits, lp_bits, lq_bits;
-  {
-    // a zero the compiler cannot see through: with it the loaded values are per-lane to the
-    // compiler, which then leaves them in vector registers instead of waiting for them at once
-    // to move them to scalar ones
-    int vzero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
-    constexpr int es = DT == 0 ? 2 : 4;
-    const __amdgpu_buffer_rsrc_t RU = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.uniforms), 0, a.uniforms ? static_cast<int>(a.n_units * 4) : 0, kBufWord3);
-    u_bits = __builtin_amdgcn_raw_buffer_load_b32(RU, static_cast<int>(ctx.t * 4) + vzero, 0, 0);
-    const int xoff = (x_ok ? xr : 0) * es + vzero;
-    const __amdgpu_buffer_rsrc_t RPX = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(prow))), 0, x_ok ? V * es : 0, kBufWord3);
-    const __amdgpu_buffer_rsrc_t RQX = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(qrow))), 0, x_ok ? V * es : 0, kBufWord3);
-    if constexpr (DT == 0) {
-      lp_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RPX, xoff, 0, 0)) << 16;
-      lq_bits = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(RQX, xoff, 0, 0)) << 16;
-    } else {
-      lp_bits = __builtin_amdgcn_raw_buffer_load_b32(RPX, xoff, 0, 0);
-      lq_bits = __builtin_amdgcn_raw_buffer_load_b32(RQX, xoff, 0, 0);
-    }
-  }
   // thread 0: the uniform's and the draft token's range checks
   auto input_flags = [&]() {
     int f = ctx.row_flags;
@@ -930,14 +926,30 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     return f;
   };
 
-  // target row: normalisers at T = 1 and T_b, argmax (lowest column among the maxima)
-  double LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);
-  const double LZTp0 = (MODE == 2) ? lanes_lz(A.ktp, A.stp, red_f, red_d) : LZ1p;
-  int argp = 0;
-  if constexpr (MODE == 1) {
-    const float Mx = block_max_f(A.amax, red_f);
-    argp = block_min_i(A.amax == Mx ? A.aidx : 0x7fffffff, sc.red_i);
+  // Normalisers at T = 1 and T_b of the target row (and the draft row), with the target's first
+  // argmax on greedy rows, in two rounds of block reductions.
+  constexpr int NZ = (PAIR ? 2 : 1) * (MODE == 2 ? 2 : 1);
+  float kz[NZ], Kz[NZ];
+  double sz[NZ], LZ[NZ];
+  kz[0] = A.kp;
+  sz[0] = A.sp;
+  if constexpr (PAIR) {
+    kz[1] = A.kq;
+    sz[1] = A.sq;
   }
+  if constexpr (MODE == 2) {
+    kz[NZ / 2] = A.ktp;
+    sz[NZ / 2] = A.stp;
+    if constexpr (PAIR) {
+      kz[3] = A.ktq;
+      sz[3] = A.stq;
+    }
+  }
+  int argp = 0;
+  lanes_lz_n<NZ, MODE == 1>(kz, sz, LZ, Kz, A.amax, A.aidx, &argp, sc.red_v);
+  double LZ1p = LZ[0];
+  const double LZTp0 = (MODE == 2) ? LZ[NZ / 2] : LZ1p;
+  const float Kp_ref = Kz[0];
   const float scale_T = (MODE == 2) ? ctx.beta : kL2E;
   RowOut* slot = ctx.b >= 0 ? a.rowout + ctx.b * a.kmax1 + ctx.pos : nullptr;
   if constexpr (!PAIR) {  // a bonus row: its offsets and flags for the draw
@@ -951,37 +963,125 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   }
 
   // draft row
-  double LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
-  if (a.rkl_out &&
-      exact_heavy_lanes<DT, VEC>(prow, qrow, V, n_slices, LZ1p, LZ1q, lacc, sc.failed, sc.s_nfail)) {
-    LZ1p = lanes_lz(A.kp, A.sp, red_f, red_d);  // A reads the replaced sums back
-    LZ1q = lanes_lz(A.kq, A.sq, red_f, red_d);
+  double LZ1q = LZ[PAIR ? 1 : 0];
+  const float Kq_ref = Kz[PAIR ? 1 : 0];
+  const double LZTq = (MODE == 2) ? LZ[NZ - 1] : LZ1q;
+  double Rsg = 0.0;
+  bool rkl_done = false;
+  bool heavy = false;
+  int n_heavy = 0, heavy_at = -1;
+  if (a.rkl_out) {
+    // One round decides the row: R over the closed-form lanes, a lower bound on L1, the lanes
+    // near the clip and the heavy lanes.  Most rows have neither and are done here.
+    const LaneClosed L0 = lane_closed(A, LZ1p, LZ1q, a.delta);
+    const HeavyParts hp = heavy_parts(A, LZ1p, LZ1q);
+    double v[6];
+    v[0] = L0.fail ? 0.0 : L0.closed;
+    v[1] = lane_l1_lower(L0);
+    v[2] = L0.fail ? 0.0 : L0.closed + L0.mass;
+    v[3] = L0.fail ? 1.0 : 0.0;
+    v[4] = hp.by_mass ? 1.0 : 0.0;
+    v[5] = hp.err;
+    block_reduce<6, 1u << 5>(v, sc.red_v);
+    const double thr = heavy_threshold(v[1]);
+    if (v[3] == 0.0 && v[4] == 0.0 && !(v[5] > thr)) {
+      rkl_done = true;
+      Rsg = v[2];
+      if (tid == 0) {
+        a.rkl_out[ctx.d] = static_cast<float>(v[0]);
+        if (a.fix) a.fix[ctx.d].n = 0;
+      }
+    } else {
+      heavy = is_heavy(hp, thr);
+      n_heavy = list_lanes(heavy, sc.failed, sc.s_nheavy);
+      if (a.fix && !a.stats && n_heavy <= kFixLanes) {
+        // left to the draw launch: each heavy thread notes its place in the list
+        if (heavy)
+          for (int j = 0; j < n_heavy; ++j)
+            if (sc.failed[j] == tid) heavy_at = j;
+      } else if (n_heavy > 0) {
+        exact_heavy_sums<DT, VEC>(prow, qrow, V, n_slices, lacc, sc.failed, n_heavy);
+        const float k2[2] = {A.kp, A.kq};  // A reads the replaced sums back
+        const double s2[2] = {A.sp, A.sq};
+        double lz2[2];
+        float K2[2];
+        lanes_lz_n<2, false>(k2, s2, lz2, K2, 0.0f, 0, nullptr, sc.red_v);
+        LZ1p = lz2[0];
+        LZ1q = lz2[1];
+        n_heavy = 0;
+      }
+    }
   }
   const double LZTp = (MODE == 2) ? LZTp0 : LZ1p;
-  const double LZTq = (MODE == 2) ? lanes_lz(A.ktq, A.stq, red_f, red_d) : LZ1q;
+  const double LZTqf = (MODE == 2) ? LZTq : LZ1q;
   if (tid == 0 && ctx.b >= 0) {
     draw_offsets(LZTp, &slot->offp, &slot->lzp);
     slot->beta = scale_T;
     slot->targ = argp;
   }
-  if (a.rkl_out) {
-    RklSums Rk;
-    if (MODE == 1 && a.stats)
-      Rk = lanes_clipped_rkl<DT, VEC, true>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, sc.direct,
-                                            sc.direct_sg, sc.failed, sc.s_nfail, red_d);
-    else
-      Rk = lanes_clipped_rkl<DT, VEC, false>(prow, qrow, V, n_slices, LZ1p, LZ1q, a.delta, A, sc.direct,
-                                             sc.direct_sg, sc.failed, sc.s_nfail, red_d);
-    if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(Rk.R);
-    if (MODE == 1 && a.stats && tid == 0) {
-      RowStats st;
-      st.lzp = LZ1p;
-      st.lzq = LZ1q;
-      st.sg = Rk.sg;
-      st.top1 = argp;
-      st.pad = 0;
-      a.stats[ctx.d] = st;
+  if (a.rkl_out && !rkl_done) {
+    if (MODE == 1 && a.stats) {
+      const LaneClosed L = lanes_clipped_rkl<DT, VEC, true, false>(prow, qrow, V, n_slices, LZ1p, LZ1q,
+                                                                   a.delta, A, sc);
+      double v[2] = {L.fail ? sc.direct[tid] : L.closed, L.fail ? sc.direct_x[tid] : L.closed + L.mass};
+      block_reduce<2, 0u>(v, sc.red_v);
+      Rsg = v[1];
+      if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(v[0]);
+    } else if (n_heavy == 0) {
+      const LaneClosed L = lanes_clipped_rkl<DT, VEC, false, false>(prow, qrow, V, n_slices, LZ1p, LZ1q,
+                                                                    a.delta, A, sc);
+      const double R = block_sum_d(L.fail ? sc.direct[tid] : L.closed, red_d);
+      if (tid == 0) {
+        a.rkl_out[ctx.d] = static_cast<float>(R);
+        if (a.fix) a.fix[ctx.d].n = 0;
+      }
+    } else {
+      // Provisional R, and the record the draw launch finishes it from: the heavy lanes that
+      // take the closed form (H) are summed apart; every other lane's part, its unclipped
+      // terms and their q-mass let the launch move it to the exact normalisers.
+      const LaneClosed L = lanes_clipped_rkl<DT, VEC, false, true>(prow, qrow, V, n_slices, LZ1p, LZ1q,
+                                                                   a.delta, A, sc);
+      const bool H = heavy && !L.fail;
+      double v[kRowSums];
+      v[0] = H ? 0.0 : (L.fail ? sc.direct[tid] : L.closed);
+      v[1] = H ? L.closed : 0.0;
+      v[2] = H ? 0.0 : (L.fail ? sc.direct_x[tid] : L.closed);
+      v[3] = H ? 0.0 : (L.fail ? sc.direct_u0[tid] : L.mass);
+      v[4] = (heavy || !(A.sp > 0.0)) ? 0.0 : ldexp(A.sp, static_cast<int>(A.kp - Kp_ref));
+      v[5] = (heavy || !(A.sq > 0.0)) ? 0.0 : ldexp(A.sq, static_cast<int>(A.kq - Kq_ref));
+      block_reduce<kRowSums, 0u>(v, sc.red_v);
+      RklFix* fx = a.fix + ctx.d;
+      if (heavy_at >= 0) {
+        RklFixLane h;
+        h.lane = tid;
+        h.direct = L.fail ? 1 : 0;
+        h.kp = A.kp;
+        h.kq = A.kq;
+        fx->h[heavy_at] = h;
+      }
+      if (tid == 0) {
+        fx->r_rest = v[0];
+        fx->u1 = v[2];
+        fx->u0 = v[3];
+        fx->lzp = LZ1p;
+        fx->lzq = LZ1q;
+        fx->sp_rest = v[4];
+        fx->sq_rest = v[5];
+        fx->kp_ref = Kp_ref;
+        fx->kq_ref = Kq_ref;
+        fx->n = n_heavy;
+        a.rkl_out[ctx.d] = static_cast<float>(v[0] + v[1]);
+      }
     }
+  }
+  if (MODE == 1 && a.stats && a.rkl_out && tid == 0) {
+    RowStats st;
+    st.lzp = LZ1p;
+    st.lzq = LZ1q;
+    st.sg = Rsg;
+    st.top1 = argp;
+    st.pad = 0;
+    a.stats[ctx.d] = st;
   }
   if constexpr (MODE == 1) {
     // hard-label cross-entropy against the target's top-1 (AdaFlash paper, Section 3.1):
@@ -993,13 +1093,13 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     }
   }
   if (tid == 0 && ctx.b >= 0) {
-    draw_offsets(LZTq, &slot->offq, &slot->lzq);
+    draw_offsets(LZTqf, &slot->offq, &slot->lzq);
     const int row_flags = input_flags();
     slot->flags = row_flags;
     int accept = 0;
     if (row_flags == 0) {  // the request's own flags are combined by the sampler
       const double Lp = static_cast<double>(__uint_as_float(lp_bits)) * scale_T - LZTp;  // log2 p_T(x)
-      const double Lq = static_cast<double>(__uint_as_float(lq_bits)) * scale_T - LZTq;  // log2 q_T(x)
+      const double Lq = static_cast<double>(__uint_as_float(lq_bits)) * scale_T - LZTqf;  // log2 q_T(x)
       if constexpr (MODE == 1) {
         accept = (xr == argp) ? 1 : 0;
       } else {
@@ -1030,6 +1130,7 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
   if (a.desc) {  // large batch: descriptors and offsets from sv_plan
     if (a.glob[0]) {
       if (tid == 0 && unit < a.n_d) {
+        if (a.fix) a.fix[unit].n = 0;
         if (a.rkl_out) store_nan(a.rkl_out + unit);
         if (a.p_at) store_nan(a.p_at + unit);
         if (a.q_at) store_nan(a.q_at + unit);
@@ -1117,6 +1218,7 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
     }
     if (vd) {
       if (tid == 0 && unit < a.n_d) {
+        if (a.fix) a.fix[unit].n = 0;
         if (a.rkl_out) store_nan(a.rkl_out + unit);
         if (a.p_at) store_nan(a.p_at + unit);
         if (a.q_at) store_nan(a.q_at + unit);
@@ -1167,15 +1269,17 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1))
 void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ LaneAcc lacc[kRowThreads];
   __shared__ double direct[kRowThreads];
-  __shared__ double direct_sg[kRowThreads];
+  __shared__ double direct_x[kRowThreads];
+  __shared__ double direct_u0[kRowThreads];
   __shared__ int failed[kRowThreads];
-  __shared__ int s_nfail;
+  __shared__ int s_nfail, s_nheavy;
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
+  __shared__ double red_v[kRowWaves * kRowSums];
   __shared__ int s_req, s_off, s_t, s_void;
   __shared__ float s_T;
-  const Scratch sc{lacc, direct, direct_sg, failed, &s_nfail, red_d, red_f, red_i};
+  const Scratch sc{lacc, direct, direct_x, direct_u0, failed, &s_nfail, &s_nheavy, red_d, red_f, red_i, red_v};
   const int tid = thread_index();
   const int64_t blk = block_index();
   const int64_t unit = PHASE == 1 ? blk / a.split : blk;

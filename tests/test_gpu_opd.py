@@ -147,11 +147,17 @@ def test_full_size_sampled():
     assert np.all(np.isfinite(got["hard_ce"].cpu().numpy()))
     t1 = got["top1"].cpu().numpy()
     assert np.all((t1 >= 0) & (t1 < w.V))
-    # the fused verification path reports the same reverse-KL bit for bit
+    # the fused verification path (whose heavy lanes are summed by the draw launch) meets the
+    # same bar on the same rows
     from gpu_util import run_gpu
 
     ver = run_gpu(w, d)
-    np.testing.assert_array_equal(got["rkl"].cpu().numpy(), ver["rkl"])
+    tl = oracle.widen_logits(w.target[:, : w.V], w.dtype)
+    dl = oracle.widen_logits(w.draft[:, : w.V], w.dtype)
+    for r in rows:
+        ref = oracle.clipped_rkl_row(tl[idx[r]], dl[r], w.delta)
+        tol = RTOL * max(abs(ref["R"]), ref["L1"]) + RKL_ABS
+        assert abs(float(ver["rkl"][r]) - ref["R"]) <= tol, (r, ver["rkl"][r], ref["R"])
 
 
 def test_bad_lengths_and_pairing_are_flagged():

@@ -13,7 +13,7 @@ from synth import make_workload, workload
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from gpu_util import RKL_ABS, compare, run_gpu, run_oracle, to_device  # noqa: E402
+from gpu_util import RKL_ABS, RTOL, compare, run_gpu, run_oracle, to_device  # noqa: E402
 from oracle_pool import oracle_refs  # noqa: E402
 
 
@@ -95,6 +95,52 @@ def test_small_delta_rereads_clipped_slices(delta):
     got = run_gpu(w)
     s = compare(w, got, run_oracle(w))
     _report(f"delta={delta}", s)
+
+
+# ----------------------------------------------------------------------------- heavy lanes
+# Rows whose mass sits on a few tokens in distinct lanes of the streaming workgroup (column
+# j 8 + (j % 4) 1024: slice j % 4, lane j), each shifted by one bf16 step between the target and
+# the draft, so that the reverse-KL of each such lane cancels strongly.  Requests cycle through
+# 12 such tokens (more heavy lanes than a row's record for the draw launch holds: summed in the
+# finalize), 6 and 2 (summed by the draw launch) and 1 token holding most of the mass.  4
+# requests split their rows over several workgroups; 40 do not.
+def _heavy_lane_workload(dtype, B, seed):
+    from synth import bf16_bits_from_f64
+
+    V = 20000
+    pattern = [12, 6, 2, 1]
+    k = [3, 2, 3, 2] * (B // 4)
+    w = make_workload(B=B, k=k, V=V, dtype=dtype, s=1.0, sigma=0.5, seed=seed)
+    rng = np.random.default_rng(list(seed) + [99])
+    to, do = w.target_offsets, w.draft_offsets
+
+    def put(arr, row, vals):
+        arr[row, :V] = bf16_bits_from_f64(vals) if dtype == "bf16" else vals.astype(np.float32)
+
+    for b in range(B):
+        n_tok = pattern[b % 4]
+        cols = np.array([j * 8 + (j % 4) * 1024 for j in range(n_tok)])
+        for i in range(int(w.k[b]) + 1):
+            lp = rng.standard_normal(V)
+            lp[cols] = (14.0 if n_tok > 1 else 12.0) + 0.25 * rng.standard_normal(n_tok)
+            put(w.target, to[b] + i, lp)
+            if i < w.k[b]:
+                lq = lp.copy()
+                lq[cols] += 0.0625
+                lq += 1e-3 * rng.standard_normal(V)
+                put(w.draft, do[b] + i, lq)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B", [4, 40])
+@pytest.mark.parametrize("delta", [1.0, 1e-3])
+def test_heavy_lanes(dtype, B, delta):
+    w = _heavy_lane_workload(dtype, B, (30, B, dtype == "f32"))
+    got = run_gpu(w, delta=delta)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w, delta=delta))
+    _report(f"heavy lanes {dtype} B={B} delta={delta}", s)
 
 
 @pytest.mark.parametrize("B", [1, 65])  # one request: split rows; 65 (130 rows): one WG per row
@@ -346,7 +392,19 @@ def test_clipped_rkl_standalone(dtype):
     assert np.isnan(o[0]) and np.all(np.isfinite(o[1:]))
 
 
-def test_fused_rkl_equals_standalone():
+def _both_meet_the_bar(w, idx, delta, standalone, fused):
+    import oracle
+
+    tl = oracle.widen_logits(w.target[:, : w.V], w.dtype)
+    dl = oracle.widen_logits(w.draft[:, : w.V], w.dtype)
+    for r in range(len(idx)):
+        ref = oracle.clipped_rkl_row(tl[idx[r]], dl[r], delta)
+        tol = RTOL * max(abs(ref["R"]), ref["L1"]) + RKL_ABS
+        for name, v in (("standalone", standalone), ("fused", fused)):
+            assert abs(float(v[r]) - ref["R"]) <= tol, (name, r, float(v[r]), ref["R"])
+
+
+def test_fused_rkl_and_standalone():
     import draft_block_verification_sv_amd as pkg
 
     w = make_workload(B=4, k=[3, 1, 5, 2], V=9000, dtype="bf16", seed=(12,))
@@ -358,7 +416,7 @@ def test_fused_rkl_equals_standalone():
                           for b in range(w.B)]).astype(np.int32)
     out, _ = pkg.clipped_rkl(d["target"], d["draft"], w.delta, torch.from_numpy(idx).cuda())
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(out.cpu().numpy(), got["rkl"])
+    _both_meet_the_bar(w, idx, w.delta, out.cpu().numpy(), got["rkl"])
 
 
 # ----------------------------------------------------------------------------- split rows
@@ -390,8 +448,9 @@ def test_split_rows_standalone_and_fused():
     out, st = pkg.clipped_rkl(d["target"], d["draft"], w.delta, torch.from_numpy(idx).cuda())
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    # the same pairing and the same split give the same bits
-    np.testing.assert_array_equal(out.cpu().numpy(), got["rkl"])
+    # the same pairing: both meet the bar (the verification call sums its heavy lanes in the
+    # draw launch, the standalone call in its finalize)
+    _both_meet_the_bar(w, idx, w.delta, out.cpu().numpy(), got["rkl"])
     tl = oracle.widen_logits(w.target[:, : w.V], "bf16")
     dl = oracle.widen_logits(w.draft[:, : w.V], "bf16")
     for delta in (1.0, 0.01):
