@@ -4,8 +4,8 @@
 //
 //   sv_head_feat   the projection z = W1 h^T as a split-K GEMM on v_mfma_f32_16x16x32_bf16.
 //                  A request's positions form ceil(k / 16) blocks of 16 rows; a workgroup
-//                  takes four blocks (one per wave) against one 64-feature tile (four MFMA
-//                  tiles) over one K-chunk, staged through LDS 32 columns at a time with
+//                  takes four blocks against all features (up to 256; wave w a quarter of
+//                  them) over one K-chunk, staged through LDS 32 columns at a time with
 //                  several stages in flight, and writes the fp32 partial sums of that chunk.
 //   sv_head_pool   one workgroup per request: z = sum of the K-chunks' partials in chunk order
 //                  + b1, SiLU, the mean over the k positions, a_hat = sigmoid(w2 . pooled + b2)
@@ -40,30 +40,35 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& w) {
   return v;
 }
 
-constexpr int kHeadStages = 8;  // 32-column K stages whose loads are in flight
+constexpr int kHeadStages = 4;   // 32-column K stages whose loads are in flight
 constexpr int kLdsRow = 32 + 8;  // bf16 per LDS row: one K stage plus 16 B of padding
+constexpr int kHeadThreads = 64 * kHeadBlocks;
+// 16-byte pieces of a stage each thread copies: one of the 64-row A stage, kBPieces of the
+// kHeadTileN-row B stage (64 bytes per row)
+constexpr int kBPieces = kHeadTileN * 4 / kHeadThreads;
+static_assert(kHeadBlocks == 4 && kBPieces == 4 && kBPieces * kHeadThreads == kHeadTileN * 4,
+              "stage copy layout: four B pieces per thread, named below");
+constexpr int kWaveFeatures = kHeadTileN / kHeadBlocks;  // features per wave
+constexpr int kWaveTiles = kWaveFeatures / 16;           // 16-feature MFMA tiles per wave
 
-__device__ __forceinline__ void fetch_stage(uint4& ra, uint4& rb, const uint16_t* gA,
-                                            const uint16_t* gB, int col) {
-  ra = *reinterpret_cast<const uint4*>(gA + col);
-  rb = *reinterpret_cast<const uint4*>(gB + col);
-}
-
-// One workgroup: blocks 4 g .. 4 g + 3 (64 rows; wave w computes block 4 g + w), features
-// n0 .. n0 + 63, K-chunk c, in stages of 32 columns.  Each thread copies one 16-byte piece of
-// the A stage (row tid / 4) and one of the B stage (feature row tid / 4): the 64 rows x 64
-// bytes of a stage are read in full 64-byte runs.  kHeadStages stages are in flight in
-// registers; a stage is written to one of two LDS buffers (rows padded to 80 bytes, so the
-// 16 rows a fragment read touches fall on distinct banks), the workgroup barrier publishes it,
-// the next stage's loads are issued, and each wave reads its A fragment and four B
-// fragments from LDS for four MFMAs.  Stage indices past the chunk are clamped (the last
-// stage again, from cache; never used).  Writes partial[((c NB + blk) 16 + row) H' + n].
-__global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs a) {
+// One workgroup: blocks 4 g .. 4 g + 3 (64 rows), features n0 .. n0 + kHeadTileN - 1 (all of
+// H' up to 256), K-chunk c, in stages of 32 columns.  Wave w computes every block against
+// features n0 + 64 w .. + 63 (4 blocks x 4 feature tiles = 16 MFMAs a stage), so each wave
+// reads 4 A and 4 B fragments per stage from LDS and h is read once per K-chunk.  Each thread
+// copies one 16-byte piece of the A stage (row tid / 4) and kBPieces of the B stage (feature
+// rows tid / 4 + 64 j): every row of a stage is read as a full 64-byte run.  kHeadStages stages
+// are in flight in registers; a stage is written to one of two LDS buffers (rows padded to 80
+// bytes, so the 16 rows a fragment read touches fall on distinct banks), the workgroup barrier
+// publishes it, the next stage's loads are issued, and each wave reads its fragments.  Stage
+// indices past the chunk are clamped (the last stage again, from cache; never used).  Writes
+// partial[((c NB + blk) 16 + row) H' + n].
+__global__ __launch_bounds__(kHeadThreads) void sv_head_feat_kernel(HeadArgs a) {
   __shared__ __align__(16) uint16_t sA[2][64 * kLdsRow];
-  __shared__ __align__(16) uint16_t sB[2][64 * kLdsRow];
+  __shared__ __align__(16) uint16_t sB[2][kHeadTileN * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n_rows = a.B * static_cast<int64_t>(a.k);
-  // this thread's copy piece: row cr of the stage, 16 bytes at column cc
+  // this thread's copy pieces: row cr of the A stage and feature rows cr + 64 j of the B stage,
+  // 16 bytes at column cc
   const int cr = tid >> 2, cc = (tid & 3) * 8;
   const int64_t cblk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + cr / 16;
   const int64_t cb = cblk / a.R;
@@ -71,82 +76,103 @@ __global__ __launch_bounds__(64 * kHeadBlocks) void sv_head_feat_kernel(HeadArgs
   int64_t hrow = cb * a.k + cpos;
   if (cpos >= a.k || hrow >= n_rows) hrow = n_rows - 1;  // clamped: row never used
   const int n0 = blockIdx.y * kHeadTileN;
-  const int wrow = min(n0 + cr, a.Hf - 1);                 // clamped: column never stored
   const uint16_t* gA = static_cast<const uint16_t*>(a.h) + hrow * a.ld_h + cc;
-  const uint16_t* gB = static_cast<const uint16_t*>(a.W1) + static_cast<int64_t>(wrow) * a.ld_w + cc;
+  // (clamped rows: columns never stored)
+  auto w1_row = [&](int j) {
+    return static_cast<const uint16_t*>(a.W1) +
+           static_cast<int64_t>(min(n0 + cr + 64 * j, a.Hf - 1)) * a.ld_w + cc;
+  };
+  const uint16_t* const gB0 = w1_row(0);
+  const uint16_t* const gB1 = w1_row(1);
+  const uint16_t* const gB2 = w1_row(2);
+  const uint16_t* const gB3 = w1_row(3);
   const int lds_w = cr * kLdsRow + cc;
-  // this lane's fragment reads: row r of its wave's block / of each feature tile, k offset kg
+  // this lane's fragment reads: row r of each block / of each of its wave's feature tiles,
+  // k offset kg
   const int r = lane & 15, kg = (lane >> 4) * 8;
-  const int ldsA = (wave * 16 + r) * kLdsRow + kg;
-  const int ldsB = r * kLdsRow + kg;
+  const int ldsA = r * kLdsRow + kg;
+  const int ldsB = (wave * kWaveFeatures + r) * kLdsRow + kg;
 
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *a.ticket = 0;
   const int c = blockIdx.z;
   const int steps = a.H / 32;
   const int s_lo = (c * steps) / a.S, s_hi = ((c + 1) * steps) / a.S;
   const int n_st = s_hi - s_lo;
-  f32x4_t acc[4];
+  f32x4_t acc[kHeadBlocks][kWaveTiles];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int bb = 0; bb < kHeadBlocks; ++bb)
+#pragma unroll
+    for (int t = 0; t < kWaveTiles; ++t) acc[bb][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the ring of stages in flight, as named registers (an array here would live in scratch)
-  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
-#define SV_HEAD_COL(st) (32 * (s_lo + min((st), n_st - 1)))
-  fetch_stage(ra0, rb0, gA, gB, SV_HEAD_COL(0));
-  fetch_stage(ra1, rb1, gA, gB, SV_HEAD_COL(1));
-  fetch_stage(ra2, rb2, gA, gB, SV_HEAD_COL(2));
-  fetch_stage(ra3, rb3, gA, gB, SV_HEAD_COL(3));
-  fetch_stage(ra4, rb4, gA, gB, SV_HEAD_COL(4));
-  fetch_stage(ra5, rb5, gA, gB, SV_HEAD_COL(5));
-  fetch_stage(ra6, rb6, gA, gB, SV_HEAD_COL(6));
-  fetch_stage(ra7, rb7, gA, gB, SV_HEAD_COL(7));
-  // stage i: publish it in LDS buffer i % 2, refill its ring slot with stage i + 8, then
-  // four MFMAs from LDS.  Full rounds of eight stages run without a condition (a load under a
-  // branch would make the wait at the join count the refills too); the last partial round is
-  // guarded by its stage index, uniform across the workgroup.
-#define SV_HEAD_STEP(J)                                                                     \
+  uint4 ra0, ra1, ra2, ra3;
+  uint4 rb0_0, rb0_1, rb0_2, rb0_3, rb1_0, rb1_1, rb1_2, rb1_3;
+  uint4 rb2_0, rb2_1, rb2_2, rb2_3, rb3_0, rb3_1, rb3_2, rb3_3;
+#define SV_HEAD_FETCH(J, st)                                                                \
   {                                                                                         \
-    *reinterpret_cast<uint4*>(&sA[(J) & 1][lds_w]) = ra##J;                                 \
-    *reinterpret_cast<uint4*>(&sB[(J) & 1][lds_w]) = rb##J;                                 \
+    const int col_ = 32 * (s_lo + min((st), n_st - 1));                                     \
+    ra##J = *reinterpret_cast<const uint4*>(gA + col_);                                     \
+    rb##J##_0 = *reinterpret_cast<const uint4*>(gB0 + col_);                                \
+    rb##J##_1 = *reinterpret_cast<const uint4*>(gB1 + col_);                                \
+    rb##J##_2 = *reinterpret_cast<const uint4*>(gB2 + col_);                                \
+    rb##J##_3 = *reinterpret_cast<const uint4*>(gB3 + col_);                                \
+  }
+  SV_HEAD_FETCH(0, 0)
+  SV_HEAD_FETCH(1, 1)
+  SV_HEAD_FETCH(2, 2)
+  SV_HEAD_FETCH(3, 3)
+  // stage i: publish it in LDS buffer i % 2, refill its ring slot with stage i + kHeadStages,
+  // then 16 MFMAs from LDS.  Full rounds run without a condition (a load under a branch would
+  // make the wait at the join count the refills too); the last partial round is guarded by its
+  // stage index, uniform across the workgroup.
+#define SV_HEAD_STEP(J, i)                                                                  \
+  {                                                                                         \
+    uint16_t* bA = sA[(J) & 1];                                                             \
+    uint16_t* bB = sB[(J) & 1];                                                             \
+    *reinterpret_cast<uint4*>(&bA[lds_w]) = ra##J;                                          \
+    *reinterpret_cast<uint4*>(&bB[lds_w]) = rb##J##_0;                                      \
+    *reinterpret_cast<uint4*>(&bB[lds_w + 64 * kLdsRow]) = rb##J##_1;                       \
+    *reinterpret_cast<uint4*>(&bB[lds_w + 128 * kLdsRow]) = rb##J##_2;                      \
+    *reinterpret_cast<uint4*>(&bB[lds_w + 192 * kLdsRow]) = rb##J##_3;                      \
     __syncthreads();                                                                        \
-    fetch_stage(ra##J, rb##J, gA, gB, SV_HEAD_COL(i0 + (J) + kHeadStages));                 \
-    const uint4 av = *reinterpret_cast<const uint4*>(&sA[(J) & 1][ldsA]);                   \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-      const uint4 bv = *reinterpret_cast<const uint4*>(&sB[(J) & 1][ldsB + t * 16 * kLdsRow]); \
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0); \
-    }                                                                                       \
+    SV_HEAD_FETCH(J, (i) + kHeadStages)                                                     \
+    uint4 av[kHeadBlocks], bv[kWaveTiles];                                                  \
+    _Pragma("unroll") for (int bb = 0; bb < kHeadBlocks; ++bb)                              \
+      av[bb] = *reinterpret_cast<const uint4*>(&bA[ldsA + bb * 16 * kLdsRow]);              \
+    _Pragma("unroll") for (int t = 0; t < kWaveTiles; ++t)                                  \
+      bv[t] = *reinterpret_cast<const uint4*>(&bB[ldsB + t * 16 * kLdsRow]);                \
+    _Pragma("unroll") for (int bb = 0; bb < kHeadBlocks; ++bb)                              \
+      _Pragma("unroll") for (int t = 0; t < kWaveTiles; ++t)                                \
+        acc[bb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[bb]),             \
+                                                             as_bf16x8(bv[t]), acc[bb][t],   \
+                                                             0, 0, 0);                      \
   }
   int i0 = 0;
   for (; i0 + kHeadStages <= n_st; i0 += kHeadStages) {
-    SV_HEAD_STEP(0)
-    SV_HEAD_STEP(1)
-    SV_HEAD_STEP(2)
-    SV_HEAD_STEP(3)
-    SV_HEAD_STEP(4)
-    SV_HEAD_STEP(5)
-    SV_HEAD_STEP(6)
-    SV_HEAD_STEP(7)
+    SV_HEAD_STEP(0, i0)
+    SV_HEAD_STEP(1, i0 + 1)
+    SV_HEAD_STEP(2, i0 + 2)
+    SV_HEAD_STEP(3, i0 + 3)
   }
   if (i0 < n_st) {
-    SV_HEAD_STEP(0)
-    if (i0 + 1 < n_st) SV_HEAD_STEP(1)
-    if (i0 + 2 < n_st) SV_HEAD_STEP(2)
-    if (i0 + 3 < n_st) SV_HEAD_STEP(3)
-    if (i0 + 4 < n_st) SV_HEAD_STEP(4)
-    if (i0 + 5 < n_st) SV_HEAD_STEP(5)
-    if (i0 + 6 < n_st) SV_HEAD_STEP(6)
+    SV_HEAD_STEP(0, i0)
+    if (i0 + 1 < n_st) SV_HEAD_STEP(1, i0 + 1)
+    if (i0 + 2 < n_st) SV_HEAD_STEP(2, i0 + 2)
   }
 #undef SV_HEAD_STEP
-#undef SV_HEAD_COL
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + wave;
-  if (blk >= a.NB) return;
-  // lane holds D[4 (l/16) + i][l % 16] of each feature tile t
-  float* P = a.partial + ((static_cast<int64_t>(c) * a.NB + blk) * 16 + 4 * (lane >> 4)) * a.Hf;
+#undef SV_HEAD_FETCH
+  // lane holds D[4 (l/16) + i][l % 16] of each (block, feature tile)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = n0 + 16 * t + r;
-    if (n < a.Hf)
+  for (int bb = 0; bb < kHeadBlocks; ++bb) {
+    const int64_t blk = static_cast<int64_t>(blockIdx.x) * kHeadBlocks + bb;
+    if (blk >= a.NB) continue;
+    float* P = a.partial + ((static_cast<int64_t>(c) * a.NB + blk) * 16 + 4 * (lane >> 4)) * a.Hf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) P[static_cast<int64_t>(i) * a.Hf + n] = acc[t][i];
+    for (int t = 0; t < kWaveTiles; ++t) {
+      const int n = n0 + wave * kWaveFeatures + 16 * t + r;
+      if (n < a.Hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[static_cast<int64_t>(i) * a.Hf + n] = acc[bb][t][i];
+    }
   }
 }
 
@@ -272,7 +298,7 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((a.NB + kHeadBlocks - 1) / kHeadBlocks),
                   static_cast<unsigned>((a.Hf + kHeadTileN - 1) / kHeadTileN),
                   static_cast<unsigned>(a.S));
-  hipLaunchKernelGGL(sv_head_feat_kernel, grid, dim3(64 * kHeadBlocks), 0, st, a);
+  hipLaunchKernelGGL(sv_head_feat_kernel, grid, dim3(kHeadThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -139,7 +139,7 @@ struct HeadArgs {
 constexpr int64_t kHeadSplitTarget = 512;  // workgroups the projection's K split aims for
 // Blocks per workgroup and features per workgroup of the projection.
 constexpr int kHeadBlocks = 4;
-constexpr int kHeadTileN = 64;
+constexpr int kHeadTileN = 256;
 constexpr int kHeadMaxSplit = 8;  // K-chunks at most
 // The split of the projection for a head call: K-chunks so that the grid has about
 // kHeadSplitTarget workgroups (at most kHeadMaxSplit chunks, at least one K step of 32
