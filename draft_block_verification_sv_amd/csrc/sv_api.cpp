@@ -176,6 +176,22 @@ bool shape_ok(int64_t V, int64_t ld_t, int64_t ld_d) {
 
 namespace {
 
+// Epochs of the launches that fold split rows: distinct for 2^32 launches in the process, never
+// 0, and spread over all 32 bits by an invertible mix, so that a flag word left in the
+// workspace by other use (small integers, floats) matches the epoch of a launch only by chance.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  while (true) {
+    uint32_t x = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    if (x != 0) return x;
+  }
+}
+
 // A workspace that lacks room for the lane records of split rows but holds everything else
 // (one sized for a larger call, say) is used without them: the call then streams each row in
 // one workgroup.
@@ -189,15 +205,24 @@ bool fit_workspace(const void* workspace, size_t bytes, Dims& dm) {
 // The streaming pass over n_units rows (pairs): one launch, or for small launches the split
 // streaming launch and the finalize launch.
 hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace& ws, int64_t rec_slots,
-                       hipStream_t st, int k_whole) {
+                       hipStream_t st, int k_whole, bool* folded_out = nullptr) {
   const int P = rec_slots > 0 ? sv::row_split(ra.n_units, ra.n_slices) : 1;
-  if (P < 2 || ra.n_units * P > rec_slots) {
+  const bool split = P >= 2 && ra.n_units * P <= rec_slots;
+  ra.folded = split && P >= sv::kFoldMinSplit ? 1 : 0;
+  if (folded_out) *folded_out = ra.folded != 0;
+  if (!split) {
     ra.phase = 0;
     ra.split = 1;
     return timed(k_whole, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
   }
   ra.split = P;
   ra.rec = ws.rec;
+  if (ra.n_units * P <= sv::kFoldGroups) {  // the last part of each row folds it, one launch
+    ra.phase = 3;
+    ra.flags = ws.flags;
+    ra.epoch = next_epoch();
+    return timed(K_ROWPAIR_PART, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
+  }
   ra.phase = 1;
   hipError_t e = timed(K_ROWPAIR_PART, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
   if (e != hipSuccess) return e;
@@ -354,7 +379,8 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.kmax1 = k_max + 1;
   ra.arrive = ws.arrive;
   if (rkl_out) ra.fix = ws.fix;  // heavy lanes of the reverse-KL rows are summed by the draw launch
-  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR) != hipSuccess) return SV_ERR_HIP;
+  bool folded = false;
+  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR, &folded) != hipSuccess) return SV_ERR_HIP;
 
   sv::SampleArgs sa{};
   sa.target = target_logits;
@@ -384,6 +410,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.rkl_out = rkl_out;
   sa.fix = ws.fix;
   sa.n_slices = n_slices;
+  sa.folded = folded ? 1 : 0;
   if (timed(K_DRAW, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

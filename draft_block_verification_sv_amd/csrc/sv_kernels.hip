@@ -529,14 +529,11 @@ __device__ __forceinline__ double fix_double(uint32_t w, int i) {
   return __hiloint2double(fix_word(w, i + 1), fix_word(w, i));
 }
 
-template <int DT, bool VEC>
-__device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, int64_t t,
-                                               uint32_t rec, int lane) {
-  const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
-  if (n <= 0) return;
-  constexpr int es = DT == 0 ? 2 : 4;
-  const void* prow = static_cast<const char*>(a.target) + t * a.ld_t * es;
-  const void* qrow = static_cast<const char*>(a.draft) + d * a.ld_d * es;
+// R of draft row d from its record (n heavy lanes) and the heavy lanes' new sums, sums(j) for
+// heavy lane j; lane 0 of the wave stores it.
+template <class Sums>
+__device__ __forceinline__ void finish_rkl_from(const SampleArgs& a, int64_t d, uint32_t rec, int n,
+                                                int lane, Sums&& sums) {
   const float Kp = __int_as_float(fix_word(rec, offsetof(RklFix, kp_ref) / 4));
   const float Kq = __int_as_float(fix_word(rec, offsetof(RklFix, kq_ref) / 4));
   double Sp = fix_double(rec, offsetof(RklFix, sp_rest) / 4);
@@ -544,13 +541,10 @@ __device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, i
   double HW = 0.0, HS = 0.0;
   for (int j = 0; j < n; ++j) {
     const int h0 = offsetof(RklFix, h) / 4 + j * 4;
-    const int src = fix_word(rec, h0);
     const bool direct = fix_word(rec, h0 + 1) != 0;
     const float hkp = __int_as_float(fix_word(rec, h0 + 2));
     const float hkq = __int_as_float(fix_word(rec, h0 + 3));
-    const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, a.V, static_cast<int>(a.n_slices), src,
-                                                lane, static_cast<double>(hkp),
-                                                static_cast<double>(hkq));
+    const LaneSums e = sums(j);
     const double sp = e.sp, sq = e.sq, w = e.w;
     if (sp > 0.0) Sp += ldexp(sp, static_cast<int>(hkp - Kp));
     if (sq > 0.0) {
@@ -573,6 +567,36 @@ __device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, i
                    kLn2 * exp2_d(static_cast<double>(Kq) - LZq) *
                        (static_cast<double>(kL2E) * HW + (LZp - LZq) * HS);
   if (lane == 0) a.rkl_out[d] = static_cast<float>(R);
+}
+
+template <int DT>
+__device__ __forceinline__ const void* logits_row(const void* base, int64_t r, int64_t ld) {
+  return static_cast<const char*>(base) + r * ld * (DT == 0 ? 2 : 4);
+}
+
+// The row finished by one wave: each heavy lane's blocks summed one after the other.
+template <int DT, bool VEC>
+__device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, int64_t t,
+                                               uint32_t rec, int lane) {
+  const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
+  if (n <= 0) return;
+  const void* prow = logits_row<DT>(a.target, t, a.ld_t);
+  const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
+  finish_rkl_from(a, d, rec, n, lane, [&](int j) {
+    const int h0 = offsetof(RklFix, h) / 4 + j * 4;
+    const int src = fix_word(rec, h0);
+    const double hkp = static_cast<double>(__int_as_float(fix_word(rec, h0 + 2)));
+    const double hkq = static_cast<double>(__int_as_float(fix_word(rec, h0 + 3)));
+    LaneSums r{0.0, 0.0, 0.0};
+    for (int q = 0; q < lane_blocks(src); ++q) {
+      const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, a.V, static_cast<int>(a.n_slices), src, q,
+                                                  lane, hkp, hkq);
+      r.sp += e.sp;
+      r.sq += e.sq;
+      r.w += e.w;
+    }
+    return r;
+  });
 }
 
 // The rows of request b (draft rows off - b + i, target rows off + i, i < k_b) left to this
@@ -599,12 +623,74 @@ __device__ __forceinline__ void finish_rkl_rows(const SampleArgs& a, int64_t b, 
   }
 }
 
+// After a split streaming pass the heavy lanes are folded ones, four times as long, and a row
+// is taken by all four waves of a workgroup, wave w summing block w of every heavy lane
+// (lane_blocks), the blocks' sums meeting in s_part (the draw's chunk masses, no longer needed)
+// and wave 0 adding them up in block order, as one wave would.  The rows go to the workgroups
+// that do not pick, by their draw ticket (ticket t: rows t, t + mass_blocks - 1, ...), so that
+// the pick waits for none of them; a request drawn without tickets (greedy, invalid) spreads
+// them over every workgroup (rows g, g + mass_blocks, ...), and a request with one workgroup
+// finishes them there after its pick.
+template <int DT, bool VEC>
+__device__ __forceinline__ void finish_rkl_rows_folded(const SampleArgs& a, int64_t b, int g,
+                                                       int64_t off, int kb, int wave, int lane,
+                                                       const int* s_ticket, double* s_part) {
+  static_assert(kMassWaves == kRowWaves && kFixLanes * kMassWaves * 3 <= kMaxChunks, "block sums fit s_part");
+  if (!a.rkl_out || !a.fix) return;
+  __syncthreads();  // every wave is done with the draw and with the chunk masses
+  const int ticket = *s_ticket;
+  int first = g, step = a.mass_blocks;
+  if (ticket >= 0 && a.mass_blocks > 1) {
+    if (ticket == a.mass_blocks - 1) return;  // the picking workgroup
+    first = ticket;
+    step = a.mass_blocks - 1;
+  }
+  for (int i = first; i < kb; i += step) {
+    const int64_t d = off - b + i;
+    const uint32_t rec = load_fix_words(a, d, true, lane);
+    const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
+    if (n <= 0) continue;
+    const void* prow = logits_row<DT>(a.target, off + i, a.ld_t);
+    const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
+    for (int j = 0; j < n; ++j) {
+      const int h0 = offsetof(RklFix, h) / 4 + j * 4;
+      const int src = fix_word(rec, h0);
+      if (wave >= lane_blocks(src)) continue;
+      const LaneSums e = exact_lane_sums<DT, VEC>(
+          prow, qrow, a.V, static_cast<int>(a.n_slices), src, wave, lane,
+          static_cast<double>(__int_as_float(fix_word(rec, h0 + 2))),
+          static_cast<double>(__int_as_float(fix_word(rec, h0 + 3))));
+      if (lane == 0) {
+        double* o = s_part + (j * kMassWaves + wave) * 3;
+        o[0] = e.sp;
+        o[1] = e.sq;
+        o[2] = e.w;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      finish_rkl_from(a, d, rec, n, lane, [&](int j) {
+        const int src = fix_word(rec, offsetof(RklFix, h) / 4 + j * 4);
+        LaneSums r{0.0, 0.0, 0.0};
+        for (int q = 0; q < lane_blocks(src); ++q) {
+          const double* o = s_part + (j * kMassWaves + q) * 3;
+          r.sp += o[0];
+          r.sq += o[1];
+          r.w += o[2];
+        }
+        return r;
+      });
+    }
+    __syncthreads();  // wave 0 has read the sums before the next row's are written
+  }
+}
+
 // One request's part of sv_draw for workgroup g (see the kernel below); returns once the
 // calling wave has nothing more to do for the draw.
 template <int DT, bool VEC>
 __device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int g, int tid, int lane,
                                              int wave, int my_tok, float my_u, const ReqState& rq,
-                                             double* s_pm, int* s_last) {
+                                             double* s_pm, int* s_ticket) {
   const int kb = rq.kb;
   const int64_t off = rq.off;
   if (rq.flags & kReqInvalid) {
@@ -651,11 +737,9 @@ __device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int
   // (An agent-scope fence here would write back and invalidate the XCD's whole L2 per wave.)
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  if (tid == 0)
-    *s_last = (__hip_atomic_fetch_add(a.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              a.mass_blocks - 1) ? 1 : 0;
+  if (tid == 0) *s_ticket = __hip_atomic_fetch_add(a.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (!*s_last) return;
+  if (*s_ticket != a.mass_blocks - 1) return;
 
   // ---- 1. chunk level (every wave computes the same total, so they agree on the fallback).
   // The masses are read back once; wave 0, which draws, keeps its lanes' masses in s_pm.
@@ -795,7 +879,7 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void sv_draw_kernel(SampleArgs a) {
   __shared__ double s_pm[kMaxChunks];  // the picking wave's chunk masses (p_T's after a fallback)
-  __shared__ int s_last;
+  __shared__ int s_ticket;  // the workgroup's draw ticket (-1: none taken)
   const int64_t b = blockIdx.x / a.mass_blocks;
   const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -814,11 +898,16 @@ void sv_draw_kernel(SampleArgs a) {
     return;
   }
   // the record of this wave's first reverse-KL row left to this launch, read while it draws
-  const int i_fix = first_fix_row(a, g, rq.kb, wave);
+  const int i_fix = a.folded ? -1 : first_fix_row(a, g, rq.kb, wave);
   const uint32_t fix_rec = load_fix_words(a, rq.off - b + (i_fix >= 0 ? i_fix : 0), i_fix >= 0, lane);
-  draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_last);
-  // each wave, once its part of the draw is done: the reverse-KL rows left to this launch
-  finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
+  if (tid == 0) s_ticket = -1;
+  draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_ticket);
+  // each wave, once its part of the draw is done (after a split streaming pass, the workgroup
+  // once every wave is): the reverse-KL rows left to this launch
+  if (a.folded)
+    finish_rkl_rows_folded<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, &s_ticket, s_pm);
+  else
+    finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
 }
 
 // =========================================================================== branch lookup

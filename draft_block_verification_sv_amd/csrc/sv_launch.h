@@ -58,7 +58,13 @@ struct RowPairArgs {
   // finalizes it.
   int32_t phase;
   int32_t split;
-  void* rec;  // [n_units * split * kRowThreads] lane records (phases 1 and 2)
+  void* rec;  // [n_units * split * rec_lanes(folded)] lane records (phases 1, 2 and 3)
+  int32_t folded;  // parts fold their four waves: kFoldLanes records a part, else kRowThreads
+  // Phase 3 streams part `blockIdx % split` of row (pair) `blockIdx / split` like phase 1; the
+  // part that arrives last (arrival flags set to the launch's nonzero epoch) folds the row's
+  // records and finalizes it, in the same launch.
+  uint32_t* flags;  // [n_units * 16]
+  uint32_t epoch;
   // verification with the reverse-KL, nullable: rows whose heavy lanes the draw launch sums
   RklFix* fix;  // [n_d]
 };
@@ -92,6 +98,7 @@ struct SampleArgs {
   float* rkl_out;
   const RklFix* fix;
   int64_t n_slices;  // the streaming pass's slices per row (lane geometry of the records)
+  int32_t folded;    // the streaming pass split rows: heavy lanes are folded ones (four blocks)
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);

@@ -39,7 +39,8 @@ constexpr int kMaxChunks = 1024;
 inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 
 // Small launches split each row (pair) over several streaming workgroups, which store their
-// lane records (at most kLaneRecBytes each) for a finalize launch.  Only launches of at most
+// lane records (at most kLaneRecBytes each) for the finalize: one per thread, or when a row has
+// at least kFoldMinSplit parts, kFoldLanes, the part's four waves folded lane by lane.  Only launches of at most
 // kSplitMaxUnits rows split (with more, one workgroup per row already covers most of the chip
 // and the finalize launch costs more than it saves); they aim at about kSplitTarget
 // streaming workgroups, with at most 16 parts per row, at least two slices per wave and at
@@ -48,6 +49,13 @@ constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMaxUnits = 128;
 constexpr int64_t kSplitSlots = 1024;
 constexpr size_t kLaneRecBytes = 72;
+constexpr int kFoldLanes = 64;
+constexpr int kFoldMinSplit = 9;
+constexpr int rec_lanes(bool folded) { return folded ? kFoldLanes : kRowThreads; }
+// Split launches of at most kFoldGroups streaming workgroups (about one per CU) fold their
+// records in the same launch (the part of a row that arrives last); larger ones in a finalize
+// launch.
+constexpr int64_t kFoldGroups = 256;
 inline int row_split(int64_t n_units, int64_t n_slices) {
   if (n_units < 1 || n_units > kSplitMaxUnits) return 1;
   int64_t P = (kSplitTarget + n_units - 1) / n_units;
@@ -140,6 +148,7 @@ struct Workspace {
   RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
   float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
   RklFix* fix;         // [n_d] verification: heavy lanes left to the draw launch per draft row
+  uint32_t* flags;     // [n_units * 16] arrival flags of rows split in a launch that folds them
 };
 
 struct Dims {
@@ -170,6 +179,7 @@ inline size_t carve(const Dims& d, Workspace* ws, char* base) {
   w.stats = reinterpret_cast<RowStats*>(take(d.n_grad * sizeof(RowStats)));
   w.coef = reinterpret_cast<float*>(take(d.n_grad * 2 * sizeof(float)));
   w.fix = reinterpret_cast<RklFix*>(take(d.n_d * sizeof(RklFix)));
+  w.flags = reinterpret_cast<uint32_t*>(take(d.rec_slots > 0 ? d.n_units * 16 * sizeof(uint32_t) : 0));
   if (ws) *ws = w;
   return off;
 }

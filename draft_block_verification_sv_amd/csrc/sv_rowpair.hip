@@ -22,8 +22,12 @@
 //   the acceptance test u < min(1, p_T(x)/q_T(x)) (paper, Section 2.1), or for T = 0
 //     the argmax match (DFlash notes, Section 5.2, worked example #4);
 //   the offsets the sampler needs to rebuild p_T and q_T of this row.
-// Launches of few rows split each row over several workgroups (phase 1), which hand their
-// lane records to a finalize launch (phase 2).
+// Launches of few rows split each row over several workgroups, which hand their lane records
+// to a finalize launch (phases 1 and 2), or, in launches of about one workgroup per CU, to the
+// part of the row that arrives last (phase 3), which folds them and finishes the row.  Rows
+// split into many parts fold each part's four waves lane by lane first, into 64 lane records
+// (lane l: the columns of thread l of every wave, in every slice), and are finished from those
+// 64 lanes.
 //
 // Request layout: for batches up to kInlinePlanMaxB requests every workgroup scans k
 // itself (no separate plan launch); larger batches read per-row descriptors.
@@ -52,6 +56,7 @@ __device__ __forceinline__ int64_t block_index() {
 }
 
 constexpr uint32_t kNaNBits = 0x7fc00000u;
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0): every load and store of the wave done
 // The bounds-checked loads of the streaming loop stream (nontemporal) like the plain ones.
 constexpr int kBufAux = 2;
 
@@ -242,6 +247,83 @@ __device__ __forceinline__ LaneRec lane_record(const LaneAcc& A) {
   R.xmax = A.xmax;
   return R;
 }
+
+// Records of split rows, one per thread of a part, or when the launch folds (a.folded) one per
+// thread of wave 0, into which the part folds its four waves lane by lane (thread l of every
+// wave reads the same column offsets of its slices, so folded lane l of a split row covers
+// columns l 8 .. l 8 + 7 of each 512-column group of every slice).  Laid out word-major: word i
+// of lane l of a part at words[i * lanes + l], so that each store and load of a wave covers
+// 512 contiguous bytes.  COHERENT (phase 3, whose records are read back within the launch):
+// written and read as 64-bit words with device-scope atomics, which go to and come from the
+// coherence point shared by every XCD instead of this XCD's L2.
+static_assert(sizeof(LaneRec) % 8 == 0 && alignof(LaneRec) == 8, "records move as 64-bit words");
+static_assert(sizeof(LaneRec) <= kLaneRecBytes && kFoldLanes == 64, "one folded record per thread of a wave");
+constexpr int kRecWords = static_cast<int>(sizeof(LaneRec) / 8);
+constexpr int kFoldMaxParts = 16;  // parts a split row may have (row_split gives at most 16)
+constexpr int kFoldRecs = 8;       // records one thread of the finalize folds, at most
+static_assert(kFoldMaxParts / kRowWaves <= kFoldRecs && kFoldMinSplit - 1 <= kFoldRecs, "finalize folds");
+template <bool COHERENT>
+__device__ __forceinline__ void store_record(uint64_t* part_words, int l, int lanes, const LaneRec& r) {
+  uint64_t w[kRecWords];
+  __builtin_memcpy(w, &r, sizeof(LaneRec));
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) {
+    if constexpr (COHERENT)
+      __hip_atomic_store(part_words + i * lanes + l, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      part_words[i * lanes + l] = w[i];
+  }
+}
+template <bool COHERENT>
+__device__ __forceinline__ LaneRec load_record(const uint64_t* part_words, int l, int lanes) {
+  uint64_t w[kRecWords];
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) {
+    if constexpr (COHERENT)
+      w[i] = __hip_atomic_load(const_cast<uint64_t*>(part_words + i * lanes + l), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    else
+      w[i] = part_words[i * lanes + l];
+  }
+  LaneRec r;
+  __builtin_memcpy(&r, w, sizeof(LaneRec));
+  return r;
+}
+// Part p's records of row (pair) unit.
+__device__ __forceinline__ uint64_t* part_records(const RowPairArgs& a, int64_t unit, int p) {
+  return static_cast<uint64_t*>(a.rec) + (unit * a.split + p) * kRecWords * rec_lanes(a.folded);
+}
+
+// The finalize of a split row, the records folded in part order with all loads issued at once
+// (load, on entry where nothing else is needed first).  Unfolded records: thread t folds its
+// lane's records of every part.  Folded: thread (q, l) folds lane l of a quarter of the parts
+// (parts q per .. q per + per - 1, per = ceil(split / 4)), then wave 0 folds the quarters in
+// order and lacc holds the row's 64 lanes, the other 192 empty.
+template <bool COHERENT>
+struct PartFold {
+  LaneRec R[kFoldRecs];
+  __device__ __forceinline__ void range(const RowPairArgs& a, int tid, int& p0, int& per) const {
+    per = a.folded ? (a.split + kRowWaves - 1) / kRowWaves : a.split;
+    p0 = a.folded ? (tid >> 6) * per : 0;
+  }
+  __device__ __forceinline__ void load(const RowPairArgs& a, int64_t unit, int tid) {
+    int p0, per;
+    range(a, tid, p0, per);
+    const int lanes = rec_lanes(a.folded), l = a.folded ? (tid & 63) : tid;
+#pragma unroll
+    for (int u = 0; u < kFoldRecs; ++u)
+      if (u < per && p0 + u < a.split) R[u] = load_record<COHERENT>(part_records(a, unit, p0 + u), l, lanes);
+  }
+  __device__ __forceinline__ void fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const;
+};
+
+// Arrival flags of a row's parts (phase 3): part p of a row sets word p of the row's
+// kFoldMaxParts flag words to the launch's epoch once its records are complete at the coherence
+// point, waits for that store to complete there, then reads every part's flag.  Of two parts,
+// the one that sets its flag later sees the other's, so the part that arrives last sees every
+// flag set (others may too, and then finish the row as well, with the same results).  A flag
+// word holding anything but the epoch (the row's flags of an earlier launch, which had its own
+// epoch, or whatever the memory held) counts as not arrived.
 
 __device__ __forceinline__ void lane_clear(LaneAcc& A) {
   A.kp = A.kq = A.ktp = A.ktq = 0.0f;
@@ -525,6 +607,27 @@ __device__ __forceinline__ void lane_merge(LaneAcc& A, const LaneRec& R) {
   }
 }
 
+template <bool COHERENT>
+__device__ __forceinline__ void PartFold<COHERENT>::fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const {
+  int p0, per;
+  range(a, tid, p0, per);
+  LaneAcc F;
+  lane_clear(F);
+#pragma unroll
+  for (int u = 0; u < kFoldRecs; ++u)
+    if (u < per && p0 + u < a.split) lane_merge(F, R[u]);
+  lacc[tid] = F;
+  if (!a.folded) return;
+  __syncthreads();
+  if (tid < kFoldLanes) {
+#pragma unroll
+    for (int q = 1; q < kRowWaves; ++q) lane_merge(F, lane_record(lacc[q * kFoldLanes + tid]));
+    lacc[tid] = F;
+  }
+  __syncthreads();  // wave 0 has read every quarter
+  if (tid >= kFoldLanes) lane_clear(lacc[tid]);
+}
+
 // ----------------------------------------------------------------------------- block helpers
 // Fixed-order reductions over the 256-thread workgroup: wave butterfly, then the four
 // wave results in order.  `red` holds kRowWaves doubles.
@@ -666,6 +769,7 @@ struct Scratch {
   int* failed;
   int* s_nfail;
   int* s_nheavy;  // a counter of its own: the heavy list is read while the next one starts
+  int* s_last;    // phase 3: this part found every part of the row arrived
   double* red_d;
   float* red_f;
   int* red_i;
@@ -755,25 +859,53 @@ __device__ __forceinline__ bool is_heavy(const HeavyParts& h, double thr) {
   return h.by_mass || h.err > thr;
 }
 
-// The n listed heavy lanes, one wave each, summed again; their records in lacc are replaced.
+// The n listed heavy lanes (sc.failed) summed again; their records in lacc are replaced.  Lane
+// t's columns are those of lane t + col_base as the re-reading helpers number lanes (col_base =
+// kRowThreads on split rows, whose lanes are the parts' folded ones).  A streaming lane is read
+// by one wave, the lanes spread over the waves; a folded lane by every wave, one block each,
+// whose sums meet in the direct arrays (block q of lane t at q kFoldLanes + t) and add up in
+// block order.
 template <int DT, bool VEC>
 __device__ __forceinline__ void exact_heavy_sums(const void* prow, const void* qrow, int V,
-                                                 int n_slices, LaneAcc* lacc, const int* list,
-                                                 int n) {
-  const int lane = thread_index() & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(thread_index() >> 6);
-  for (int f = wave; f < n; f += kRowWaves) {
-    const int src = list[f];
-    const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, V, n_slices, src, lane,
+                                                 int n_slices, LaneAcc* lacc, const Scratch& sc,
+                                                 int n, int col_base) {
+  const int tid = thread_index(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = lane_blocks(col_base);
+  for (int it = wave; it < n * nb; it += kRowWaves) {
+    const int f = it / nb, q = it - f * nb;
+    const int src = sc.failed[f];
+    const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, V, n_slices, src + col_base, q, lane,
                                                 static_cast<double>(lacc[src].kp),
                                                 static_cast<double>(lacc[src].kq));
     if (lane == 0) {
-      lacc[src].sp = e.sp;
-      lacc[src].sq = e.sq;
-      lacc[src].w = e.w;
+      if (nb == 1) {
+        lacc[src].sp = e.sp;
+        lacc[src].sq = e.sq;
+        lacc[src].w = e.w;
+      } else {
+        sc.direct[q * kFoldLanes + src] = e.sp;
+        sc.direct_x[q * kFoldLanes + src] = e.sq;
+        sc.direct_u0[q * kFoldLanes + src] = e.w;
+      }
     }
   }
   __syncthreads();
+  if (nb > 1) {
+    for (int f = tid; f < n; f += kRowThreads) {
+      const int src = sc.failed[f];
+      double sp = 0.0, sq = 0.0, w = 0.0;
+      for (int q = 0; q < nb; ++q) {
+        sp += sc.direct[q * kFoldLanes + src];
+        sq += sc.direct_x[q * kFoldLanes + src];
+        w += sc.direct_u0[q * kFoldLanes + src];
+      }
+      lacc[src].sp = sp;
+      lacc[src].sq = sq;
+      lacc[src].w = w;
+    }
+    __syncthreads();
+  }
 }
 
 // The row's clipped reverse-KL, lane by lane (lane_closed): closed form, or for a lane near the
@@ -785,11 +917,12 @@ __device__ __forceinline__ void exact_heavy_sums(const void* prow, const void* q
 // gradient (g_y = 1[t_y < delta] (ln q_y - ln p_y + 1)), whose closed form on a passing lane is
 // the lane's closed form plus Q.  With FIX instead, direct_x = sum over the unclipped terms and
 // direct_u0 = their q-mass, from which the draw launch moves the lane's sum to new normalisers.
+// Lane t's columns: as for exact_heavy_sums.
 template <int DT, bool VEC, bool SG, bool FIX>
 __device__ __forceinline__ LaneClosed lanes_clipped_rkl(const void* prow, const void* qrow, int V,
                                                        int n_slices, double LZp, double LZq,
                                                        float delta, const LaneAcc& A,
-                                                       const Scratch& sc) {
+                                                       const Scratch& sc, int col_base) {
   static_assert(!(SG && FIX), "one use of the extra per-lane sums at a time");
   const int tid = thread_index(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -798,10 +931,12 @@ __device__ __forceinline__ LaneClosed lanes_clipped_rkl(const void* prow, const 
   const int nfail = list_lanes(out.fail, sc.failed, sc.s_nfail);
   if (nfail > 0) {
     const double dd = static_cast<double>(delta);
-    for (int f = wave; f < nfail; f += kRowWaves) {
-      const int src = sc.failed[f];
+    const int nb = lane_blocks(col_base);  // blocks meet as in exact_heavy_sums
+    for (int it = wave; it < nfail * nb; it += kRowWaves) {
+      const int f = it / nb, q = it - f * nb;
+      const int src = sc.failed[f], slot = q * kFoldLanes + src;
       double part = 0.0, xpart = 0.0, u0 = 0.0;
-      for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src, lane, [&](float lp, float lq) {
+      for_lane_columns<DT, VEC>(prow, qrow, V, n_slices, src + col_base, q, lane, [&](float lp, float lq) {
         const double a = static_cast<double>(lq) * static_cast<double>(kL2E);
         const double q = static_cast<double>(fast_exp2(static_cast<float>(a - LZq)));
         const double term =
@@ -814,17 +949,32 @@ __device__ __forceinline__ LaneClosed lanes_clipped_rkl(const void* prow, const 
         }
       });
       part = wave_sum_d(part);
-      if (lane == 0) sc.direct[src] = part;
+      if (lane == 0) sc.direct[slot] = part;
       if constexpr (SG || FIX) {
         xpart = wave_sum_d(xpart);
-        if (lane == 0) sc.direct_x[src] = xpart;
+        if (lane == 0) sc.direct_x[slot] = xpart;
       }
       if constexpr (FIX) {
         u0 = wave_sum_d(u0);
-        if (lane == 0) sc.direct_u0[src] = u0;
+        if (lane == 0) sc.direct_u0[slot] = u0;
       }
     }
     __syncthreads();
+    if (nb > 1) {
+      for (int f = tid; f < nfail; f += kRowThreads) {
+        const int src = sc.failed[f];
+        double part = 0.0, xpart = 0.0, u0 = 0.0;
+        for (int q = 0; q < nb; ++q) {
+          part += sc.direct[q * kFoldLanes + src];
+          if constexpr (SG || FIX) xpart += sc.direct_x[q * kFoldLanes + src];
+          if constexpr (FIX) u0 += sc.direct_u0[q * kFoldLanes + src];
+        }
+        sc.direct[src] = part;
+        if constexpr (SG || FIX) sc.direct_x[src] = xpart;
+        if constexpr (FIX) sc.direct_u0[src] = u0;
+      }
+      __syncthreads();
+    }
   }
   return out;
 }
@@ -898,8 +1048,9 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   if constexpr (PHASE != 2) {  // stream the row (pair), or this workgroup's part of it
     LaneAcc L;
     lane_clear(L);
-    const int first = (PHASE == 1 ? ctx.part * kRowWaves : 0) + wave;
-    const int step = kRowWaves * (PHASE == 1 ? a.split : 1);
+    constexpr bool PART = PHASE == 1 || PHASE == 3;
+    const int first = (PART ? ctx.part * kRowWaves : 0) + wave;
+    const int step = kRowWaves * (PART ? a.split : 1);
     stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, first, step, lane, L);
     const float Mp = lane_max(L.mhp, L.mlp);
     correct_top(L.sp, Mp, kL2E, L.kp);
@@ -909,14 +1060,47 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       correct_top(L.sq, Mq, kL2E, L.kq);
       if constexpr (MODE == 2) correct_top(L.stq, Mq, ctx.beta, L.ktq);
     }
-    if constexpr (PHASE == 1) {  // a part: its lane records go to the workspace for the finalize
-      static_cast<LaneRec*>(a.rec)[(ctx.unit * a.split + ctx.part) * kRowThreads + tid] = lane_record(L);
-      return;
-    }
     lacc[tid] = L;  // the finalize reads the record back as it needs it
+    if constexpr (PART) {
+      // A part stores its lane records (folded: wave 0 folds the four waves' lanes first).
+      // Phase 1 leaves them to the finalize launch.  In phase 3 they go to the coherence point
+      // shared by every XCD; once every wave's are complete there wave 0 sets the part's
+      // arrival flag and reads the row's.  A part that finds every flag set reads the records
+      // back from the coherence point, folds them and finishes the row; the others are done.
+      uint64_t* mine = part_records(a, ctx.unit, ctx.part);
+      if (a.folded) {
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+          for (int q = 1; q < kRowWaves; ++q) lane_merge(L, lane_record(lacc[q * kFoldLanes + lane]));
+          store_record<PHASE == 3>(mine, lane, kFoldLanes, lane_record(L));
+        }
+      } else {
+        store_record<PHASE == 3>(mine, tid, kRowThreads, lane_record(L));
+      }
+      if constexpr (PHASE == 1) return;
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t* flags = a.flags + ctx.unit * kFoldMaxParts;
+        if (lane == 0) __hip_atomic_store(flags + ctx.part, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        const uint32_t e = lane < a.split
+                               ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : a.epoch;
+        const int all = __all(e == a.epoch);
+        if (lane == 0) *sc.s_last = all ? 1 : 0;
+      }
+      __syncthreads();
+      if (!*sc.s_last) return;
+      PartFold<true> pf;
+      pf.load(a, ctx.unit, tid);
+      pf.fold(a, tid, lacc);
+    }
   }
   // (the finalize launch folded the row's part records into lacc on entry)
   const LaneAcc& A = lacc[tid];
+  const int col_base = (PHASE != 0 && a.folded) ? kRowThreads : 0;  // how the lanes' columns are numbered
 
   // thread 0: the uniform's and the draft token's range checks
   auto input_flags = [&]() {
@@ -1000,7 +1184,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
           for (int j = 0; j < n_heavy; ++j)
             if (sc.failed[j] == tid) heavy_at = j;
       } else if (n_heavy > 0) {
-        exact_heavy_sums<DT, VEC>(prow, qrow, V, n_slices, lacc, sc.failed, n_heavy);
+        exact_heavy_sums<DT, VEC>(prow, qrow, V, n_slices, lacc, sc, n_heavy, col_base);
         const float k2[2] = {A.kp, A.kq};  // A reads the replaced sums back
         const double s2[2] = {A.sp, A.sq};
         double lz2[2];
@@ -1022,14 +1206,14 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   if (a.rkl_out && !rkl_done) {
     if (MODE == 1 && a.stats) {
       const LaneClosed L = lanes_clipped_rkl<DT, VEC, true, false>(prow, qrow, V, n_slices, LZ1p, LZ1q,
-                                                                   a.delta, A, sc);
+                                                                   a.delta, A, sc, col_base);
       double v[2] = {L.fail ? sc.direct[tid] : L.closed, L.fail ? sc.direct_x[tid] : L.closed + L.mass};
       block_reduce<2, 0u>(v, sc.red_v);
       Rsg = v[1];
       if (tid == 0) a.rkl_out[ctx.d] = static_cast<float>(v[0]);
     } else if (n_heavy == 0) {
       const LaneClosed L = lanes_clipped_rkl<DT, VEC, false, false>(prow, qrow, V, n_slices, LZ1p, LZ1q,
-                                                                    a.delta, A, sc);
+                                                                    a.delta, A, sc, col_base);
       const double R = block_sum_d(L.fail ? sc.direct[tid] : L.closed, red_d);
       if (tid == 0) {
         a.rkl_out[ctx.d] = static_cast<float>(R);
@@ -1040,7 +1224,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       // take the closed form (H) are summed apart; every other lane's part, its unclipped
       // terms and their q-mass let the launch move it to the exact normalisers.
       const LaneClosed L = lanes_clipped_rkl<DT, VEC, false, true>(prow, qrow, V, n_slices, LZ1p, LZ1q,
-                                                                   a.delta, A, sc);
+                                                                   a.delta, A, sc, col_base);
       const bool H = heavy && !L.fail;
       double v[kRowSums];
       v[0] = H ? 0.0 : (L.fail ? sc.direct[tid] : L.closed);
@@ -1053,7 +1237,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       RklFix* fx = a.fix + ctx.d;
       if (heavy_at >= 0) {
         RklFixLane h;
-        h.lane = tid;
+        h.lane = tid + col_base;
         h.direct = L.fail ? 1 : 0;
         h.kp = A.kp;
         h.kq = A.kq;
@@ -1229,38 +1413,6 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
   return s_req >= 0;  // false only when the layout is invalid, which the scan reports
 }
 
-// The finalize of a split row: the lane's records of every part, folded in part order, eight
-// in flight at a time (a batch past the last part re-reads it and skips it).  The first batch
-// is fetched on entry, before anything else, and folded once the row is resolved.
-struct PartBatch {
-  LaneRec R[8];
-  __device__ __forceinline__ void load(const RowPairArgs& a, int64_t unit, int tid, int j) {
-    const LaneRec* mine = static_cast<const LaneRec*>(a.rec) + unit * a.split * kRowThreads + tid;
-    const int last = a.split - 1;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) R[u] = mine[min(j + u, last) * kRowThreads];
-  }
-  __device__ __forceinline__ void fold(LaneAcc& L, int j, int last) const {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j + u <= last) lane_merge(L, R[u]);
-  }
-};
-
-__device__ __forceinline__ void merge_parts(const RowPairArgs& a, int64_t unit, int tid,
-                                            const PartBatch& first, LaneAcc* lacc) {
-  LaneAcc L;
-  lane_clear(L);
-  const int last = a.split - 1;
-  first.fold(L, 0, last);
-  for (int j = 8; j <= last; j += 8) {
-    PartBatch nb;
-    nb.load(a, unit, tid, j);
-    nb.fold(L, j, last);
-  }
-  lacc[tid] = L;
-}
-
 // PHASE 0: one workgroup streams and finishes a row (pair).  PHASE 1: workgroup blockIdx
 // streams part blockIdx % split of row (pair) blockIdx / split and stores its lane records.
 // PHASE 2: one workgroup per row (pair) folds the records and finishes it.
@@ -1272,23 +1424,23 @@ void sv_rowpair_kernel(RowPairArgs a) {
   __shared__ double direct_x[kRowThreads];
   __shared__ double direct_u0[kRowThreads];
   __shared__ int failed[kRowThreads];
-  __shared__ int s_nfail, s_nheavy;
+  __shared__ int s_nfail, s_nheavy, s_last;
   __shared__ double red_d[kRowWaves];
   __shared__ float red_f[kRowWaves];
   __shared__ int red_i[kRowWaves];
   __shared__ double red_v[kRowWaves * kRowSums];
   __shared__ int s_req, s_off, s_t, s_void;
   __shared__ float s_T;
-  const Scratch sc{lacc, direct, direct_x, direct_u0, failed, &s_nfail, &s_nheavy, red_d, red_f, red_i, red_v};
+  const Scratch sc{lacc, direct, direct_x, direct_u0, failed, &s_nfail, &s_nheavy, &s_last, red_d, red_f, red_i, red_v};
   const int tid = thread_index();
   const int64_t blk = block_index();
-  const int64_t unit = PHASE == 1 ? blk / a.split : blk;
-  PartBatch first;  // phase 2: the first records, which depend on nothing else
-  if constexpr (PHASE == 2) first.load(a, unit, tid, 0);
+  const int64_t unit = (PHASE == 1 || PHASE == 3) ? blk / a.split : blk;
+  PartFold<false> first;  // phase 2: the records, which depend on nothing else
+  if constexpr (PHASE == 2) first.load(a, unit, tid);
 
   RowCtx ctx;
   ctx.unit = unit;
-  ctx.part = PHASE == 1 ? static_cast<int>(blk - unit * a.split) : 0;
+  ctx.part = (PHASE == 1 || PHASE == 3) ? static_cast<int>(blk - unit * a.split) : 0;
   if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
     ctx.d = unit;
     ctx.t = a.p_row_index ? a.p_row_index[unit] : unit;
@@ -1306,7 +1458,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
       return;
     }
     if (tid == 0) a.row_flags[unit] = 0;
-    if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
+    if constexpr (PHASE == 2) first.fold(a, tid, lacc);
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
       rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, -1);
@@ -1346,7 +1498,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
     if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
   }
   ctx.row_flags = flags;  // thread 0 adds the token and uniform bits after the stream
-  if constexpr (PHASE == 2) merge_parts(a, unit, tid, first, lacc);
+  if constexpr (PHASE == 2) first.fold(a, tid, lacc);
   if (ctx.d >= 0) {
     if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, sc, xr);
     if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, xr);
@@ -1526,21 +1678,24 @@ hipError_t launch_row_argmax(int dtype, bool vec, const ArgmaxArgs& a, hipStream
 
 // ----------------------------------------------------------------------------- launch
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.n_units * (a.phase == 1 ? a.split : 1)));
+  const dim3 grid(static_cast<unsigned>(a.n_units * ((a.phase == 1 || a.phase == 3) ? a.split : 1)));
   if (a.n_units == 0) return hipSuccess;
-  if (a.phase < 0 || a.phase > 2 || (a.phase != 0 && (a.split < 2 || !a.rec))) return hipErrorInvalidValue;
+  if (a.phase < 0 || a.phase > 3 || (a.phase != 0 && (a.split < 2 || !a.rec)) ||
+      (a.phase == 3 && (!a.flags || a.epoch == 0 || a.split > kFoldMaxParts)))
+    return hipErrorInvalidValue;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, a); };
-  auto by_phase = [&](auto k0, auto k1, auto k2) {
+  auto by_phase = [&](auto k0, auto k1, auto k2, auto k3) {
     if (a.phase == 0) go(k0);
     else if (a.phase == 1) go(k1);
-    else go(k2);
+    else if (a.phase == 2) go(k2);
+    else go(k3);
   };
   if (dtype == 0) {
-    if (vec) by_phase(sv_rowpair_kernel<0, true, 0>, sv_rowpair_kernel<0, true, 1>, sv_rowpair_kernel<0, true, 2>);
-    else by_phase(sv_rowpair_kernel<0, false, 0>, sv_rowpair_kernel<0, false, 1>, sv_rowpair_kernel<0, false, 2>);
+    if (vec) by_phase(sv_rowpair_kernel<0, true, 0>, sv_rowpair_kernel<0, true, 1>, sv_rowpair_kernel<0, true, 2>, sv_rowpair_kernel<0, true, 3>);
+    else by_phase(sv_rowpair_kernel<0, false, 0>, sv_rowpair_kernel<0, false, 1>, sv_rowpair_kernel<0, false, 2>, sv_rowpair_kernel<0, false, 3>);
   } else {
-    if (vec) by_phase(sv_rowpair_kernel<1, true, 0>, sv_rowpair_kernel<1, true, 1>, sv_rowpair_kernel<1, true, 2>);
-    else by_phase(sv_rowpair_kernel<1, false, 0>, sv_rowpair_kernel<1, false, 1>, sv_rowpair_kernel<1, false, 2>);
+    if (vec) by_phase(sv_rowpair_kernel<1, true, 0>, sv_rowpair_kernel<1, true, 1>, sv_rowpair_kernel<1, true, 2>, sv_rowpair_kernel<1, true, 3>);
+    else by_phase(sv_rowpair_kernel<1, false, 0>, sv_rowpair_kernel<1, false, 1>, sv_rowpair_kernel<1, false, 2>, sv_rowpair_kernel<1, false, 3>);
   }
   return hipGetLastError();
 }

@@ -104,10 +104,9 @@ def test_small_delta_rereads_clipped_slices(delta):
 # 12 such tokens (more heavy lanes than a row's record for the draw launch holds: summed in the
 # finalize), 6 and 2 (summed by the draw launch) and 1 token holding most of the mass.  4
 # requests split their rows over several workgroups; 40 do not.
-def _heavy_lane_workload(dtype, B, seed):
+def _heavy_lane_workload(dtype, B, seed, V=20000):
     from synth import bf16_bits_from_f64
 
-    V = 20000
     pattern = [12, 6, 2, 1]
     k = [3, 2, 3, 2] * (B // 4)
     w = make_workload(B=B, k=k, V=V, dtype=dtype, s=1.0, sigma=0.5, seed=seed)
@@ -141,6 +140,20 @@ def test_heavy_lanes(dtype, B, delta):
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w, delta=delta))
     _report(f"heavy lanes {dtype} B={B} delta={delta}", s)
+
+
+# The same rows long enough (137 slices) that a small launch splits them into 16 parts, which
+# fold their four waves into 64 lanes: the heavy tokens' lanes stay distinct, now holding four
+# times the columns, re-read in four blocks (finalize: 12 heavy lanes; draw launch: 6, 2, 1).
+# B = 4 (14 rows): one launch; B = 8 (28 rows): parts, then a finalize launch.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B", [4, 8])
+def test_heavy_lanes_folded(dtype, B):
+    w = _heavy_lane_workload(dtype, B, (31, B, dtype == "f32"), V=140001)
+    got = run_gpu(w, delta=1.0)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w, delta=1.0))
+    _report(f"heavy lanes folded {dtype} B={B}", s)
 
 
 @pytest.mark.parametrize("B", [1, 65])  # one request: split rows; 65 (130 rows): one WG per row
@@ -432,6 +445,29 @@ def test_split_rows_parity(dtype, ld):
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w))
     _report(f"split {dtype} ld={ld}", s)
+    assert s["exact"] >= w.B - 1
+
+
+# The four ways a small launch splits its rows, by rows (n) and parts per row (P): 16 parts
+# fold each part's four waves into 64 lanes, fewer keep 256; a launch of at most 256
+# workgroups finishes its rows itself (the last part to arrive), a larger one in a finalize
+# launch.  V = 70001 (69 slices, ragged): P = 8; V = 140001 (137 slices): P = 16.
+@pytest.mark.parametrize("case", [
+    ("folded, one launch", 140001, [6, 5], "bf16"),                 # n = 13, P = 16: 208 WGs
+    ("folded, finalize launch", 140001, [9, 7, 8], "bf16"),         # n = 27, P = 16: 432 WGs
+    ("folded, finalize launch f32", 140004, [4, 9, 2, 6], "f32"),   # n = 25, P = 16
+    ("unfolded, finalize launch", 70001, [7, 7, 7, 7, 7], "bf16"),  # n = 40, P = 8: 320 WGs
+])
+def test_split_regimes(case):
+    name, V, k, dtype = case
+    B = len(k)
+    w = make_workload(B=B, k=k, V=V, dtype=dtype, s=3.0, sigma=[0.5, 1.0, 2.0, 0.8, 1.4][:B],
+                      temperature=[1.0, 0.0, 0.7, 1.3, 1.0][:B], delta=0.05, outlier_frac=0.05,
+                      seed=(15, V, B))
+    got = run_gpu(w)
+    assert got["device_status"][0] == 0
+    s = compare(w, got, run_oracle(w))
+    _report(f"split {name}", s)
     assert s["exact"] >= w.B - 1
 
 
