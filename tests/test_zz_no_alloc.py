@@ -53,3 +53,33 @@ def test_noalloc_matches_workspace_entry_point():
         got = {k_: v.cpu().numpy() for k_, v in out.items()}
         s = compare(w, got, run_oracle(w))
         assert s["exact"] + len(s["flips"]) == w.B
+
+
+def test_noalloc_split_rows_in_one_launch():
+    # Rows split into 16 parts that fold their waves: a single request of 16 rows finishes in
+    # the streaming launch (arrival flags in the scratch), 19 rows in a finalize launch.  The
+    # fixed scratch holds their records, so both entry points split alike and agree bit for bit.
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_block_verification_sv_amd as pkg
+
+    one = make_workload(B=1, k=[15], V=140001, dtype="bf16", s=4.0, sigma=[1.0], delta=1.0,
+                        seed=(33,))
+    two = make_workload(B=2, k=[9, 8], V=140001, dtype="bf16", s=3.0, sigma=[0.5, 1.5],
+                        temperature=[1.0, 0.7], delta=0.05, seed=(34,))
+    for i, w in enumerate((one, two, one)):
+        print(f"[noalloc split] call {i}: B={w.B} V={w.V}", flush=True)
+        d = to_device(w)
+        ref = pkg.verify_block(d["target"], d["draft"], d["k"], d["draft_tokens"], d["uniforms"],
+                               d["temperature"], w.delta, k_max=w.k_max)
+        out = _outputs(w, torch.device("cuda:0"))
+        pkg.verify_block_noalloc(d["target"], d["draft"], d["k"], d["draft_tokens"],
+                                 d["uniforms"], d["temperature"], w.delta, out, k_max=w.k_max)
+        torch.cuda.synchronize()
+        for key in ("accept_len", "out_tokens", "rkl", "p_at_draft", "q_at_draft",
+                    "device_status"):
+            np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key].cpu().numpy(), key)
+        assert int(out["device_status"].item()) == 0
+    got = {k_: v.cpu().numpy() for k_, v in out.items()}
+    s = compare(one, got, run_oracle(one))
+    assert s["exact"] + len(s["flips"]) == one.B
