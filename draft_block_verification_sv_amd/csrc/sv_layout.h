@@ -40,11 +40,11 @@ inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 
 // Small launches split each row (pair) over several streaming workgroups, which store their
 // lane records (at most kLaneRecBytes each) for the finalize: one per thread, or when a row has
-// at least kFoldMinSplit parts, kFoldLanes, the part's four waves folded lane by lane.  Only launches of at most
-// kSplitMaxUnits rows split (with more, one workgroup per row already covers most of the chip
-// and the finalize launch costs more than it saves); they aim at about kSplitTarget
-// streaming workgroups, with at most 16 parts per row, at least two slices per wave and at
-// most kSplitSlots record sets in all.
+// at least kFoldMinSplit parts, kFoldLanes, the part's four waves folded lane by lane.  Only
+// launches of at most kSplitMaxUnits rows split (with more, one workgroup per row already
+// covers most of the chip and the records and their fold cost more than they save); they aim
+// at about kSplitTarget streaming workgroups, with at most 16 parts per row, at least two
+// slices per wave and at most kSplitSlots record sets in all.
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMaxUnits = 128;
 constexpr int64_t kSplitSlots = 1024;

@@ -11,7 +11,8 @@
 //   S_T = sum 2^(l beta - k_T)               rows with T_b not in {0, 1};
 //   W   = sum 2^(l_q L2E - k_q) (l_q - l_p)  and D = max (l_q - l_p)   (row pairs);
 //   the running maxima, and for greedy rows the first argmax of the target row.
-// The workgroup then finishes the row from the 256 lane records, in fixed order:
+// The workgroup then finishes the row from the lane records (256, or 64 folded ones for rows
+// split into many parts, below), in fixed order:
 //   log2 normalisers LZ = K + log2(sum_l S_l 2^(k_l - K)), fp64;
 //   the clipped reverse-KL R = sum_y min(delta, q log(q/p)) at T = 1 (AdaFlash paper,
 //     Section 3.1 equation; Appendix B.1 for the temperature): per lane, with c2 = LZp - LZq,
@@ -1098,7 +1099,8 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       pf.fold(a, tid, lacc);
     }
   }
-  // (the finalize launch folded the row's part records into lacc on entry)
+  // (a split row's records were folded into lacc: by the finalize launch on entry, or above by
+  // the part that arrived last)
   const LaneAcc& A = lacc[tid];
   const int col_base = (PHASE != 0 && a.folded) ? kRowThreads : 0;  // how the lanes' columns are numbered
 
