@@ -169,3 +169,22 @@ def test_many_clipped_lanes(dtype, ld):
     assert int(got["device_status"].item()) == 0
     worst = _compare(w, got, 0.004, 0.8, idx, range(w.n_draft_rows))
     print(f"[grad] many clipped lanes {dtype} ld={ld}: max rel err {worst:.2e}", flush=True)
+
+
+def test_many_clipped_folded_lanes():
+    # rows of 137 slices split into 16 parts folded into 64 lanes (9 rows: finished by the last
+    # part in the streaming launch); the small delta fails the bound on most folded lanes, whose
+    # columns are then re-read in four blocks, one per wave
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=3, k=[2, 4, 3], V=140001, dtype="bf16", s=3.0, sigma=[0.5, 1.5, 1.0],
+                      outlier_frac=0.05, seed=(35,))
+    d = to_device(w)
+    idx = _pairing(w)
+    got = pkg.opd_loss_grad(d["target"], d["draft"], torch.from_numpy(w.k).cuda(), delta=0.004,
+                            alpha=0.8, p_row_index=torch.from_numpy(idx).cuda(),
+                            grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(got["device_status"].item()) == 0
+    worst = _compare(w, got, 0.004, 0.8, idx, range(w.n_draft_rows))
+    print(f"[grad] many clipped folded lanes: max rel err {worst:.2e}", flush=True)

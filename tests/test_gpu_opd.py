@@ -204,3 +204,26 @@ def test_split_rows(dtype):
         assert int(got["device_status"].item()) == 0
         worst = _check(w, got, delta, alpha, idx)
         print(f"[opd] split rows {dtype} delta={delta}: max hard-CE rel err {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,k", [("bf16", [4, 1, 5]), ("f32", [4, 1, 5]), ("bf16", [9, 8, 7])])
+def test_folded_split_rows(dtype, k):
+    # 137 slices a row: split into 16 parts that fold their waves into 64 lanes.  10 rows: the
+    # part arriving last finishes each row in the streaming launch; 24 rows: a finalize launch.
+    # Without a draw launch every heavy or clipped lane is summed again in the finalize, in
+    # four blocks.
+    import draft_block_verification_sv_amd as pkg
+
+    w = make_workload(B=3, k=k, V=140001, dtype=dtype, s=3.0, sigma=[0.3, 1.2, 2.0],
+                      outlier_frac=0.05, seed=(26, dtype == "f32", len(k)))
+    d = to_device(w)
+    idx = _pairing(w)
+    kt = torch.from_numpy(w.k.astype(np.int32)).cuda()
+    for delta, alpha in ((1.0, 0.8), (0.01, 0.5)):
+        got = pkg.opd_loss(d["target"], d["draft"], kt, delta=delta, alpha=alpha,
+                           p_row_index=torch.from_numpy(idx).cuda())
+        torch.cuda.synchronize()
+        assert int(got["device_status"].item()) == 0
+        worst = _check(w, got, delta, alpha, idx)
+        print(f"[opd] folded split rows {dtype} k={k} delta={delta}: max hard-CE rel err {worst:.2e}",
+              flush=True)
