@@ -18,15 +18,15 @@ namespace {
 using sv::Dims;
 using sv::Workspace;
 
-constexpr int kNumKernels = 23;
+constexpr int kNumKernels = 22;
 const char* const kKernelNames[kNumKernels] = {
     "sv_plan",        "sv_rowpair",      "sv_draw",
     "sv_rkl_rowpair", "sv_rkl_status",   "sv_opd_rowpair", "sv_opd_status",
     "sv_opd_reduce",  "sv_grad_rowpair", "sv_grad_reduce", "sv_opd_grad",
     "sv_greedy_plan", "sv_greedy",       "sv_greedy_pick", "sv_head_feat",
     "sv_head_pool",   "sv_len_loss",
-    "sv_branch",      "sv_tree_argmax",  "sv_tree_walk",    "sv_rowpair_part",
-    "sv_rowpair_fin",  "sv_read_probe"};
+    "sv_branch",      "sv_tree_argmax",  "sv_tree_walk",    "sv_rowpair_split",
+    "sv_read_probe"};
 enum {
   K_PLAN,
   K_ROWPAIR,
@@ -48,8 +48,7 @@ enum {
   K_BRANCH,
   K_TREE_ARGMAX,
   K_TREE_WALK,
-  K_ROWPAIR_PART,
-  K_ROWPAIR_FIN,
+  K_ROWPAIR_SPLIT,
   K_READ_PROBE
 };
 
@@ -202,8 +201,8 @@ bool fit_workspace(const void* workspace, size_t bytes, Dims& dm) {
   return bytes >= sv::carve(dm, nullptr, nullptr);
 }
 
-// The streaming pass over n_units rows (pairs): one launch, or for small launches the split
-// streaming launch and the finalize launch.
+// The streaming pass over n_units rows (pairs): one launch, each row streamed by one workgroup,
+// or for small launches by several (the part of a row that arrives last finishes it).
 hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace& ws, int64_t rec_slots,
                        hipStream_t st, int k_whole, bool* folded_out = nullptr) {
   const int P = rec_slots > 0 ? sv::row_split(ra.n_units, ra.n_slices) : 1;
@@ -215,19 +214,12 @@ hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace&
     ra.split = 1;
     return timed(k_whole, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
   }
+  ra.phase = 1;
   ra.split = P;
   ra.rec = ws.rec;
-  if (ra.n_units * P <= sv::kFoldGroups) {  // the last part of each row folds it, one launch
-    ra.phase = 3;
-    ra.flags = ws.flags;
-    ra.epoch = next_epoch();
-    return timed(K_ROWPAIR_PART, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
-  }
-  ra.phase = 1;
-  hipError_t e = timed(K_ROWPAIR_PART, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
-  if (e != hipSuccess) return e;
-  ra.phase = 2;
-  return timed(K_ROWPAIR_FIN, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
+  ra.flags = ws.flags;
+  ra.epoch = next_epoch();
+  return timed(K_ROWPAIR_SPLIT, st, [&] { return sv::launch_rowpair(dtype, vec, ra, st); });
 }
 
 // The clipped reverse-KL of n_rows row pairs, and with hard_out the hard-label

@@ -54,15 +54,13 @@ struct RowPairArgs {
   int32_t* arrive;  // nullable: per-request draw counters, zeroed here for the draw kernel
   // Rows split over several workgroups (small launches): phase 0 streams and finalizes each
   // row (pair) in one workgroup; phase 1 streams part `blockIdx % split` of row (pair)
-  // `blockIdx / split` and stores its lane records in rec; phase 2 folds a row's records and
-  // finalizes it.
+  // `blockIdx / split`, stores its lane records in rec and sets its arrival flag (the launch's
+  // nonzero epoch); the part that finds every part of its row arrived folds the row's records
+  // and finalizes it.
   int32_t phase;
   int32_t split;
-  void* rec;  // [n_units * split * rec_lanes(folded)] lane records (phases 1, 2 and 3)
+  void* rec;       // [n_units * split * rec_lanes(folded)] lane records
   int32_t folded;  // parts fold their four waves: kFoldLanes records a part, else kRowThreads
-  // Phase 3 streams part `blockIdx % split` of row (pair) `blockIdx / split` like phase 1; the
-  // part that arrives last (arrival flags set to the launch's nonzero epoch) folds the row's
-  // records and finalizes it, in the same launch.
   uint32_t* flags;  // [n_units * 16]
   uint32_t epoch;
   // verification with the reverse-KL, nullable: rows whose heavy lanes the draw launch sums

@@ -52,10 +52,6 @@ constexpr size_t kLaneRecBytes = 72;
 constexpr int kFoldLanes = 64;
 constexpr int kFoldMinSplit = 9;
 constexpr int rec_lanes(bool folded) { return folded ? kFoldLanes : kRowThreads; }
-// Split launches of at most kFoldGroups streaming workgroups (about one per CU) fold their
-// records in the same launch (the part of a row that arrives last); larger ones in a finalize
-// launch.
-constexpr int64_t kFoldGroups = 256;
 inline int row_split(int64_t n_units, int64_t n_slices) {
   if (n_units < 1 || n_units > kSplitMaxUnits) return 1;
   int64_t P = (kSplitTarget + n_units - 1) / n_units;
@@ -148,7 +144,7 @@ struct Workspace {
   RowStats* stats;     // [n_grad] OPD gradient: per-row forward statistics
   float* coef;         // [2 n_grad] OPD gradient: (alpha / k_b, (1 - alpha) / k_b) per row
   RklFix* fix;         // [n_d] verification: heavy lanes left to the draw launch per draft row
-  uint32_t* flags;     // [n_units * 16] arrival flags of rows split in a launch that folds them
+  uint32_t* flags;     // [n_units * 16] arrival flags of the parts of split rows
 };
 
 struct Dims {

@@ -23,12 +23,11 @@
 //   the acceptance test u < min(1, p_T(x)/q_T(x)) (paper, Section 2.1), or for T = 0
 //     the argmax match (DFlash notes, Section 5.2, worked example #4);
 //   the offsets the sampler needs to rebuild p_T and q_T of this row.
-// Launches of few rows split each row over several workgroups, which hand their lane records
-// to a finalize launch (phases 1 and 2), or, in launches of about one workgroup per CU, to the
-// part of the row that arrives last (phase 3), which folds them and finishes the row.  Rows
-// split into many parts fold each part's four waves lane by lane first, into 64 lane records
-// (lane l: the columns of thread l of every wave, in every slice), and are finished from those
-// 64 lanes.
+// Launches of few rows split each row over several workgroups (PHASE 1), which hand their
+// lane records to the part of the row that arrives last; that part folds them and finishes the
+// row.  Rows split into many parts fold each part's four waves lane by lane first, into 64 lane
+// records (lane l: the columns of thread l of every wave, in every slice), and are finished
+// from those 64 lanes.
 //
 // Request layout: for batches up to kInlinePlanMaxB requests every workgroup scans k
 // itself (no separate plan launch); larger batches read per-row descriptors.
@@ -254,38 +253,28 @@ __device__ __forceinline__ LaneRec lane_record(const LaneAcc& A) {
 // wave reads the same column offsets of its slices, so folded lane l of a split row covers
 // columns l 8 .. l 8 + 7 of each 512-column group of every slice).  Laid out word-major: word i
 // of lane l of a part at words[i * lanes + l], so that each store and load of a wave covers
-// 512 contiguous bytes.  COHERENT (phase 3, whose records are read back within the launch):
-// written and read as 64-bit words with device-scope atomics, which go to and come from the
-// coherence point shared by every XCD instead of this XCD's L2.
+// 512 contiguous bytes.  The records are read back within the launch, so they are written and
+// read as 64-bit words with device-scope atomics, which go to and come from the coherence
+// point shared by every XCD instead of this XCD's L2.
 static_assert(sizeof(LaneRec) % 8 == 0 && alignof(LaneRec) == 8, "records move as 64-bit words");
 static_assert(sizeof(LaneRec) <= kLaneRecBytes && kFoldLanes == 64, "one folded record per thread of a wave");
 constexpr int kRecWords = static_cast<int>(sizeof(LaneRec) / 8);
 constexpr int kFoldMaxParts = 16;  // parts a split row may have (row_split gives at most 16)
 constexpr int kFoldRecs = 8;       // records one thread of the finalize folds, at most
 static_assert(kFoldMaxParts / kRowWaves <= kFoldRecs && kFoldMinSplit - 1 <= kFoldRecs, "finalize folds");
-template <bool COHERENT>
 __device__ __forceinline__ void store_record(uint64_t* part_words, int l, int lanes, const LaneRec& r) {
   uint64_t w[kRecWords];
   __builtin_memcpy(w, &r, sizeof(LaneRec));
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) {
-    if constexpr (COHERENT)
-      __hip_atomic_store(part_words + i * lanes + l, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      part_words[i * lanes + l] = w[i];
-  }
+  for (int i = 0; i < kRecWords; ++i)
+    __hip_atomic_store(part_words + i * lanes + l, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <bool COHERENT>
 __device__ __forceinline__ LaneRec load_record(const uint64_t* part_words, int l, int lanes) {
   uint64_t w[kRecWords];
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) {
-    if constexpr (COHERENT)
-      w[i] = __hip_atomic_load(const_cast<uint64_t*>(part_words + i * lanes + l), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    else
-      w[i] = part_words[i * lanes + l];
-  }
+  for (int i = 0; i < kRecWords; ++i)
+    w[i] = __hip_atomic_load(const_cast<uint64_t*>(part_words + i * lanes + l), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   LaneRec r;
   __builtin_memcpy(&r, w, sizeof(LaneRec));
   return r;
@@ -295,12 +284,11 @@ __device__ __forceinline__ uint64_t* part_records(const RowPairArgs& a, int64_t 
   return static_cast<uint64_t*>(a.rec) + (unit * a.split + p) * kRecWords * rec_lanes(a.folded);
 }
 
-// The finalize of a split row, the records folded in part order with all loads issued at once
-// (load, on entry where nothing else is needed first).  Unfolded records: thread t folds its
+// The finalize of a split row, the records folded in part order with all loads issued at once.
+// Unfolded records: thread t folds its
 // lane's records of every part.  Folded: thread (q, l) folds lane l of a quarter of the parts
 // (parts q per .. q per + per - 1, per = ceil(split / 4)), then wave 0 folds the quarters in
 // order and lacc holds the row's 64 lanes, the other 192 empty.
-template <bool COHERENT>
 struct PartFold {
   LaneRec R[kFoldRecs];
   __device__ __forceinline__ void range(const RowPairArgs& a, int tid, int& p0, int& per) const {
@@ -313,12 +301,12 @@ struct PartFold {
     const int lanes = rec_lanes(a.folded), l = a.folded ? (tid & 63) : tid;
 #pragma unroll
     for (int u = 0; u < kFoldRecs; ++u)
-      if (u < per && p0 + u < a.split) R[u] = load_record<COHERENT>(part_records(a, unit, p0 + u), l, lanes);
+      if (u < per && p0 + u < a.split) R[u] = load_record(part_records(a, unit, p0 + u), l, lanes);
   }
   __device__ __forceinline__ void fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const;
 };
 
-// Arrival flags of a row's parts (phase 3): part p of a row sets word p of the row's
+// Arrival flags of a row's parts: part p of a row sets word p of the row's
 // kFoldMaxParts flag words to the launch's epoch once its records are complete at the coherence
 // point, waits for that store to complete there, then reads every part's flag.  Of two parts,
 // the one that sets its flag later sees the other's, so the part that arrives last sees every
@@ -608,8 +596,7 @@ __device__ __forceinline__ void lane_merge(LaneAcc& A, const LaneRec& R) {
   }
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ void PartFold<COHERENT>::fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const {
+__device__ __forceinline__ void PartFold::fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const {
   int p0, per;
   range(a, tid, p0, per);
   LaneAcc F;
@@ -770,7 +757,7 @@ struct Scratch {
   int* failed;
   int* s_nfail;
   int* s_nheavy;  // a counter of its own: the heavy list is read while the next one starts
-  int* s_last;    // phase 3: this part found every part of the row arrived
+  int* s_last;    // split rows: this part found every part of the row arrived
   double* red_d;
   float* red_f;
   int* red_i;
@@ -1022,7 +1009,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
   // and touch no memory.
   const bool x_ok = PAIR && xr >= 0 && xr < V;
   uint32_t u_bits = 0, lp_bits = 0, lq_bits = 0;
-  if constexpr (PHASE != 1) {
+  {
     // a zero the compiler cannot see through: with it the loaded values are per-lane to the
     // compiler, which then leaves them in vector registers instead of waiting for them at once
     // to move them to scalar ones
@@ -1046,10 +1033,10 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     }
   }
 
-  if constexpr (PHASE != 2) {  // stream the row (pair), or this workgroup's part of it
+  {  // stream the row (pair), or this workgroup's part of it
     LaneAcc L;
     lane_clear(L);
-    constexpr bool PART = PHASE == 1 || PHASE == 3;
+    constexpr bool PART = PHASE == 1;
     const int first = (PART ? ctx.part * kRowWaves : 0) + wave;
     const int step = kRowWaves * (PART ? a.split : 1);
     stream_row<DT, VEC, PAIR, MODE>(prow, qrow, ctx.beta, V, n_slices, first, step, lane, L);
@@ -1063,23 +1050,22 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
     }
     lacc[tid] = L;  // the finalize reads the record back as it needs it
     if constexpr (PART) {
-      // A part stores its lane records (folded: wave 0 folds the four waves' lanes first).
-      // Phase 1 leaves them to the finalize launch.  In phase 3 they go to the coherence point
-      // shared by every XCD; once every wave's are complete there wave 0 sets the part's
-      // arrival flag and reads the row's.  A part that finds every flag set reads the records
-      // back from the coherence point, folds them and finishes the row; the others are done.
+      // A part stores its lane records (folded: wave 0 folds the four waves' lanes first) at
+      // the coherence point shared by every XCD; once every wave's are complete there wave 0
+      // sets the part's arrival flag and reads the row's.  A part that finds every flag set
+      // reads the records back from the coherence point, folds them and finishes the row; the
+      // others are done.
       uint64_t* mine = part_records(a, ctx.unit, ctx.part);
       if (a.folded) {
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
           for (int q = 1; q < kRowWaves; ++q) lane_merge(L, lane_record(lacc[q * kFoldLanes + lane]));
-          store_record<PHASE == 3>(mine, lane, kFoldLanes, lane_record(L));
+          store_record(mine, lane, kFoldLanes, lane_record(L));
         }
       } else {
-        store_record<PHASE == 3>(mine, tid, kRowThreads, lane_record(L));
+        store_record(mine, tid, kRowThreads, lane_record(L));
       }
-      if constexpr (PHASE == 1) return;
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       if (wave == 0) {
@@ -1094,13 +1080,12 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       }
       __syncthreads();
       if (!*sc.s_last) return;
-      PartFold<true> pf;
+      PartFold pf;
       pf.load(a, ctx.unit, tid);
       pf.fold(a, tid, lacc);
     }
   }
-  // (a split row's records were folded into lacc: by the finalize launch on entry, or above by
-  // the part that arrived last)
+  // (a split row's records were folded into lacc above, by the part that arrived last)
   const LaneAcc& A = lacc[tid];
   const int col_base = (PHASE != 0 && a.folded) ? kRowThreads : 0;  // how the lanes' columns are numbered
 
@@ -1416,8 +1401,8 @@ __device__ __forceinline__ bool resolve_unit(const RowPairArgs& a, int64_t unit,
 }
 
 // PHASE 0: one workgroup streams and finishes a row (pair).  PHASE 1: workgroup blockIdx
-// streams part blockIdx % split of row (pair) blockIdx / split and stores its lane records.
-// PHASE 2: one workgroup per row (pair) folds the records and finishes it.
+// streams part blockIdx % split of row (pair) blockIdx / split and stores its lane records;
+// the part of the row that arrives last folds them and finishes the row.
 template <int DT, bool VEC, int PHASE>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void sv_rowpair_kernel(RowPairArgs a) {
@@ -1436,13 +1421,11 @@ void sv_rowpair_kernel(RowPairArgs a) {
   const Scratch sc{lacc, direct, direct_x, direct_u0, failed, &s_nfail, &s_nheavy, &s_last, red_d, red_f, red_i, red_v};
   const int tid = thread_index();
   const int64_t blk = block_index();
-  const int64_t unit = (PHASE == 1 || PHASE == 3) ? blk / a.split : blk;
-  PartFold<false> first;  // phase 2: the records, which depend on nothing else
-  if constexpr (PHASE == 2) first.load(a, unit, tid);
+  const int64_t unit = PHASE == 1 ? blk / a.split : blk;
 
   RowCtx ctx;
   ctx.unit = unit;
-  ctx.part = (PHASE == 1 || PHASE == 3) ? static_cast<int>(blk - unit * a.split) : 0;
+  ctx.part = PHASE == 1 ? static_cast<int>(blk - unit * a.split) : 0;
   if (a.rkl_only) {  // unit = draft row, paired with target row p_row_index[unit]
     ctx.d = unit;
     ctx.t = a.p_row_index ? a.p_row_index[unit] : unit;
@@ -1460,7 +1443,6 @@ void sv_rowpair_kernel(RowPairArgs a) {
       return;
     }
     if (tid == 0) a.row_flags[unit] = 0;
-    if constexpr (PHASE == 2) first.fold(a, tid, lacc);
     if (a.hard_out) {  // with the hard-label cross-entropy: track the target row's argmax
       ctx.mode = 1;
       rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, -1);
@@ -1474,7 +1456,7 @@ void sv_rowpair_kernel(RowPairArgs a) {
   // every thread, is fetched with the lengths and temperatures; it is checked, and the logits
   // at it are fetched, once the row has been streamed
   int32_t xr = -1;
-  if (PHASE != 1 && unit < a.n_d) xr = a.tokens[unit];
+  if (unit < a.n_d) xr = a.tokens[unit];
   if (!resolve_unit<true>(a, unit, tid, red_i, s_req, s_off, s_t, s_void, &s_T)) return;
   const int64_t b = s_req;
   const int64_t off = s_off;
@@ -1495,12 +1477,11 @@ void sv_rowpair_kernel(RowPairArgs a) {
     ctx.mode = 2;
     ctx.beta = kL2E / T;
   }
-  if (PHASE != 1 && i == 0 && tid == 0 && !a.desc) {
+  if (i == 0 && tid == 0 && !a.desc) {
     a.off_t[b] = static_cast<int32_t>(off);
     if (a.arrive) a.arrive[b] = 0;  // the draw kernel counts its workgroups from zero
   }
   ctx.row_flags = flags;  // thread 0 adds the token and uniform bits after the stream
-  if constexpr (PHASE == 2) first.fold(a, tid, lacc);
   if (ctx.d >= 0) {
     if (ctx.mode == 0) rowpair_body<DT, VEC, PHASE, true, 0>(a, ctx, sc, xr);
     if (ctx.mode == 1) rowpair_body<DT, VEC, PHASE, true, 1>(a, ctx, sc, xr);
@@ -1680,24 +1661,22 @@ hipError_t launch_row_argmax(int dtype, bool vec, const ArgmaxArgs& a, hipStream
 
 // ----------------------------------------------------------------------------- launch
 hipError_t launch_rowpair(int dtype, bool vec, const RowPairArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.n_units * ((a.phase == 1 || a.phase == 3) ? a.split : 1)));
+  const dim3 grid(static_cast<unsigned>(a.n_units * (a.phase == 1 ? a.split : 1)));
   if (a.n_units == 0) return hipSuccess;
-  if (a.phase < 0 || a.phase > 3 || (a.phase != 0 && (a.split < 2 || !a.rec)) ||
-      (a.phase == 3 && (!a.flags || a.epoch == 0 || a.split > kFoldMaxParts)))
+  if (a.phase < 0 || a.phase > 1 ||
+      (a.phase == 1 && (a.split < 2 || a.split > kFoldMaxParts || !a.rec || !a.flags || a.epoch == 0)))
     return hipErrorInvalidValue;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, a); };
-  auto by_phase = [&](auto k0, auto k1, auto k2, auto k3) {
+  auto by_phase = [&](auto k0, auto k1) {
     if (a.phase == 0) go(k0);
-    else if (a.phase == 1) go(k1);
-    else if (a.phase == 2) go(k2);
-    else go(k3);
+    else go(k1);
   };
   if (dtype == 0) {
-    if (vec) by_phase(sv_rowpair_kernel<0, true, 0>, sv_rowpair_kernel<0, true, 1>, sv_rowpair_kernel<0, true, 2>, sv_rowpair_kernel<0, true, 3>);
-    else by_phase(sv_rowpair_kernel<0, false, 0>, sv_rowpair_kernel<0, false, 1>, sv_rowpair_kernel<0, false, 2>, sv_rowpair_kernel<0, false, 3>);
+    if (vec) by_phase(sv_rowpair_kernel<0, true, 0>, sv_rowpair_kernel<0, true, 1>);
+    else by_phase(sv_rowpair_kernel<0, false, 0>, sv_rowpair_kernel<0, false, 1>);
   } else {
-    if (vec) by_phase(sv_rowpair_kernel<1, true, 0>, sv_rowpair_kernel<1, true, 1>, sv_rowpair_kernel<1, true, 2>, sv_rowpair_kernel<1, true, 3>);
-    else by_phase(sv_rowpair_kernel<1, false, 0>, sv_rowpair_kernel<1, false, 1>, sv_rowpair_kernel<1, false, 2>, sv_rowpair_kernel<1, false, 3>);
+    if (vec) by_phase(sv_rowpair_kernel<1, true, 0>, sv_rowpair_kernel<1, true, 1>);
+    else by_phase(sv_rowpair_kernel<1, false, 0>, sv_rowpair_kernel<1, false, 1>);
   }
   return hipGetLastError();
 }

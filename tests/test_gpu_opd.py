@@ -188,7 +188,7 @@ def test_bad_lengths_and_pairing_are_flagged():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_split_rows(dtype):
-    # 10 rows of 60 slices: each row is streamed in parts and folded by the finalize launch;
+    # 10 rows of 60 slices: each row is streamed in parts and folded by the part that arrives last;
     # the hard-label cross-entropy needs the first argmax across parts
     import draft_block_verification_sv_amd as pkg
 
@@ -208,8 +208,8 @@ def test_split_rows(dtype):
 
 @pytest.mark.parametrize("dtype,k", [("bf16", [4, 1, 5]), ("f32", [4, 1, 5]), ("bf16", [9, 8, 7])])
 def test_folded_split_rows(dtype, k):
-    # 137 slices a row: split into 16 parts that fold their waves into 64 lanes.  10 rows: the
-    # part arriving last finishes each row in the streaming launch; 24 rows: a finalize launch.
+    # 137 slices a row: split into 16 parts that fold their waves into 64 lanes (10 rows: 160
+    # workgroups; 24 rows: 384), the part arriving last finishing each row.
     # Without a draw launch every heavy or clipped lane is summed again in the finalize, in
     # four blocks.
     import draft_block_verification_sv_amd as pkg

@@ -145,7 +145,7 @@ def test_heavy_lanes(dtype, B, delta):
 # The same rows long enough (137 slices) that a small launch splits them into 16 parts, which
 # fold their four waves into 64 lanes: the heavy tokens' lanes stay distinct, now holding four
 # times the columns, re-read in four blocks (finalize: 12 heavy lanes; draw launch: 6, 2, 1).
-# B = 4 (14 rows): one launch; B = 8 (28 rows): parts, then a finalize launch.
+# B = 4 (14 rows): 224 streaming workgroups; B = 8 (28 rows): 448.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B", [4, 8])
 def test_heavy_lanes_folded(dtype, B):
@@ -433,9 +433,9 @@ def test_fused_rkl_and_standalone():
 
 
 # ----------------------------------------------------------------------------- split rows
-# Launches of a few rows split each row over several workgroups (parts) and fold the parts'
-# lane records in a finalize launch.  V = 70001: 69 slices, so 8 parts per row, the last
-# slice ragged.
+# Launches of a few rows split each row over several workgroups (parts); the part of a row
+# that arrives last folds the parts' lane records.  V = 70001: 69 slices, so 8 parts per row,
+# the last slice ragged.
 @pytest.mark.parametrize("dtype,ld", [("bf16", 70001), ("f32", 70004)])
 def test_split_rows_parity(dtype, ld):
     w = make_workload(B=4, k=[3, 1, 5, 2], V=70001, ld=ld, dtype=dtype, s=3.0,
@@ -448,15 +448,15 @@ def test_split_rows_parity(dtype, ld):
     assert s["exact"] >= w.B - 1
 
 
-# The four ways a small launch splits its rows, by rows (n) and parts per row (P): 16 parts
-# fold each part's four waves into 64 lanes, fewer keep 256; a launch of at most 256
-# workgroups finishes its rows itself (the last part to arrive), a larger one in a finalize
-# launch.  V = 70001 (69 slices, ragged): P = 8; V = 140001 (137 slices): P = 16.
+# Small launches split their rows, by rows (n) and parts per row (P): more than 8 parts fold
+# each part's four waves into 64 lanes, fewer keep 256; launches of up to about one and of
+# about two workgroups per CU.  V = 70001 (69 slices, ragged): P = 8; V = 140001 (137 slices):
+# P = 16.
 @pytest.mark.parametrize("case", [
-    ("folded, one launch", 140001, [6, 5], "bf16"),                 # n = 13, P = 16: 208 WGs
-    ("folded, finalize launch", 140001, [9, 7, 8], "bf16"),         # n = 27, P = 16: 432 WGs
-    ("folded, finalize launch f32", 140004, [4, 9, 2, 6], "f32"),   # n = 25, P = 16
-    ("unfolded, finalize launch", 70001, [7, 7, 7, 7, 7], "bf16"),  # n = 40, P = 8: 320 WGs
+    ("folded, 13 rows", 140001, [6, 5], "bf16"),                # n = 13, P = 16: 208 WGs
+    ("folded, 27 rows", 140001, [9, 7, 8], "bf16"),             # n = 27, P = 16: 432 WGs
+    ("folded, 25 rows f32", 140004, [4, 9, 2, 6], "f32"),       # n = 25, P = 16
+    ("unfolded, 40 rows", 70001, [7, 7, 7, 7, 7], "bf16"),      # n = 40, P = 8: 320 WGs
 ])
 def test_split_regimes(case):
     name, V, k, dtype = case

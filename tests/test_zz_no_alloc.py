@@ -56,9 +56,10 @@ def test_noalloc_matches_workspace_entry_point():
 
 
 def test_noalloc_split_rows_in_one_launch():
-    # Rows split into 16 parts that fold their waves: a single request of 16 rows finishes in
-    # the streaming launch (arrival flags in the scratch), 19 rows in a finalize launch.  The
-    # fixed scratch holds their records, so both entry points split alike and agree bit for bit.
+    # Rows split into 16 parts that fold their waves (a single request of 16 rows, and 19
+    # rows), finished by the part of each row that arrives last (arrival flags in the scratch).
+    # The fixed scratch holds their records, so both entry points split alike and agree bit
+    # for bit.
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import draft_block_verification_sv_amd as pkg
