@@ -776,7 +776,7 @@ def main():
     meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
     # small launches split each row over several workgroups: the streaming launch then reads
     # every logit and a short finalize launch folds the parts
-    stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_part"
+    stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_split"
     rows_us = kernels[stream_name]["avg_us"]
     kernel_gbs = rows_bytes / (rows_us * 1e-6) / 1e9
     traffic = None

@@ -42,9 +42,10 @@ inline int64_t n_slices_for(int64_t V) { return (V + kSlice - 1) / kSlice; }
 // lane records (at most kLaneRecBytes each) for the finalize: one per thread, or when a row has
 // at least kFoldMinSplit parts, kFoldLanes, the part's four waves folded lane by lane.  Only
 // launches of at most kSplitMaxUnits rows split (with more, one workgroup per row already
-// covers most of the chip and the records and their fold cost more than they save); they aim
-// at about kSplitTarget streaming workgroups, with at most 16 parts per row, at least two
-// slices per wave and at most kSplitSlots record sets in all.
+// covers most of the chip and the records and their fold cost more than they save); they take
+// at most kSplitTarget streaming workgroups (two per CU, which the split kernel's registers
+// allow at once: a launch that needs a second round of workgroups is slower), with at most 16
+// parts per row, at least two slices per wave and at most kSplitSlots record sets in all.
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitMaxUnits = 128;
 constexpr int64_t kSplitSlots = 1024;
@@ -54,7 +55,7 @@ constexpr int kFoldMinSplit = 9;
 constexpr int rec_lanes(bool folded) { return folded ? kFoldLanes : kRowThreads; }
 inline int row_split(int64_t n_units, int64_t n_slices) {
   if (n_units < 1 || n_units > kSplitMaxUnits) return 1;
-  int64_t P = (kSplitTarget + n_units - 1) / n_units;
+  int64_t P = kSplitTarget / n_units;
   if (P > 16) P = 16;
   if (P > n_slices / 8) P = n_slices / 8;
   if (P > kSplitSlots / n_units) P = kSplitSlots / n_units;
