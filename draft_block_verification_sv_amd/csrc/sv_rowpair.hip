@@ -285,10 +285,10 @@ __device__ __forceinline__ uint64_t* part_records(const RowPairArgs& a, int64_t 
 }
 
 // The finalize of a split row, the records folded in part order with all loads issued at once.
-// Unfolded records: thread t folds its
-// lane's records of every part.  Folded: thread (q, l) folds lane l of a quarter of the parts
-// (parts q per .. q per + per - 1, per = ceil(split / 4)), then wave 0 folds the quarters in
-// order and lacc holds the row's 64 lanes, the other 192 empty.
+// Unfolded records: thread t folds its lane's records of every part.  Folded: thread (q, l)
+// folds lane l of a quarter of the parts (parts q per .. q per + per - 1, per = ceil(split /
+// 4)), then wave 0 folds the quarters in order and lacc holds the row's 64 lanes, the other 192
+// empty.
 struct PartFold {
   LaneRec R[kFoldRecs];
   __device__ __forceinline__ void range(const RowPairArgs& a, int tid, int& p0, int& per) const {
@@ -306,13 +306,13 @@ struct PartFold {
   __device__ __forceinline__ void fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const;
 };
 
-// Arrival flags of a row's parts: part p of a row sets word p of the row's
-// kFoldMaxParts flag words to the launch's epoch once its records are complete at the coherence
-// point, waits for that store to complete there, then reads every part's flag.  Of two parts,
-// the one that sets its flag later sees the other's, so the part that arrives last sees every
-// flag set (others may too, and then finish the row as well, with the same results).  A flag
-// word holding anything but the epoch (the row's flags of an earlier launch, which had its own
-// epoch, or whatever the memory held) counts as not arrived.
+// Arrival flags of a row's parts: part p of a row sets word p of the row's kFoldMaxParts flag
+// words to the launch's epoch once its records are complete at the coherence point, waits for
+// that store to complete there, then reads every part's flag.  Of two parts, the one that sets
+// its flag later sees the other's, so the part that arrives last sees every flag set (others
+// may too, and then finish the row as well, with the same results).  A flag word holding
+// anything but the epoch (the row's flags of an earlier launch, which had its own epoch, or
+// whatever the memory held) counts as not arrived.
 
 __device__ __forceinline__ void lane_clear(LaneAcc& A) {
   A.kp = A.kq = A.ktp = A.ktq = 0.0f;
