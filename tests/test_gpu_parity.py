@@ -145,15 +145,16 @@ def test_heavy_lanes(dtype, B, delta):
 # The same rows long enough (137 slices) that a small launch splits them into 16 parts, which
 # fold their four waves into 64 lanes: the heavy tokens' lanes stay distinct, now holding four
 # times the columns, re-read in four blocks (finalize: 12 heavy lanes; draw launch: 6, 2, 1).
-# B = 4 (14 rows): 224 streaming workgroups; B = 8 (28 rows): 448.
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+# B = 4 (14 rows): 224 streaming workgroups; B = 8 (28 rows): 448.  V = 140001 leaves bf16 rows
+# unaligned (column by column loads); V = 139264 (136 slices) gives 16-byte rows.
+@pytest.mark.parametrize("dtype,V", [("bf16", 140001), ("f32", 140001), ("bf16", 139264)])
 @pytest.mark.parametrize("B", [4, 8])
-def test_heavy_lanes_folded(dtype, B):
-    w = _heavy_lane_workload(dtype, B, (31, B, dtype == "f32"), V=140001)
+def test_heavy_lanes_folded(dtype, V, B):
+    w = _heavy_lane_workload(dtype, B, (31, B, dtype == "f32"), V=V)
     got = run_gpu(w, delta=1.0)
     assert got["device_status"][0] == 0
     s = compare(w, got, run_oracle(w, delta=1.0))
-    _report(f"heavy lanes folded {dtype} B={B}", s)
+    _report(f"heavy lanes folded {dtype} V={V} B={B}", s)
 
 
 @pytest.mark.parametrize("B", [1, 65])  # one request: split rows; 65 (130 rows): one WG per row
