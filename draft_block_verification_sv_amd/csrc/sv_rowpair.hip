@@ -256,28 +256,89 @@ __device__ __forceinline__ LaneRec lane_record(const LaneAcc& A) {
 // 512 contiguous bytes.  The records are read back within the launch, so they are written and
 // read as 64-bit words with device-scope atomics, which go to and come from the coherence
 // point shared by every XCD instead of this XCD's L2.
-static_assert(sizeof(LaneRec) % 8 == 0 && alignof(LaneRec) == 8, "records move as 64-bit words");
+// A record moves only the words its row uses: (kp, kq), S_p, then for row pairs S_q, W and
+// (D, max E_q (l_q - l_p)); (amax, aidx) for greedy rows; (kt_p, kt_q), S_T,p and for pairs
+// S_T,q for rows with T_b not in {0, 1}.  The fields it leaves out read back as a cleared lane
+// holds them.  A part's slot keeps room for every word (kRecWords per lane).
 static_assert(sizeof(LaneRec) <= kLaneRecBytes && kFoldLanes == 64, "one folded record per thread of a wave");
-constexpr int kRecWords = static_cast<int>(sizeof(LaneRec) / 8);
+constexpr int kRecWords = static_cast<int>((sizeof(LaneRec) + 7) / 8);
 constexpr int kFoldMaxParts = 16;  // parts a split row may have (row_split gives at most 16)
 constexpr int kFoldRecs = 8;       // records one thread of the finalize folds, at most
 static_assert(kFoldMaxParts / kRowWaves <= kFoldRecs && kFoldMinSplit - 1 <= kFoldRecs, "finalize folds");
+template <bool PAIR, int MODE>
+constexpr int rec_words() {
+  return (PAIR ? 5 : 2) + (MODE == 1 ? 1 : 0) + (MODE == 2 ? (PAIR ? 3 : 2) : 0);
+}
+static_assert(rec_words<true, 2>() <= kRecWords, "a record fits its slot");
+__device__ __forceinline__ uint64_t two_words(float lo, float hi) {
+  return static_cast<uint64_t>(__float_as_uint(lo)) | (static_cast<uint64_t>(__float_as_uint(hi)) << 32);
+}
+__device__ __forceinline__ float lo_float(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+__device__ __forceinline__ float hi_float(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w >> 32)); }
+__device__ __forceinline__ uint64_t dword(double d) { return static_cast<uint64_t>(__double_as_longlong(d)); }
+__device__ __forceinline__ double dval(uint64_t w) { return __longlong_as_double(static_cast<long long>(w)); }
+template <bool PAIR, int MODE>
+__device__ __forceinline__ void pack_record(const LaneRec& r, uint64_t (&w)[rec_words<PAIR, MODE>()]) {
+  int i = 0;
+  w[i++] = two_words(r.kp, r.kq);
+  w[i++] = dword(r.sp);
+  if constexpr (PAIR) {
+    w[i++] = dword(r.sq);
+    w[i++] = dword(r.w);
+    w[i++] = two_words(r.dmax, r.xmax);
+  }
+  if constexpr (MODE == 1) w[i++] = two_words(r.amax, __int_as_float(r.aidx));
+  if constexpr (MODE == 2) {
+    w[i++] = two_words(r.ktp, r.ktq);
+    w[i++] = dword(r.stp);
+    if constexpr (PAIR) w[i++] = dword(r.stq);
+  }
+}
+template <bool PAIR, int MODE>
+__device__ __forceinline__ LaneRec unpack_record(const uint64_t (&w)[rec_words<PAIR, MODE>()]) {
+  LaneRec r;
+  r.ktp = r.ktq = 0.0f;
+  r.sq = r.w = r.stp = r.stq = 0.0;
+  r.dmax = r.xmax = r.amax = -INFINITY;
+  r.aidx = 0x7fffffff;
+  int i = 0;
+  r.kp = lo_float(w[i]);
+  r.kq = hi_float(w[i++]);
+  r.sp = dval(w[i++]);
+  if constexpr (PAIR) {
+    r.sq = dval(w[i++]);
+    r.w = dval(w[i++]);
+    r.dmax = lo_float(w[i]);
+    r.xmax = hi_float(w[i++]);
+  }
+  if constexpr (MODE == 1) {
+    r.amax = lo_float(w[i]);
+    r.aidx = __float_as_int(hi_float(w[i++]));
+  }
+  if constexpr (MODE == 2) {
+    r.ktp = lo_float(w[i]);
+    r.ktq = hi_float(w[i++]);
+    r.stp = dval(w[i++]);
+    if constexpr (PAIR) r.stq = dval(w[i++]);
+  }
+  return r;
+}
+template <bool PAIR, int MODE>
 __device__ __forceinline__ void store_record(uint64_t* part_words, int l, int lanes, const LaneRec& r) {
-  uint64_t w[kRecWords];
-  __builtin_memcpy(w, &r, sizeof(LaneRec));
+  uint64_t w[rec_words<PAIR, MODE>()];
+  pack_record<PAIR, MODE>(r, w);
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i)
+  for (int i = 0; i < rec_words<PAIR, MODE>(); ++i)
     __hip_atomic_store(part_words + i * lanes + l, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+template <bool PAIR, int MODE>
 __device__ __forceinline__ LaneRec load_record(const uint64_t* part_words, int l, int lanes) {
-  uint64_t w[kRecWords];
+  uint64_t w[rec_words<PAIR, MODE>()];
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i)
+  for (int i = 0; i < rec_words<PAIR, MODE>(); ++i)
     w[i] = __hip_atomic_load(const_cast<uint64_t*>(part_words + i * lanes + l), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-  LaneRec r;
-  __builtin_memcpy(&r, w, sizeof(LaneRec));
-  return r;
+  return unpack_record<PAIR, MODE>(w);
 }
 // Part p's records of row (pair) unit.
 __device__ __forceinline__ uint64_t* part_records(const RowPairArgs& a, int64_t unit, int p) {
@@ -295,13 +356,15 @@ struct PartFold {
     per = a.folded ? (a.split + kRowWaves - 1) / kRowWaves : a.split;
     p0 = a.folded ? (tid >> 6) * per : 0;
   }
+  template <bool PAIR, int MODE>
   __device__ __forceinline__ void load(const RowPairArgs& a, int64_t unit, int tid) {
     int p0, per;
     range(a, tid, p0, per);
     const int lanes = rec_lanes(a.folded), l = a.folded ? (tid & 63) : tid;
 #pragma unroll
     for (int u = 0; u < kFoldRecs; ++u)
-      if (u < per && p0 + u < a.split) R[u] = load_record(part_records(a, unit, p0 + u), l, lanes);
+      if (u < per && p0 + u < a.split)
+        R[u] = load_record<PAIR, MODE>(part_records(a, unit, p0 + u), l, lanes);
   }
   __device__ __forceinline__ void fold(const RowPairArgs& a, int tid, LaneAcc* lacc) const;
 };
@@ -1061,10 +1124,10 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
         if (wave == 0) {
 #pragma unroll
           for (int q = 1; q < kRowWaves; ++q) lane_merge(L, lane_record(lacc[q * kFoldLanes + lane]));
-          store_record(mine, lane, kFoldLanes, lane_record(L));
+          store_record<PAIR, MODE>(mine, lane, kFoldLanes, lane_record(L));
         }
       } else {
-        store_record(mine, tid, kRowThreads, lane_record(L));
+        store_record<PAIR, MODE>(mine, tid, kRowThreads, lane_record(L));
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
@@ -1081,7 +1144,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
       __syncthreads();
       if (!*sc.s_last) return;
       PartFold pf;
-      pf.load(a, ctx.unit, tid);
+      pf.load<PAIR, MODE>(a, ctx.unit, tid);
       pf.fold(a, tid, lacc);
     }
   }
