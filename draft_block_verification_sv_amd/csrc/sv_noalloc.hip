@@ -8,7 +8,8 @@
 // later call there: the array's name is a host-side stand-in in host code and is never passed
 // to a kernel.  The verification kernels write every scratch byte they read within the call,
 // except the arrival flags of rows split over several workgroups, which count only when
-// they hold that launch's own nonzero epoch, so nothing has to start at zero.  All calls on one GPU share that GPU's array: calls that
+// they hold that launch's own nonzero epoch and are cleared by the part that finishes the
+// row, so nothing has to start at zero.  All calls on one GPU share that GPU's array: calls that
 // overlap on one GPU (two streams, or two host threads) race on it and must be serialised by
 // the caller.
 #include <hip/hip_runtime.h>

@@ -375,7 +375,9 @@ struct PartFold {
 // its flag later sees the other's, so the part that arrives last sees every flag set (others
 // may too, and then finish the row as well, with the same results).  A flag word holding
 // anything but the epoch (the row's flags of an earlier launch, which had its own epoch, or
-// whatever the memory held) counts as not arrived.
+// whatever the memory held) counts as not arrived.  A part that finds every flag set clears
+// them: all parts have set theirs by then, so they stay cleared, and a replay of a captured
+// launch, which carries the same epoch, starts from cleared flags.
 
 __device__ __forceinline__ void lane_clear(LaneAcc& A) {
   A.kp = A.kq = A.ktp = A.ktq = 0.0f;
@@ -1139,6 +1141,10 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
                                ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                : a.epoch;
         const int all = __all(e == a.epoch);
+        // every part has set its flag: back to 0, so that a replay of this launch with the
+        // same epoch (a captured graph) starts from cleared flags
+        if (all && lane < a.split)
+          __hip_atomic_store(flags + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) *sc.s_last = all ? 1 : 0;
       }
       __syncthreads();
