@@ -403,6 +403,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.fix = ws.fix;
   sa.n_slices = n_slices;
   sa.folded = folded ? 1 : 0;
+  sa.fix_rows = (folded && rkl_out) ? n_d : 0;
   if (timed(K_DRAW, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

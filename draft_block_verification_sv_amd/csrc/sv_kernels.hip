@@ -623,65 +623,50 @@ __device__ __forceinline__ void finish_rkl_rows(const SampleArgs& a, int64_t b, 
   }
 }
 
-// After a split streaming pass the heavy lanes are folded ones, four times as long, and a row
-// is taken by all four waves of a workgroup, wave w summing block w of every heavy lane
-// (lane_blocks), the blocks' sums meeting in s_part (the draw's chunk masses, no longer needed)
-// and wave 0 adding them up in block order, as one wave would.  The rows go to the workgroups
-// that do not pick, by their draw ticket (ticket t: rows t, t + mass_blocks - 1, ...), so that
-// the pick waits for none of them; a request drawn without tickets (greedy, invalid) spreads
-// them over every workgroup (rows g, g + mass_blocks, ...), and a request with one workgroup
-// finishes them there after its pick.
+// After a split streaming pass the heavy lanes are folded ones, four times as long, and each
+// draft row has a workgroup of its own, after the drawing ones, so that the rows start with
+// the launch and the pick waits for none of them.  Wave w sums block w of every heavy lane
+// (lane_blocks), the blocks' sums meet in s_part, and wave 0 adds them up in block order, as
+// one wave would.  The record (n = 0 for a row the stream finished, and for every row of a void
+// call) names the row's target row.
 template <int DT, bool VEC>
-__device__ __forceinline__ void finish_rkl_rows_folded(const SampleArgs& a, int64_t b, int g,
-                                                       int64_t off, int kb, int wave, int lane,
-                                                       const int* s_ticket, double* s_part) {
+__device__ __forceinline__ void finish_rkl_row_folded(const SampleArgs& a, int64_t d, int wave,
+                                                      int lane, double* s_part) {
   static_assert(kMassWaves == kRowWaves && kFixLanes * kMassWaves * 3 <= kMaxChunks, "block sums fit s_part");
-  if (!a.rkl_out || !a.fix) return;
-  __syncthreads();  // every wave is done with the draw and with the chunk masses
-  const int ticket = *s_ticket;
-  int first = g, step = a.mass_blocks;
-  if (ticket >= 0 && a.mass_blocks > 1) {
-    if (ticket == a.mass_blocks - 1) return;  // the picking workgroup
-    first = ticket;
-    step = a.mass_blocks - 1;
+  const uint32_t rec = load_fix_words(a, d, true, lane);
+  const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
+  if (n <= 0) return;
+  const int64_t t = fix_word(rec, offsetof(RklFix, t_row) / 4);
+  const void* prow = logits_row<DT>(a.target, t, a.ld_t);
+  const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
+  for (int j = 0; j < n; ++j) {
+    const int h0 = offsetof(RklFix, h) / 4 + j * 4;
+    const int src = fix_word(rec, h0);
+    if (wave >= lane_blocks(src)) continue;
+    const LaneSums e = exact_lane_sums<DT, VEC>(
+        prow, qrow, a.V, static_cast<int>(a.n_slices), src, wave, lane,
+        static_cast<double>(__int_as_float(fix_word(rec, h0 + 2))),
+        static_cast<double>(__int_as_float(fix_word(rec, h0 + 3))));
+    if (lane == 0) {
+      double* o = s_part + (j * kMassWaves + wave) * 3;
+      o[0] = e.sp;
+      o[1] = e.sq;
+      o[2] = e.w;
+    }
   }
-  for (int i = first; i < kb; i += step) {
-    const int64_t d = off - b + i;
-    const uint32_t rec = load_fix_words(a, d, true, lane);
-    const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
-    if (n <= 0) continue;
-    const void* prow = logits_row<DT>(a.target, off + i, a.ld_t);
-    const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
-    for (int j = 0; j < n; ++j) {
-      const int h0 = offsetof(RklFix, h) / 4 + j * 4;
-      const int src = fix_word(rec, h0);
-      if (wave >= lane_blocks(src)) continue;
-      const LaneSums e = exact_lane_sums<DT, VEC>(
-          prow, qrow, a.V, static_cast<int>(a.n_slices), src, wave, lane,
-          static_cast<double>(__int_as_float(fix_word(rec, h0 + 2))),
-          static_cast<double>(__int_as_float(fix_word(rec, h0 + 3))));
-      if (lane == 0) {
-        double* o = s_part + (j * kMassWaves + wave) * 3;
-        o[0] = e.sp;
-        o[1] = e.sq;
-        o[2] = e.w;
+  __syncthreads();
+  if (wave == 0) {
+    finish_rkl_from(a, d, rec, n, lane, [&](int j) {
+      const int src = fix_word(rec, offsetof(RklFix, h) / 4 + j * 4);
+      LaneSums r{0.0, 0.0, 0.0};
+      for (int q = 0; q < lane_blocks(src); ++q) {
+        const double* o = s_part + (j * kMassWaves + q) * 3;
+        r.sp += o[0];
+        r.sq += o[1];
+        r.w += o[2];
       }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      finish_rkl_from(a, d, rec, n, lane, [&](int j) {
-        const int src = fix_word(rec, offsetof(RklFix, h) / 4 + j * 4);
-        LaneSums r{0.0, 0.0, 0.0};
-        for (int q = 0; q < lane_blocks(src); ++q) {
-          const double* o = s_part + (j * kMassWaves + q) * 3;
-          r.sp += o[0];
-          r.sq += o[1];
-          r.w += o[2];
-        }
-        return r;
-      });
-    }
-    __syncthreads();  // wave 0 has read the sums before the next row's are written
+      return r;
+    });
   }
 }
 
@@ -873,17 +858,24 @@ __device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int
 // calls and invalid requests are written by workgroup 0, with their input-check bits.
 // Each wave derives the request state itself (a few cached loads), so only the pick needs
 // the workgroup's barrier.  A wave done with the draw then finishes the request's reverse-KL
-// rows that the streaming pass left to this launch (finish_rkl_rows).  Register use is capped so that all the workgroups of a B = 128
+// rows that the streaming pass left to this launch (finish_rkl_rows); after a split streaming
+// pass whose parts were folded, the workgroups after the drawing ones take one draft row each
+// (finish_rkl_row_folded).  Register use is capped so that all the workgroups of a B = 128
 // call are resident at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void sv_draw_kernel(SampleArgs a) {
   __shared__ double s_pm[kMaxChunks];  // the picking wave's chunk masses (p_T's after a fallback)
-  __shared__ int s_ticket;  // the workgroup's draw ticket (-1: none taken)
-  const int64_t b = blockIdx.x / a.mass_blocks;
-  const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
+  __shared__ int s_ticket;  // the workgroup's draw ticket
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t drawing = a.B * a.mass_blocks;
+  if (static_cast<int64_t>(blockIdx.x) >= drawing) {  // a folded draft row's heavy lanes
+    finish_rkl_row_folded<DT, VEC>(a, blockIdx.x - drawing, wave, lane, s_pm);
+    return;
+  }
+  const int64_t b = blockIdx.x / a.mass_blocks;
+  const int g = static_cast<int>(blockIdx.x - b * a.mass_blocks);
   int my_tok;    // lane i holds draft token i of the request
   float my_u;    // and the uniform of target row i
   const ReqState rq = wave_request_state(a, b, &my_tok, &my_u);
@@ -900,14 +892,10 @@ void sv_draw_kernel(SampleArgs a) {
   // the record of this wave's first reverse-KL row left to this launch, read while it draws
   const int i_fix = a.folded ? -1 : first_fix_row(a, g, rq.kb, wave);
   const uint32_t fix_rec = load_fix_words(a, rq.off - b + (i_fix >= 0 ? i_fix : 0), i_fix >= 0, lane);
-  if (tid == 0) s_ticket = -1;
   draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_ticket);
-  // each wave, once its part of the draw is done (after a split streaming pass, the workgroup
-  // once every wave is): the reverse-KL rows left to this launch
-  if (a.folded)
-    finish_rkl_rows_folded<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, &s_ticket, s_pm);
-  else
-    finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
+  // each wave, once its part of the draw is done: the reverse-KL rows left to this launch
+  // (folded rows have workgroups of their own)
+  if (!a.folded) finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
 }
 
 // =========================================================================== branch lookup
@@ -1148,7 +1136,7 @@ hipError_t launch_branch(const BranchArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_draw(int dtype, bool vec, const SampleArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.mass_blocks));
+  const dim3 grid(static_cast<unsigned>(a.B * a.mass_blocks + a.fix_rows));
   if (dtype == 0) {
     if (vec) hipLaunchKernelGGL((sv_draw_kernel<0, true>), grid, dim3(kMassThreads), 0, st, a);
     else hipLaunchKernelGGL((sv_draw_kernel<0, false>), grid, dim3(kMassThreads), 0, st, a);

@@ -124,12 +124,13 @@ struct RklFix {
   double lzp, lzq;          // the normalisers the streaming pass used
   double sp_rest, sq_rest;  // the other lanes' sums scaled to 2^kp_ref and 2^kq_ref
   float kp_ref, kq_ref;     // the normalisers' reference offsets (largest lane offsets)
-  int32_t n, pad;  // n: heavy lanes recorded (0: R is final)
+  int32_t n;       // heavy lanes recorded (0: R is final; nothing else is set then)
+  int32_t t_row;   // the draft row's target row
   RklFixLane h[kFixLanes];
 };
 constexpr int kFixDwords = static_cast<int>(sizeof(RklFix) / 4);
 static_assert(sizeof(RklFix) % 8 == 0 && kFixDwords <= 64, "one word per lane of a wave");
-static_assert(offsetof(RklFix, kp_ref) == 56 && offsetof(RklFix, n) == 64 &&
+static_assert(offsetof(RklFix, kp_ref) == 56 && offsetof(RklFix, n) == 64 && offsetof(RklFix, t_row) == 68 &&
               offsetof(RklFix, h) == 72 && sizeof(RklFixLane) == 16, "word offsets the draw reads");
 
 // Device pointers carved out of the caller's workspace.

@@ -1310,6 +1310,7 @@ __device__ __forceinline__ void rowpair_body(const RowPairArgs& a, const RowCtx&
         fx->kp_ref = Kp_ref;
         fx->kq_ref = Kq_ref;
         fx->n = n_heavy;
+        fx->t_row = static_cast<int32_t>(ctx.t);
         a.rkl_out[ctx.d] = static_cast<float>(v[0] + v[1]);
       }
     }
