@@ -774,8 +774,8 @@ def main():
     esize = 2 if w.dtype == "bf16" else 4
     rows_bytes = (w.n_target_rows + n_d) * V * esize  # every logit read once
     meta_bytes = 4 * (2 * (n_d + B) + B + n_d) + 4 * (B + (n_d + B) + 3 * n_d)
-    # small launches split each row over several workgroups: the streaming launch then reads
-    # every logit and a short finalize launch folds the parts
+    # small launches split each row over several workgroups of one launch (timed under the
+    # streaming kernel's name with a "_split" suffix), which still reads every logit once
     stream_name = STREAM_KERNEL if STREAM_KERNEL in kernels else STREAM_KERNEL + "_split"
     rows_us = kernels[stream_name]["avg_us"]
     kernel_gbs = rows_bytes / (rows_us * 1e-6) / 1e9
