@@ -623,15 +623,16 @@ __device__ __forceinline__ void finish_rkl_rows(const SampleArgs& a, int64_t b, 
   }
 }
 
-// After a split streaming pass the heavy lanes are folded ones, four times as long, and each
-// draft row has a workgroup of its own, after the drawing ones, so that the rows start with
-// the launch and the pick waits for none of them.  Wave w sums block w of every heavy lane
-// (lane_blocks), the blocks' sums meet in s_part, and wave 0 adds them up in block order, as
-// one wave would.  The record (n = 0 for a row the stream finished, and for every row of a void
-// call) names the row's target row.
+// After a split streaming pass each draft row has a workgroup of its own, after the drawing
+// ones, so that the rows start with the launch and the pick waits for none of them.  The
+// heavy lanes' blocks (lane_blocks: four for the folded lanes of a row whose parts were
+// folded, four times as long, else one) are spread over the waves, item i = (lane i / blocks,
+// block i % blocks) to wave i % 4; the blocks' sums meet in s_part, and wave 0 adds them up in
+// block order, as one wave would.  The record (n = 0 for a row the stream finished, and for
+// every row of a void call) names the row's target row.
 template <int DT, bool VEC>
-__device__ __forceinline__ void finish_rkl_row_folded(const SampleArgs& a, int64_t d, int wave,
-                                                      int lane, double* s_part) {
+__device__ __forceinline__ void finish_rkl_row_own(const SampleArgs& a, int64_t d, int wave,
+                                                   int lane, double* s_part) {
   static_assert(kMassWaves == kRowWaves && kFixLanes * kMassWaves * 3 <= kMaxChunks, "block sums fit s_part");
   const uint32_t rec = load_fix_words(a, d, true, lane);
   const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
@@ -639,16 +640,16 @@ __device__ __forceinline__ void finish_rkl_row_folded(const SampleArgs& a, int64
   const int64_t t = fix_word(rec, offsetof(RklFix, t_row) / 4);
   const void* prow = logits_row<DT>(a.target, t, a.ld_t);
   const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
-  for (int j = 0; j < n; ++j) {
+  const int blocks = lane_blocks(fix_word(rec, offsetof(RklFix, h) / 4));  // the same for every lane of the row
+  for (int it = wave; it < n * blocks; it += kMassWaves) {
+    const int j = it / blocks, q = it - j * blocks;
     const int h0 = offsetof(RklFix, h) / 4 + j * 4;
-    const int src = fix_word(rec, h0);
-    if (wave >= lane_blocks(src)) continue;
     const LaneSums e = exact_lane_sums<DT, VEC>(
-        prow, qrow, a.V, static_cast<int>(a.n_slices), src, wave, lane,
+        prow, qrow, a.V, static_cast<int>(a.n_slices), fix_word(rec, h0), q, lane,
         static_cast<double>(__int_as_float(fix_word(rec, h0 + 2))),
         static_cast<double>(__int_as_float(fix_word(rec, h0 + 3))));
     if (lane == 0) {
-      double* o = s_part + (j * kMassWaves + wave) * 3;
+      double* o = s_part + (j * kMassWaves + q) * 3;
       o[0] = e.sp;
       o[1] = e.sq;
       o[2] = e.w;
@@ -657,9 +658,8 @@ __device__ __forceinline__ void finish_rkl_row_folded(const SampleArgs& a, int64
   __syncthreads();
   if (wave == 0) {
     finish_rkl_from(a, d, rec, n, lane, [&](int j) {
-      const int src = fix_word(rec, offsetof(RklFix, h) / 4 + j * 4);
       LaneSums r{0.0, 0.0, 0.0};
-      for (int q = 0; q < lane_blocks(src); ++q) {
+      for (int q = 0; q < blocks; ++q) {
         const double* o = s_part + (j * kMassWaves + q) * 3;
         r.sp += o[0];
         r.sq += o[1];
@@ -859,8 +859,7 @@ __device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int
 // Each wave derives the request state itself (a few cached loads), so only the pick needs
 // the workgroup's barrier.  A wave done with the draw then finishes the request's reverse-KL
 // rows that the streaming pass left to this launch (finish_rkl_rows); after a split streaming
-// pass whose parts were folded, the workgroups after the drawing ones take one draft row each
-// (finish_rkl_row_folded).  Register use is capped so that all the workgroups of a B = 128
+// pass, the workgroups after the drawing ones take one draft row each (finish_rkl_row_own).  Register use is capped so that all the workgroups of a B = 128
 // call are resident at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
@@ -870,8 +869,8 @@ void sv_draw_kernel(SampleArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t drawing = a.B * a.mass_blocks;
-  if (static_cast<int64_t>(blockIdx.x) >= drawing) {  // a folded draft row's heavy lanes
-    finish_rkl_row_folded<DT, VEC>(a, blockIdx.x - drawing, wave, lane, s_pm);
+  if (static_cast<int64_t>(blockIdx.x) >= drawing) {  // a draft row's heavy lanes
+    finish_rkl_row_own<DT, VEC>(a, blockIdx.x - drawing, wave, lane, s_pm);
     return;
   }
   const int64_t b = blockIdx.x / a.mass_blocks;
@@ -890,12 +889,12 @@ void sv_draw_kernel(SampleArgs a) {
     return;
   }
   // the record of this wave's first reverse-KL row left to this launch, read while it draws
-  const int i_fix = a.folded ? -1 : first_fix_row(a, g, rq.kb, wave);
+  const int i_fix = a.fix_rows ? -1 : first_fix_row(a, g, rq.kb, wave);
   const uint32_t fix_rec = load_fix_words(a, rq.off - b + (i_fix >= 0 ? i_fix : 0), i_fix >= 0, lane);
   draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_ticket);
   // each wave, once its part of the draw is done: the reverse-KL rows left to this launch
-  // (folded rows have workgroups of their own)
-  if (!a.folded) finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
+  // (after a split streaming pass the rows have workgroups of their own)
+  if (!a.fix_rows) finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
 }
 
 // =========================================================================== branch lookup

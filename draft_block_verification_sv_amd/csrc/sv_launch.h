@@ -96,9 +96,9 @@ struct SampleArgs {
   float* rkl_out;
   const RklFix* fix;
   int64_t n_slices;  // the streaming pass's slices per row (lane geometry of the records)
-  int32_t folded;    // the streaming pass split rows: heavy lanes are folded ones (four blocks)
-  // folded with the reverse-KL: the workgroups after the B * mass_blocks drawing ones, one per
-  // draft row, that finish the rows left to this launch (0: none)
+  // after a split streaming pass, with the reverse-KL: the workgroups after the B * mass_blocks
+  // drawing ones, one per draft row, that finish the rows left to this launch (0: none; the
+  // drawing workgroups' waves finish them)
   int64_t fix_rows;
 };
 
