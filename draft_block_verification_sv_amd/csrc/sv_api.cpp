@@ -204,11 +204,10 @@ bool fit_workspace(const void* workspace, size_t bytes, Dims& dm) {
 // The streaming pass over n_units rows (pairs): one launch, each row streamed by one workgroup,
 // or for small launches by several (the part of a row that arrives last finishes it).
 hipError_t run_rowpair(int dtype, bool vec, sv::RowPairArgs ra, const Workspace& ws, int64_t rec_slots,
-                       hipStream_t st, int k_whole, bool* split_out = nullptr) {
+                       hipStream_t st, int k_whole) {
   const int P = rec_slots > 0 ? sv::row_split(ra.n_units, ra.n_slices) : 1;
   const bool split = P >= 2 && ra.n_units * P <= rec_slots;
   ra.folded = split && P >= sv::kFoldMinSplit ? 1 : 0;
-  if (split_out) *split_out = split;
   if (!split) {
     ra.phase = 0;
     ra.split = 1;
@@ -371,8 +370,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   ra.kmax1 = k_max + 1;
   ra.arrive = ws.arrive;
   if (rkl_out) ra.fix = ws.fix;  // heavy lanes of the reverse-KL rows are summed by the draw launch
-  bool split = false;
-  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR, &split) != hipSuccess) return SV_ERR_HIP;
+  if (run_rowpair(dtype, vec, ra, ws, dm.rec_slots, st, K_ROWPAIR) != hipSuccess) return SV_ERR_HIP;
 
   sv::SampleArgs sa{};
   sa.target = target_logits;
@@ -402,7 +400,7 @@ sv_status sv_verify_block(int32_t dtype, int32_t B, int32_t k_max, int64_t V, in
   sa.rkl_out = rkl_out;
   sa.fix = ws.fix;
   sa.n_slices = n_slices;
-  sa.fix_rows = (split && rkl_out) ? n_d : 0;
+  sa.fix_rows = rkl_out ? n_d : 0;
   if (timed(K_DRAW, st, [&] { return sv::launch_draw(dtype, vec, sa, st); }) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

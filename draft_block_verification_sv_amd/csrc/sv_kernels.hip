@@ -497,7 +497,7 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int64_t t, int
 }
 
 // The clipped reverse-KL of draft row d (target row t), which the streaming pass left
-// provisional with a record of its heavy lanes (RklFix), finished by one wave: each heavy lane
+// provisional with a record of its heavy lanes (RklFix), finished by the draw launch: each heavy lane
 // is summed again from the logits in fp64 (exp2 in fp64, against the lane's own offsets), the
 // normalisers are formed with the new sums, and R moves to them.  With LZp, LZq the streaming
 // pass's normalisers and LZp', LZq' the new ones, c2 = LZp - LZq, c2' = LZp' - LZq' and
@@ -574,59 +574,10 @@ __device__ __forceinline__ const void* logits_row(const void* base, int64_t r, i
   return static_cast<const char*>(base) + r * ld * (DT == 0 ? 2 : 4);
 }
 
-// The row finished by one wave: each heavy lane's blocks summed one after the other.
-template <int DT, bool VEC>
-__device__ __forceinline__ void finish_rkl_row(const SampleArgs& a, int64_t d, int64_t t,
-                                               uint32_t rec, int lane) {
-  const int n = min(fix_word(rec, offsetof(RklFix, n) / 4), kFixLanes);
-  if (n <= 0) return;
-  const void* prow = logits_row<DT>(a.target, t, a.ld_t);
-  const void* qrow = logits_row<DT>(a.draft, d, a.ld_d);
-  finish_rkl_from(a, d, rec, n, lane, [&](int j) {
-    const int h0 = offsetof(RklFix, h) / 4 + j * 4;
-    const int src = fix_word(rec, h0);
-    const double hkp = static_cast<double>(__int_as_float(fix_word(rec, h0 + 2)));
-    const double hkq = static_cast<double>(__int_as_float(fix_word(rec, h0 + 3)));
-    LaneSums r{0.0, 0.0, 0.0};
-    for (int q = 0; q < lane_blocks(src); ++q) {
-      const LaneSums e = exact_lane_sums<DT, VEC>(prow, qrow, a.V, static_cast<int>(a.n_slices), src, q,
-                                                  lane, hkp, hkq);
-      r.sp += e.sp;
-      r.sq += e.sq;
-      r.w += e.w;
-    }
-    return r;
-  });
-}
-
-// The rows of request b (draft rows off - b + i, target rows off + i, i < k_b) left to this
-// launch: row i goes to workgroup i % mass_blocks of the request, and there to wave
-// 3 - (i / mass_blocks) % 4, so that wave 0, which draws in the picking workgroup, comes last.
-// A wave's first row has its record loaded when the wave starts (first_fix_row /
-// load_fix_words), so that only the heavy lanes' columns are read after the draw; each wave
-// finishes its rows where it has nothing else left to do.
-__device__ __forceinline__ int first_fix_row(const SampleArgs& a, int g, int kb, int wave) {
-  const int i = g + (kMassWaves - 1 - wave) * a.mass_blocks;
-  return i < kb ? i : -1;
-}
-
-template <int DT, bool VEC>
-__device__ __forceinline__ void finish_rkl_rows(const SampleArgs& a, int64_t b, int g, int64_t off,
-                                                int kb, int wave, int lane, uint32_t first_rec) {
-  if (!a.rkl_out || !a.fix) return;
-  int j = 0;
-  for (int i = g; i < kb; i += a.mass_blocks, ++j) {
-    if (kMassWaves - 1 - (j % kMassWaves) != wave) continue;
-    const int64_t d = off - b + i;
-    const uint32_t rec = j < kMassWaves ? first_rec : load_fix_words(a, d, true, lane);
-    finish_rkl_row<DT, VEC>(a, d, off + i, rec, lane);
-  }
-}
-
-// After a split streaming pass each draft row has a workgroup of its own, after the drawing
-// ones, so that the rows start with the launch and the pick waits for none of them.  The
-// heavy lanes' blocks (lane_blocks: four for the folded lanes of a row whose parts were
-// folded, four times as long, else one) are spread over the waves, item i = (lane i / blocks,
+// Each draft row has a workgroup of its own, after the drawing ones, so that the rows start
+// with the launch and the draw waits for none of them.  The heavy lanes' blocks (lane_blocks:
+// four for the folded lanes of a split row whose parts were folded, four times as long, else
+// one) are spread over the waves, item i = (lane i / blocks,
 // block i % blocks) to wave i % 4; the blocks' sums meet in s_part, and wave 0 adds them up in
 // block order, as one wave would.  The record (n = 0 for a row the stream finished, and for
 // every row of a void call) names the row's target row.
@@ -857,10 +808,10 @@ __device__ __forceinline__ void draw_request(const SampleArgs& a, int64_t b, int
 // every request of sv_verify_block_greedy) emit the target's argmax from workgroup 0; void
 // calls and invalid requests are written by workgroup 0, with their input-check bits.
 // Each wave derives the request state itself (a few cached loads), so only the pick needs
-// the workgroup's barrier.  A wave done with the draw then finishes the request's reverse-KL
-// rows that the streaming pass left to this launch (finish_rkl_rows); after a split streaming
-// pass, the workgroups after the drawing ones take one draft row each (finish_rkl_row_own).  Register use is capped so that all the workgroups of a B = 128
-// call are resident at once.
+// the workgroup's barrier.  With the reverse-KL, the workgroups after the drawing ones take
+// one draft row each and finish it if the streaming pass left it to this launch
+// (finish_rkl_row_own).  Register use is capped so that all the drawing workgroups of a
+// B = 128 call are resident at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMassThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void sv_draw_kernel(SampleArgs a) {
@@ -888,13 +839,7 @@ void sv_draw_kernel(SampleArgs a) {
     }
     return;
   }
-  // the record of this wave's first reverse-KL row left to this launch, read while it draws
-  const int i_fix = a.fix_rows ? -1 : first_fix_row(a, g, rq.kb, wave);
-  const uint32_t fix_rec = load_fix_words(a, rq.off - b + (i_fix >= 0 ? i_fix : 0), i_fix >= 0, lane);
   draw_request<DT, VEC>(a, b, g, tid, lane, wave, my_tok, my_u, rq, s_pm, &s_ticket);
-  // each wave, once its part of the draw is done: the reverse-KL rows left to this launch
-  // (after a split streaming pass the rows have workgroups of their own)
-  if (!a.fix_rows) finish_rkl_rows<DT, VEC>(a, b, g, rq.off, rq.kb, wave, lane, fix_rec);
 }
 
 // =========================================================================== branch lookup

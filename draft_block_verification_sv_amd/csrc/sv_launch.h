@@ -96,9 +96,8 @@ struct SampleArgs {
   float* rkl_out;
   const RklFix* fix;
   int64_t n_slices;  // the streaming pass's slices per row (lane geometry of the records)
-  // after a split streaming pass, with the reverse-KL: the workgroups after the B * mass_blocks
-  // drawing ones, one per draft row, that finish the rows left to this launch (0: none; the
-  // drawing workgroups' waves finish them)
+  // with the reverse-KL, n_d: the workgroups after the B * mass_blocks drawing ones, one per
+  // draft row, that finish the rows the streaming pass left to this launch (0: none)
   int64_t fix_rows;
 };
 
