@@ -361,6 +361,33 @@ def test_void_calls():
     assert np.all(got["accept_len"] == -1)
 
 
+# One workspace through a call whose rows leave heavy lanes to the draw launch (records with
+# lanes), a void call (every record must then read as empty, so that the draw's per-row
+# workgroups leave the NaN outputs alone), and the first call again.  B = 4: split rows;
+# B = 40: one workgroup per row.
+@pytest.mark.parametrize("B", [4, 40])
+def test_void_call_after_heavy_rows_on_one_workspace(B):
+    import draft_block_verification_sv_amd as pkg
+
+    w = _heavy_lane_workload("bf16", B, (32, B))
+    ws = pkg.alloc_workspace(pkg.workspace_size(B, w.k_max, w.V, pkg.SV_BF16), "cuda")
+    dev = to_device(w)
+    ref = run_oracle(w, delta=1.0)
+    first = run_gpu(w, dev, delta=1.0, workspace=ws)
+    compare(w, first, ref)
+    bad = w.k.copy()
+    bad[1] = 0  # k_b outside [1, k_max]: the whole call is void
+    dev_bad = dict(dev)
+    dev_bad["k"] = torch.from_numpy(bad).cuda()
+    got = run_gpu(w, dev_bad, delta=1.0, workspace=ws)
+    assert int(got["device_status"][0]) & 1
+    assert np.all(got["accept_len"] == -1) and np.all(got["out_tokens"] == -1)
+    assert np.all(np.isnan(got["rkl"]))
+    again = run_gpu(w, dev, delta=1.0, workspace=ws)
+    compare(w, again, ref)
+    assert np.array_equal(again["rkl"].view(np.uint32), first["rkl"].view(np.uint32))
+
+
 def test_workspace_reuse_between_shapes():
     import draft_block_verification_sv_amd as pkg
 
